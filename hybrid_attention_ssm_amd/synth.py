@@ -1,0 +1,106 @@
+"""Seeded synthetic inputs for the hybrid-head layer.
+
+Both the GPU path and the CPU oracle consume these arrays; this module holds
+only random draws and storage rounding, none of the layer's arithmetic.
+
+Recipe (one numpy PCG64 generator per workload, seeded with the workload seed,
+draws in this fixed order):
+  1. x      [B, n, d]          ~ N(0, 1)
+  2. R      [m, d]             ~ N(0, 1)            (meta tokens)
+  3. W_in   [N_in, d]          ~ N(0, 1/d)          (rows Q|K|V|xs|z|dt|B|C)
+  4. dt     [D]                ~ exp(U[ln 1e-3, ln 1e-1]);  b_dt = log(expm1(dt))
+     so that softplus(b_dt) is log-uniform in [1e-3, 1e-1]
+  5. A      [D, N]             = -exp(U[ln 1, ln 16])
+  6. conv_w [D, k]             ~ N(0, 1/k);  conv_b = 0
+  7. W_out  [d, H*hd + D]      ~ N(0, 1/(H*hd + D))
+  8. beta_attn = beta_ssm = 1
+For bf16 workloads x, R, W_in, conv_w and W_out are rounded to bf16 once
+(round to nearest even); every consumer sees the rounded values.  A, b_dt and
+the betas stay fp32.  A consumer layer (no K/V projection) drops the K and V
+rows of the same draw, so it shares every other weight with its producer.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .configs import DecodeWorkload, LayerDims, PrefillWorkload
+
+
+def round_bf16(a) -> np.ndarray:
+    """Round float32 values to the nearest bf16 (ties to even); keep float32."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).reshape(a.shape)
+
+
+def _store(dims: LayerDims, a) -> np.ndarray:
+    a = np.asarray(a, dtype=np.float32)
+    return round_bf16(a) if dims.dtype == "bf16" else a
+
+
+def _normal(rng, shape, std=1.0) -> np.ndarray:
+    out = rng.standard_normal(shape, dtype=np.float32)
+    if std != 1.0:
+        out *= np.float32(std)
+    return out
+
+
+def layer_weights(rng, dims: LayerDims, kv_producer: bool = True) -> dict:
+    """Draw one layer's parameters (steps 3-8 of the recipe)."""
+    d, D, N, k = dims.d_model, dims.d_inner, dims.d_state, dims.d_conv
+    Wa, kv = dims.attn_width, dims.n_kv_heads * dims.head_dim
+    w_in = _store(dims, _normal(rng, (dims.n_in(True), d), (1.0 / d) ** 0.5))
+    if not kv_producer:
+        w_in = np.ascontiguousarray(np.concatenate([w_in[:Wa], w_in[Wa + 2 * kv:]]))
+    dt = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), size=D))
+    dt_bias = np.log(np.expm1(dt)).astype(np.float32)
+    A = (-np.exp(rng.uniform(np.log(1.0), np.log(16.0), size=(D, N)))).astype(np.float32)
+    conv_w = _store(dims, _normal(rng, (D, k), (1.0 / k) ** 0.5))
+    conv_b = np.zeros(D, np.float32)
+    w_out = _store(dims, _normal(rng, (d, Wa + D), (1.0 / (Wa + D)) ** 0.5))
+    return dict(w_in=w_in, dt_bias=dt_bias, A=A, conv_w=conv_w, conv_b=conv_b,
+                beta_attn=np.ones(Wa, np.float32), beta_ssm=np.ones(D, np.float32),
+                w_out=w_out, kv_producer=bool(kv_producer))
+
+
+def prefill_inputs(w: PrefillWorkload, kv_producer: bool = True, seed=None) -> dict:
+    """x, meta tokens R and the layer weights for a prefill workload."""
+    dims = w.dims
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    x = _store(dims, _normal(rng, (w.batch, w.seqlen, dims.d_model)))
+    R = _store(dims, _normal(rng, (dims.n_meta, dims.d_model)))
+    weights = layer_weights(rng, dims, kv_producer)
+    return dict(x=x, R=R, weights=weights)
+
+
+def decode_inputs(w: DecodeWorkload, seed=None) -> dict:
+    """Weights, caches, SSM states and new tokens for a decode workload.
+
+    Draw order: per layer (in layer order) its weights; then per cache (sorted
+    by name) meta K, meta V, cache K, cache V; then per layer h [B, D, N]
+    (fp32), its conv tail [B, k-1, D] and its new token x_t [B, d]; all N(0, 1).
+    Every sequence holds `context` real positions before the step.
+    """
+    dims = w.dims
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    G, m, hd = dims.n_kv_heads, dims.n_meta, dims.head_dim
+    B, D, N, k = w.batch, dims.d_inner, dims.d_state, dims.d_conv
+    layers = []
+    for spec in w.layers:
+        layers.append(dict(spec=spec, weights=layer_weights(rng, dims, spec.kv_producer)))
+    caches = {}
+    for name in sorted({s.cache for s in w.layers}):
+        is_ring = name != "global"
+        cap = w.window if is_ring else w.global_cap
+        caches[name] = dict(
+            meta_k=_store(dims, _normal(rng, (G, m, hd))),
+            meta_v=_store(dims, _normal(rng, (G, m, hd))),
+            k=_store(dims, _normal(rng, (B, G, cap, hd))),
+            v=_store(dims, _normal(rng, (B, G, cap, hd))),
+            len=np.full(B, w.context, np.int32), cap=cap, is_ring=is_ring)
+    for lay in layers:
+        lay["h"] = _normal(rng, (B, D, N))
+        lay["conv"] = _store(dims, _normal(rng, (B, k - 1, D)))
+        lay["x_t"] = _store(dims, _normal(rng, (B, dims.d_model)))
+    return dict(layers=layers, caches=caches)

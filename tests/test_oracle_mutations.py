@@ -1,0 +1,103 @@
+"""Plant plausible mistakes in the oracle (CPU only) and check that the pins
+catch each one: the library-composition pin must disagree for every mutant."""
+import numpy as np
+import pytest
+
+from oracle import hymba_ref as ref
+from tests.test_oracle_pins import GQA, _layer, layer_by_library
+
+
+def _max_err(window=7, is_global=False):
+    dims = GQA
+    x, R, w = _layer(dims, 30, seed=21)
+    got = ref.prefill(dims.as_dict(), w, R, x, window, is_global)
+    want = layer_by_library(dims, w, R, x[0], window, is_global)
+    return float(np.abs(got["out"][0] - want["out"]).max())
+
+
+_orig_split = ref.split_projection
+_orig_attend = ref.attend
+_orig_scan = ref.selective_scan
+_orig_conv = ref.causal_conv
+
+
+def _swap_xs_z(P, dims, kv_producer=True):
+    p = _orig_split(P, dims, kv_producer)
+    p["xs"], p["z"] = p["z"], p["xs"]
+    return p
+
+
+def _swap_b_c(P, dims, kv_producer=True):
+    p = _orig_split(P, dims, kv_producer)
+    p["B"], p["C"] = p["C"], p["B"]
+    return p
+
+
+def _no_scale(q, K, V, rows, scale):
+    return _orig_attend(q, K, V, rows, 1.0)
+
+
+def _kv_swapped(q, K, V, rows, scale):
+    return _orig_attend(q, V, K, rows, scale)
+
+
+def _group_interleaved(q, K, V, rows, scale):
+    H, G = q.shape[0], K.shape[1]
+    perm = np.arange(H) % G                   # wrong head -> group map
+    out = np.empty_like(q)
+    for h in range(H):
+        o, _ = _orig_attend(q[h:h + 1], K[:, perm[h]:perm[h] + 1], V[:, perm[h]:perm[h] + 1], rows, scale)
+        out[h] = o[0]
+    return out, None
+
+
+def _window_off_by_one(i, m, window, is_global):
+    lo = m if is_global else max(m, i - window)
+    return np.concatenate([np.arange(m), np.arange(lo, i + 1)]).astype(np.int64)
+
+
+def _no_meta_keys(i, m, window, is_global):
+    lo = m if is_global else max(m, i - window + 1)
+    return np.arange(lo, i + 1).astype(np.int64)
+
+
+def _scan_no_delta_in_input(u, delta, A, Bm, Cm, h):
+    return _orig_scan(u / np.where(delta == 0, 1, delta), delta, A, Bm, Cm, h)
+
+
+def _scan_positive_exponent(u, delta, A, Bm, Cm, h):
+    return _orig_scan(u, delta, -A * 0.5, Bm, Cm, h)
+
+
+def _conv_taps_not_reversed(xs, conv_w, conv_b, history):
+    return _orig_conv(xs, conv_w[:, ::-1], conv_b, history)
+
+
+MUTANTS = {
+    "xs<->z": ("split_projection", _swap_xs_z),
+    "B<->C": ("split_projection", _swap_b_c),
+    "no 1/sqrt(hd)": ("attend", _no_scale),
+    "K<->V": ("attend", _kv_swapped),
+    "head->group map": ("attend", _group_interleaved),
+    "window off by one": ("allowed_rows", _window_off_by_one),
+    "meta keys dropped": ("allowed_rows", _no_meta_keys),
+    "Delta missing from input term": ("selective_scan", _scan_no_delta_in_input),
+    "wrong decay": ("selective_scan", _scan_positive_exponent),
+    "conv taps not reversed": ("causal_conv", _conv_taps_not_reversed),
+    "softplus -> exp": ("softplus", np.exp),
+    "silu -> sigmoid": ("silu", lambda v: 0.5 * (1.0 + np.tanh(0.5 * v))),
+    "no eps / sum not mean": ("rms_normalize", lambda v, eps: v / np.sqrt(np.sum(v * v, axis=-1, keepdims=True))),
+    "sum not average": ("fuse", lambda O, Y, b1, b2, eps: 2.0 * ref.__dict__["_fuse_orig"](O, Y, b1, b2, eps)),
+}
+ref._fuse_orig = ref.fuse
+
+
+def test_unmutated_oracle_agrees():
+    assert _max_err() < 1e-9
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(ref, attr, fn)
+    assert _max_err() > 1e-4, f"mutant '{name}' not caught"

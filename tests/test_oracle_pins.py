@@ -1,0 +1,365 @@
+"""Pins for the CPU oracle, independent of the oracle's own code.
+
+Each test checks the oracle against something it does not share code with:
+hand-derived values (tests/golden), closed forms, invariants the Hymba paper's
+equations imply, or the layer composed from library routines (torch CPU in
+fp64: linear, conv1d, scaled_dot_product_attention with an explicit boolean
+mask, softplus, silu, rms_norm) with the SSM written in the alternative
+alpha-matrix form of Eq. (2).  CPU only.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as TF
+
+from oracle import hymba_ref as ref
+from hybrid_attention_ssm_amd.configs import TINY, LayerDims
+from hybrid_attention_ssm_amd.synth import layer_weights
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append([float(v) for v in line.split()])
+    return rows
+
+
+def _layer(dims: LayerDims, n, seed, kv_producer=True, batch=1):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((batch, n, dims.d_model)).astype(np.float32)
+    R = rng.standard_normal((dims.n_meta, dims.d_model)).astype(np.float32)
+    w = layer_weights(rng, dims, kv_producer)
+    return x, R, w
+
+
+GQA = LayerDims(d_model=48, n_heads=4, n_kv_heads=2, head_dim=8, d_inner=24,
+                d_state=4, d_conv=4, n_meta=3, dtype="f32")
+
+
+# ---------------------------------------------------------------------------
+# the layer composed from library routines; SSM via Eq. (2)'s alpha matrix
+# ---------------------------------------------------------------------------
+def layer_by_library(dims: LayerDims, w, R, xb, window, is_global):
+    t = lambda a: torch.as_tensor(np.asarray(a, dtype=np.float64))
+    m, n = R.shape[0], xb.shape[0]
+    T = m + n
+    H, G, hd, D, N, k = (dims.n_heads, dims.n_kv_heads, dims.head_dim,
+                         dims.d_inner, dims.d_state, dims.d_conv)
+    Xt = torch.cat([t(R), t(xb)])
+    P = TF.linear(Xt, t(w["w_in"]))
+    q, kk, v, xs, z, dt, Bm, Cm = torch.split(
+        P, [H * hd, G * hd, G * hd, D, D, D, N, N], dim=-1)
+    # A-shape mask: meta keys always, real keys in the window (or causal)
+    i = torch.arange(T)[:, None]
+    j = torch.arange(T)[None, :]
+    real = (j >= m) & (j <= i) & ((i - j < window) | is_global)
+    mask = (j < m) | real
+    qh = q.view(T, H, hd).transpose(0, 1)
+    kh = kk.view(T, G, hd).transpose(0, 1).repeat_interleave(H // G, dim=0)
+    vh = v.view(T, G, hd).transpose(0, 1).repeat_interleave(H // G, dim=0)
+    O = TF.scaled_dot_product_attention(qh, kh, vh, attn_mask=mask)
+    O = O.transpose(0, 1).reshape(T, H * hd)
+    c = TF.conv1d(xs.T[None], t(w["conv_w"])[:, None, :], t(w["conv_b"]),
+                  padding=k - 1, groups=D)[0, :, :T].T
+    u = TF.silu(c)
+    delta = TF.softplus(dt + t(w["dt_bias"]), threshold=1e4)
+    A = t(w["A"])
+    cs = torch.cumsum(delta, 0)                       # sum_{k<=i} Delta_k
+    y = torch.zeros(T, D, dtype=torch.float64)
+    hT = torch.zeros(D, N, dtype=torch.float64)
+    lower = (j <= i)
+    for ch in range(D):
+        # prod_{k=j+1..i} exp(A Delta_k) = exp(A (cs_i - cs_j)) for j <= i
+        diff = torch.where(lower, cs[:, ch][:, None] - cs[:, ch][None, :], torch.zeros(()))
+        E = torch.exp(A[ch][None, None, :] * diff[:, :, None])          # [T, T, N]
+        alpha = torch.einsum("is,ijs,js->ij", Cm, E, Bm) * delta[:, ch][None, :]
+        alpha = torch.where(lower, alpha, torch.zeros(()))
+        y[:, ch] = alpha @ u[:, ch]
+        ET = torch.exp(A[ch][None, :] * (cs[-1, ch] - cs[:, ch])[:, None])  # [T, N]
+        hT[ch] = (ET * Bm * (delta[:, ch] * u[:, ch])[:, None]).sum(0)
+    Y = TF.silu(z) * y
+    F = 0.5 * torch.cat([t(w["beta_attn"]) * TF.rms_norm(O, (H * hd,), eps=dims.eps),
+                         t(w["beta_ssm"]) * TF.rms_norm(Y, (D,), eps=dims.eps)], dim=-1)
+    out = TF.linear(F, t(w["w_out"]))
+    return dict(out=out[m:].numpy(), h=hT.numpy(), K=kk.view(T, G, hd).numpy(),
+                xs=xs.numpy(), O=O[m:].numpy(), Y=Y[m:].numpy())
+
+
+@pytest.mark.parametrize("dims,n,window,is_global", [
+    (TINY, 40, 16, False), (TINY, 24, 16, True), (GQA, 30, 7, False), (GQA, 17, 5, True)])
+def test_layer_matches_library_composition(dims, n, window, is_global):
+    x, R, w = _layer(dims, n, seed=11)
+    got = ref.prefill(dims.as_dict(), w, R, x, window, is_global)
+    want = layer_by_library(dims, w, R, x[0], window, is_global)
+    np.testing.assert_allclose(got["out"][0], want["out"], rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(got["h"][0], want["h"], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(got["K_all"][0], want["K"], rtol=1e-12, atol=1e-12)
+    k = dims.d_conv
+    np.testing.assert_allclose(got["conv_tail"][0], want["xs"][-(k - 1):], rtol=1e-12, atol=1e-12)
+
+
+def test_meta_prefix_matches_prefill_state():
+    """The offline meta part equals the state of the literal [R; X] pass at row m."""
+    dims = TINY
+    x, R, w = _layer(dims, 1, seed=5)
+    mp = ref.meta_prefix(dims.as_dict(), w, R)
+    want = layer_by_library(dims, w, R, x[0][:0], 16, False)
+    np.testing.assert_allclose(mp["h0"], want["h"], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(mp["k"].transpose(1, 0, 2), want["K"], rtol=1e-12)
+    np.testing.assert_allclose(mp["conv_tail"], want["xs"][-3:], rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# hand-derived golden values
+# ---------------------------------------------------------------------------
+def test_golden_scan_geometric():
+    rows = _golden("scan_geometric.txt")
+    T = len(rows)
+    ln2 = math.log(2.0)
+    y, h = ref.selective_scan(np.ones((T, 1)), np.full((T, 1), ln2),
+                              np.array([[-1.0, -2.0]]), np.tile([[1.0, 2.0]], (T, 1)),
+                              np.ones((T, 2)), np.zeros((1, 2)))
+    for t, (tt, y_ln2, h0, h1) in enumerate(rows):
+        assert int(tt) == t
+        assert y[t, 0] == pytest.approx(y_ln2 * ln2, rel=1e-14)
+    assert h[0, 0] == pytest.approx(rows[-1][2] * ln2, rel=1e-14)
+    assert h[0, 1] == pytest.approx(rows[-1][3] * ln2, rel=1e-14)
+
+
+def test_golden_attention_two_keys():
+    (p1, p2), o_want = _golden("attention_two_keys.txt")
+    q = np.array([[1.0, 0, 0, 0]])
+    K = np.zeros((2, 1, 4)); K[0, 0, 0] = 2 * math.log(3.0)
+    V = np.zeros((2, 1, 4)); V[0, 0, 0] = 4.0; V[1, 0, 1] = 8.0
+    o, p = ref.attend(q, K, V, np.array([0, 1]), 1.0 / math.sqrt(4))
+    np.testing.assert_allclose(p[0], [p1, p2], rtol=1e-14)
+    np.testing.assert_allclose(o[0], o_want, rtol=1e-14, atol=1e-14)
+
+
+def test_golden_conv_taps():
+    xs_in, c_want = _golden("conv_taps.txt")
+    c = ref.causal_conv(np.array(xs_in)[:, None], np.array([[1.0, 2, 3, 4]]),
+                        np.zeros(1), np.zeros((3, 1)))
+    np.testing.assert_array_equal(c[:, 0], c_want)
+
+
+def test_softplus_silu_closed_forms():
+    assert ref.softplus(0.0) == pytest.approx(math.log(2.0), rel=1e-15)
+    assert ref.softplus(50.0) == pytest.approx(50.0 + math.exp(-50.0), rel=1e-15)
+    assert ref.softplus(-50.0) == pytest.approx(math.exp(-50.0), rel=1e-12)
+    assert ref.silu(0.0) == 0.0
+    assert ref.silu(2.0) == pytest.approx(2.0 / (1.0 + math.exp(-2.0)), rel=1e-15)
+    assert ref.silu(-800.0) == pytest.approx(0.0, abs=1e-300)
+
+
+# ---------------------------------------------------------------------------
+# invariants and special cases
+# ---------------------------------------------------------------------------
+def test_window_at_least_n_equals_global():
+    dims = GQA
+    x, R, w = _layer(dims, 20, seed=3)
+    a = ref.prefill(dims.as_dict(), w, R, x, 20, False)
+    b = ref.prefill(dims.as_dict(), w, R, x, 10 ** 6, False)
+    c = ref.prefill(dims.as_dict(), w, R, x, 1, True)
+    np.testing.assert_allclose(a["out"], c["out"], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(b["out"], c["out"], rtol=1e-13, atol=1e-13)
+    d_ = ref.prefill(dims.as_dict(), w, R, x, 19, False)
+    assert np.abs(d_["out"] - c["out"]).max() > 1e-6   # the window does bite below n
+
+
+def test_allowed_rows_shape():
+    m, W = 4, 3
+    assert list(ref.allowed_rows(m + 0, m, W, False)) == [0, 1, 2, 3, 4]
+    assert list(ref.allowed_rows(m + 5, m, W, False)) == [0, 1, 2, 3, 7, 8, 9]
+    assert list(ref.allowed_rows(m + 5, m, W, True)) == [0, 1, 2, 3, 4, 5, 6, 7, 8, 9]
+
+
+def test_softmax_rows_sum_to_one():
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal((4, 8)) * 3
+    K = rng.standard_normal((30, 2, 8)) * 3
+    V = rng.standard_normal((30, 2, 8))
+    for i in (3, 10, 29):
+        rows = ref.allowed_rows(i, 3, 5, False)
+        _, p = ref.attend(q, K, V, rows, 1 / math.sqrt(8))
+        np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=1e-14)
+        assert p.shape[1] == 3 + min(5, i - 3 + 1)
+
+
+def test_quiet_attention_zero_token():
+    """A K = V = 0 key adds exactly 1 to the softmax denominator (paper §2.3,
+    'exit tokens'): o = sum e^s v / (1 + sum e^s)."""
+    rng = np.random.default_rng(1)
+    q = rng.standard_normal((1, 8))
+    K = rng.standard_normal((6, 1, 8)); K[0] = 0.0
+    V = rng.standard_normal((6, 1, 8)); V[0] = 0.0
+    o, _ = ref.attend(q, K, V, np.arange(6), 1.0)
+    s = K[1:, 0] @ q[0]
+    want = (np.exp(s)[:, None] * V[1:, 0]).sum(0) / (1.0 + np.exp(s).sum())
+    np.testing.assert_allclose(o[0], want, rtol=1e-13)
+
+
+def test_gqa_equals_mha_with_duplicated_heads():
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal((4, 8))
+    K = rng.standard_normal((12, 2, 8))
+    V = rng.standard_normal((12, 2, 8))
+    rows = np.arange(12)
+    o_gqa, _ = ref.attend(q, K, V, rows, 0.3)
+    Kd, Vd = np.repeat(K, 2, axis=1), np.repeat(V, 2, axis=1)
+    o_mha, _ = ref.attend(q, Kd, Vd, rows, 0.3)
+    np.testing.assert_allclose(o_gqa, o_mha, rtol=1e-14)
+    # heads 0,1 read group 0 and heads 2,3 read group 1
+    o_h2, _ = ref.attend(q[2:3], K[:, 1:2], V[:, 1:2], rows, 0.3)
+    np.testing.assert_allclose(o_gqa[2], o_h2[0], rtol=1e-14)
+
+
+def test_zero_delta_keeps_state():
+    rng = np.random.default_rng(4)
+    T, D, N = 7, 5, 3
+    h0 = rng.standard_normal((D, N))
+    Cm = rng.standard_normal((T, N))
+    y, h = ref.selective_scan(rng.standard_normal((T, D)), np.zeros((T, D)),
+                              -np.exp(rng.standard_normal((D, N))),
+                              rng.standard_normal((T, N)), Cm, h0)
+    np.testing.assert_array_equal(h, h0)
+    np.testing.assert_allclose(y, (h0 @ Cm.T).T, rtol=1e-14)
+
+
+def test_constant_input_geometric_sum():
+    rng = np.random.default_rng(6)
+    T, D, N = 50, 4, 3
+    A = -np.exp(rng.uniform(0, 2, (D, N)))
+    dlt = rng.uniform(0.01, 0.2, D)
+    u = rng.standard_normal(D)
+    Bv = rng.standard_normal(N)
+    h0 = rng.standard_normal((D, N))
+    _, h = ref.selective_scan(np.tile(u, (T, 1)), np.tile(dlt, (T, 1)), A,
+                              np.tile(Bv, (T, 1)), np.ones((T, N)), h0)
+    a = np.exp(dlt[:, None] * A)
+    inj = (dlt * u)[:, None] * Bv[None, :]
+    want = a ** T * h0 + inj * (1 - a ** T) / (1 - a)
+    np.testing.assert_allclose(h, want, rtol=1e-12)
+
+
+def test_full_decay_limit():
+    """A -> -inf: the state forgets everything, h_t = Delta_t u_t B_t."""
+    rng = np.random.default_rng(7)
+    T, D, N = 6, 3, 4
+    dlt = rng.uniform(0.1, 1, (T, D)); u = rng.standard_normal((T, D))
+    Bm = rng.standard_normal((T, N)); Cm = rng.standard_normal((T, N))
+    y, h = ref.selective_scan(u, dlt, np.full((D, N), -1e300), Bm, Cm,
+                              rng.standard_normal((D, N)))
+    np.testing.assert_allclose(y, (dlt * u) * (Bm * Cm).sum(1)[:, None], rtol=1e-13)
+    np.testing.assert_allclose(h, (dlt[-1] * u[-1])[:, None] * Bm[-1][None, :], rtol=1e-13)
+
+
+def test_beta_zero_selects_one_branch():
+    """beta1 = 0 leaves only 1/2 W_out[:, Wa:] norm(Y); beta2 = 0 only the
+    attention half (paper §2.1 and App. C head-importance analysis)."""
+    dims = TINY
+    x, R, w = _layer(dims, 12, seed=8)
+    Wa = dims.attn_width
+    full = ref.prefill(dims.as_dict(), w, R, x, 16, False)
+    O, Y = full["O"][0], full["Y"][0]
+    nrm = lambda v: v / np.sqrt((v * v).mean(-1, keepdims=True) + dims.eps)
+    w1 = dict(w, beta_attn=np.zeros_like(w["beta_attn"]))
+    got = ref.prefill(dims.as_dict(), w1, R, x, 16, False)["out"][0]
+    np.testing.assert_allclose(got, 0.5 * nrm(Y) @ w["w_out"][:, Wa:].T.astype(np.float64),
+                               rtol=1e-11, atol=1e-12)
+    w2 = dict(w, beta_ssm=np.zeros_like(w["beta_ssm"]))
+    got = ref.prefill(dims.as_dict(), w2, R, x, 16, False)["out"][0]
+    np.testing.assert_allclose(got, 0.5 * nrm(O) @ w["w_out"][:, :Wa].T.astype(np.float64),
+                               rtol=1e-11, atol=1e-12)
+
+
+def test_consumer_reads_producer_kv():
+    """A consumer with the producer's Q weights and input gives the producer's
+    attention output; its K/V are the producer's, bit for bit."""
+    dims = GQA
+    x, R, wp = _layer(dims, 15, seed=9, kv_producer=True)
+    rng = np.random.default_rng(9)
+    _ = rng  # the consumer draw drops the K/V rows of the same weights
+    Wa, kv = dims.attn_width, dims.n_kv_heads * dims.head_dim
+    wc = dict(wp, kv_producer=False,
+              w_in=np.concatenate([wp["w_in"][:Wa], wp["w_in"][Wa + 2 * kv:]]))
+    prod = ref.prefill(dims.as_dict(), wp, R, x, 6, False)
+    cons = ref.prefill(dims.as_dict(), wc, R, x, 6, False,
+                       shared_kv=(prod["K_all"], prod["V_all"]))
+    np.testing.assert_array_equal(cons["K_all"], prod["K_all"])
+    np.testing.assert_allclose(cons["O"], prod["O"], rtol=1e-14)
+    np.testing.assert_allclose(cons["out"], prod["out"], rtol=1e-13)
+
+
+@pytest.mark.parametrize("is_global,n0,steps,cap", [
+    (False, 5, 4, 6), (False, 9, 6, 6), (True, 5, 4, 16)])
+def test_prefill_then_decode_equals_longer_prefill(is_global, n0, steps, cap):
+    """prefill(n) + k decode steps == prefill(n + k): outputs, state, conv
+    tail and cache slots (including ring wrap-around when n + k > cap)."""
+    dims = GQA
+    window = cap
+    x, R, w = _layer(dims, n0 + steps, seed=10, batch=2)
+    B = x.shape[0]
+    G, hd = dims.n_kv_heads, dims.head_dim
+    zeros = np.zeros((B, G, cap, hd))
+    cache0 = dict(k=zeros, v=zeros, is_ring=not is_global)
+    full = ref.prefill(dims.as_dict(), w, R, x, window, is_global, cache=cache0)
+    pre = ref.prefill(dims.as_dict(), w, R, x[:, :n0], window, is_global, cache=cache0)
+    mp = ref.meta_prefix(dims.as_dict(), w, R)
+    cache = dict(k=pre["cache_k"], v=pre["cache_v"], len=np.full(B, n0), is_ring=not is_global)
+    h, conv = pre["h"], pre["conv_tail"]
+    for s in range(steps):
+        r = ref.decode_step(dims.as_dict(), w, x[:, n0 + s], mp["k"], mp["v"], window,
+                            is_global, cache, h, conv)
+        np.testing.assert_allclose(r["out"], full["out"][:, n0 + s], rtol=1e-10, atol=1e-11)
+        cache = dict(k=r["cache_k"], v=r["cache_v"], len=r["len"], is_ring=not is_global)
+        h, conv = r["h"], r["conv"]
+    np.testing.assert_allclose(h, full["h"], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(conv, full["conv_tail"], rtol=1e-12)
+    # same slots hold the same positions (values agree up to BLAS rounding order)
+    np.testing.assert_allclose(cache["k"], full["cache_k"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(cache["v"], full["cache_v"], rtol=1e-12, atol=1e-14)
+    assert list(cache["len"]) == [n0 + steps] * B
+
+
+def test_ring_slot_holds_last_position_with_that_residue():
+    dims = GQA
+    x, R, w = _layer(dims, 13, seed=12)
+    cap = 5
+    zeros = np.zeros((1, dims.n_kv_heads, cap, dims.head_dim))
+    r = ref.prefill(dims.as_dict(), w, R, x, cap, False,
+                    cache=dict(k=zeros, v=zeros, is_ring=True))
+    for s in range(cap):
+        p = max(q for q in range(13) if q % cap == s)
+        np.testing.assert_array_equal(r["cache_k"][0, :, s], r["k_full"][0, :, p])
+        np.testing.assert_array_equal(r["cache_v"][0, :, s], r["v_full"][0, :, p])
+
+
+def test_consumer_decode_sees_token_appended_by_producer():
+    dims = GQA
+    x, R, wp = _layer(dims, 8, seed=13, batch=2)
+    Wa, kv = dims.attn_width, dims.n_kv_heads * dims.head_dim
+    wc = dict(wp, kv_producer=False,
+              w_in=np.concatenate([wp["w_in"][:Wa], wp["w_in"][Wa + 2 * kv:]]))
+    mp = ref.meta_prefix(dims.as_dict(), wp, R)
+    cap = 4
+    pre = ref.prefill(dims.as_dict(), wp, R, x[:, :7], cap, False,
+                      cache=dict(k=np.zeros((2, 2, cap, 8)), v=np.zeros((2, 2, cap, 8)),
+                                 is_ring=True))
+    cache = dict(k=pre["cache_k"], v=pre["cache_v"], len=np.full(2, 7), is_ring=True)
+    rp = ref.decode_step(dims.as_dict(), wp, x[:, 7], mp["k"], mp["v"], cap, False,
+                         cache, pre["h"], pre["conv_tail"])
+    cache2 = dict(k=rp["cache_k"], v=rp["cache_v"], len=rp["len"], is_ring=True)
+    rc = ref.decode_step(dims.as_dict(), wc, x[:, 7], mp["k"], mp["v"], cap, False,
+                         cache2, pre["h"], pre["conv_tail"])
+    np.testing.assert_allclose(rc["out"], rp["out"], rtol=1e-13)
+    np.testing.assert_array_equal(rc["cache_k"], rp["cache_k"])
+    assert list(rc["len"]) == [8, 8]
