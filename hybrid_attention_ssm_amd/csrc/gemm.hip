@@ -1,0 +1,278 @@
+// Input and output projections of the hybrid-head layer
+// (Hymba paper, §2.1: the fused W_in_proj of the design formulation, and
+// Eq. (3)'s W_out_proj).
+//
+// C[M, N] = A[M, K] B[N, K]^T with A, B row-major and K contiguous ("NT"), so
+// both operands are read along K.  bf16 path: MFMA v_mfma_f32_32x32x16_bf16
+// with fp32 accumulators; the fp32 path uses a plain LDS-tiled FMA kernel.
+// Results go through an epilogue functor (the in-projection splits its
+// columns into Q, K/V (+ cache slots), xs, z, softplus(dt + b), B, C).
+#include "hh_internal.h"
+
+namespace hh {
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA kernel
+// ---------------------------------------------------------------------------
+template <int BM_, int BN_, int WM_, int WN_>
+struct GemmCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int BK = 64;                      // bf16 elements per k-tile
+  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+  static constexpr int NWAVES = WAVES_M * WAVES_N;
+  static constexpr int NT = NWAVES * 64;
+  static constexpr int TM = WM / 32, TN = WN / 32;   // 32x32 blocks per wave
+  static constexpr int A_CHUNKS = BM * BK / 8;       // 16-byte chunks per tile
+  static constexpr int B_CHUNKS = BN * BK / 8;
+  static constexpr int A_PER_T = (A_CHUNKS + NT - 1) / NT;
+  static constexpr int B_PER_T = (B_CHUNKS + NT - 1) / NT;
+  static constexpr int STAGE = A_CHUNKS + B_CHUNKS;
+};
+
+// LDS position of 16-byte chunk kc (0..7) of tile row `row`.  Rows are 128 B;
+// XOR-ing the chunk with (row/2)%8 spreads the 32 rows one MFMA operand read
+// touches over all banks.
+__device__ __forceinline__ int swz(int row, int kc) { return row * 8 + (kc ^ ((row >> 1) & 7)); }
+
+// Map the linear block id to an output tile.  Hardware hands consecutive
+// block ids to the 8 XCDs in turn; the remap gives each XCD a contiguous run
+// of logical tiles, and the grouped order (GROUP row-tiles per column sweep)
+// keeps the A rows and B columns of that run in the XCD's own L2.
+__device__ __forceinline__ bool tile_of(int tiles_m, int tiles_n, int &tm, int &tn) {
+  constexpr int GROUP = 8;
+  int bid = blockIdx.x;
+  const int nb = gridDim.x;  // a multiple of 8
+  bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  if (bid >= tiles_m * tiles_n) return false;
+  const int group_size = GROUP * tiles_n;
+  const int first_m = (bid / group_size) * GROUP;
+  const int gm = min(tiles_m - first_m, GROUP);
+  const int in_group = bid % group_size;
+  tm = first_m + in_group % gm;
+  tn = in_group / gm;
+  return true;
+}
+
+template <class Cfg, class Epi>
+__global__ void __launch_bounds__(Cfg::NT)
+gemm_bf16_mfma(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int N, int K,
+               Epi epi) {
+  __shared__ uint4 smem[2 * Cfg::STAGE];
+  int tm, tn;
+  if (!tile_of((M + Cfg::BM - 1) / Cfg::BM, (N + Cfg::BN - 1) / Cfg::BN, tm, tn)) return;
+  const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
+  const int lr = lane & 31, lh = lane >> 5;
+
+  uint4 ra[Cfg::A_PER_T], rb[Cfg::B_PER_T];
+  auto gload = [&](int kt) {
+    const int k0 = kt * Cfg::BK;
+#pragma unroll
+    for (int i = 0; i < Cfg::A_PER_T; ++i) {
+      const int c = tid + i * Cfg::NT;
+      const int r = c >> 3, gk = k0 + (c & 7) * 8;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (c < Cfg::A_CHUNKS && m0 + r < M && gk < K)
+        v = *reinterpret_cast<const uint4 *>(A + (size_t)(m0 + r) * K + gk);
+      ra[i] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg::B_PER_T; ++i) {
+      const int c = tid + i * Cfg::NT;
+      const int r = c >> 3, gk = k0 + (c & 7) * 8;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (c < Cfg::B_CHUNKS && n0 + r < N && gk < K)
+        v = *reinterpret_cast<const uint4 *>(B + (size_t)(n0 + r) * K + gk);
+      rb[i] = v;
+    }
+  };
+  auto sstore = [&](int buf) {
+    uint4 *sA = smem + buf * Cfg::STAGE;
+    uint4 *sB = sA + Cfg::A_CHUNKS;
+#pragma unroll
+    for (int i = 0; i < Cfg::A_PER_T; ++i) {
+      const int c = tid + i * Cfg::NT;
+      if (c < Cfg::A_CHUNKS) sA[swz(c >> 3, c & 7)] = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg::B_PER_T; ++i) {
+      const int c = tid + i * Cfg::NT;
+      if (c < Cfg::B_CHUNKS) sB[swz(c >> 3, c & 7)] = rb[i];
+    }
+  };
+
+  f32x16 acc[Cfg::TM][Cfg::TN];
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int ktiles = (K + Cfg::BK - 1) / Cfg::BK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < ktiles; ++kt) {
+    const bool more = kt + 1 < ktiles;
+    if (more) gload(kt + 1);
+    const uint4 *sA = smem + (kt & 1) * Cfg::STAGE;
+    const uint4 *sB = sA + Cfg::A_CHUNKS;
+#pragma unroll
+    for (int ks = 0; ks < Cfg::BK / 16; ++ks) {
+      bf16x8 af[Cfg::TM], bfr[Cfg::TN];
+#pragma unroll
+      for (int i = 0; i < Cfg::TM; ++i) {
+        const uint4 v = sA[swz(wm * Cfg::WM + i * 32 + lr, ks * 2 + lh)];
+        af[i] = __builtin_bit_cast(bf16x8, v);
+      }
+#pragma unroll
+      for (int j = 0; j < Cfg::TN; ++j) {
+        const uint4 v = sB[swz(wn * Cfg::WN + j * 32 + lr, ks * 2 + lh)];
+        bfr[j] = __builtin_bit_cast(bf16x8, v);
+      }
+#pragma unroll
+      for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) sstore((kt + 1) & 1);
+    __syncthreads();
+  }
+
+  // 32x32 accumulator layout: lane holds column lane%32; register r holds
+  // row 8*(r/4) + 4*(lane/32) + r%4.
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::TN; ++j) {
+      const int col = n0 + wn * Cfg::WN + j * 32 + lr;
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * Cfg::WM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        if (row < M) epi(row, col, acc[i][j][r]);
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel: 64x64 tile, k-step 16, 4x4 outputs per thread
+// ---------------------------------------------------------------------------
+template <class Epi>
+__global__ void __launch_bounds__(256)
+gemm_f32_tiled(const float *__restrict__ A, const float *__restrict__ B, int M, int N, int K,
+               Epi epi) {
+  __shared__ float sA[16][64 + 4];
+  __shared__ float sB[16][64 + 4];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+  for (int k0 = 0; k0 < K; k0 += 16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = threadIdx.x + i * 256;
+      const int r = e >> 4, kk = e & 15;
+      sA[kk][r] = (m0 + r < M && k0 + kk < K) ? A[(size_t)(m0 + r) * K + k0 + kk] : 0.0f;
+      sB[kk][r] = (n0 + r < N && k0 + kk < K) ? B[(size_t)(n0 + r) * K + k0 + kk] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = sA[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = sB[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = m0 + ty * 4 + i, col = n0 + tx * 4 + j;
+      if (row < M && col < N) epi(row, col, acc[i][j]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// epilogues and launchers
+// ---------------------------------------------------------------------------
+template <class T>
+struct InProjEpi {
+  InProjOut e;
+  __device__ __forceinline__ void operator()(int row, int col, float v) const {
+    inproj_store<T>(e, row, col, v);
+  }
+};
+
+template <class T>
+struct StoreEpi {
+  T *out;
+  int ld;
+  __device__ __forceinline__ void operator()(int row, int col, float v) const {
+    out[(size_t)row * ld + col] = from_f32<T>(v);
+  }
+};
+
+template <class Cfg, class Epi>
+static hipError_t run_bf16(const bf16 *A, int M, int K, const bf16 *B, int N, const Epi &epi,
+                           hipStream_t s) {
+  const int tiles = ((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
+  const int grid = (tiles + 7) / 8 * 8;
+  hipLaunchKernelGGL((gemm_bf16_mfma<Cfg, Epi>), dim3(grid), dim3(Cfg::NT), 0, s, A, B, M, N,
+                     K, epi);
+  return hipGetLastError();
+}
+
+using CfgLarge = GemmCfg<256, 256, 128, 128>;
+using CfgSmall = GemmCfg<128, 64, 64, 32>;
+
+template <class Epi>
+static hipError_t run_bf16_auto(const bf16 *A, int M, int K, const bf16 *B, int N, const Epi &epi,
+                                hipStream_t s) {
+  if (M >= 1024) return run_bf16<CfgLarge>(A, M, K, B, N, epi, s);
+  return run_bf16<CfgSmall>(A, M, K, B, N, epi, s);
+}
+
+template <class Epi>
+static hipError_t run_f32(const float *A, int M, int K, const float *B, int N, const Epi &epi,
+                          hipStream_t s) {
+  dim3 grid((N + 63) / 64, (M + 63) / 64);
+  hipLaunchKernelGGL((gemm_f32_tiled<Epi>), grid, dim3(256), 0, s, A, B, M, N, K, epi);
+  return hipGetLastError();
+}
+
+template <>
+hipError_t launch_inproj<bf16>(const bf16 *x, int M, int K, const bf16 *w, int Ncols,
+                               const InProjOut &e, hipStream_t s) {
+  return run_bf16_auto(x, M, K, w, Ncols, InProjEpi<bf16>{e}, s);
+}
+template <>
+hipError_t launch_inproj<float>(const float *x, int M, int K, const float *w, int Ncols,
+                                const InProjOut &e, hipStream_t s) {
+  return run_f32(x, M, K, w, Ncols, InProjEpi<float>{e}, s);
+}
+template <>
+hipError_t launch_outproj<bf16>(const bf16 *f, int M, int K, const bf16 *w, int Ncols, bf16 *out,
+                                hipStream_t s) {
+  return run_bf16_auto(f, M, K, w, Ncols, StoreEpi<bf16>{out, Ncols}, s);
+}
+template <>
+hipError_t launch_outproj<float>(const float *f, int M, int K, const float *w, int Ncols,
+                                 float *out, hipStream_t s) {
+  return run_f32(f, M, K, w, Ncols, StoreEpi<float>{out, Ncols}, s);
+}
+
+}  // namespace hh

@@ -1,0 +1,419 @@
+// C ABI of libhymba_hh: argument validation, workspace layout and the launch
+// sequence of each entry point.  Every check runs on the host before the
+// first launch, so a rejected call touches no buffer.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/hh.h"
+#include "hh_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+hh_status fail(hh_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+hh_status fail(hh_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+hh_status hip_fail(hipError_t e, const char *where) {
+  return fail(HH_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return p && ((uintptr_t)p & 15u) == 0; }
+
+size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct Shape {
+  int d, H, G, hd, D, N, k, m, Wa, KV, n_in, dtype;
+  size_t es;
+  float eps;
+};
+
+hh_status check_dims(const hh_dims *dm, int kv_producer, Shape &s) {
+  if (!dm) return fail(HH_ERR_INVALID_ARG, "dims is NULL");
+  if (dm->dtype != HH_F32 && dm->dtype != HH_BF16)
+    return fail(HH_ERR_INVALID_ARG, "dtype %d is neither HH_F32 nor HH_BF16", dm->dtype);
+  if (dm->d_model <= 0 || dm->n_heads <= 0 || dm->n_kv_heads <= 0 || dm->head_dim <= 0 ||
+      dm->d_inner <= 0 || dm->d_state <= 0 || dm->d_conv <= 0 || dm->n_meta < 0)
+    return fail(HH_ERR_INVALID_ARG, "dimensions must be positive (n_meta >= 0)");
+  if (dm->n_heads % dm->n_kv_heads)
+    return fail(HH_ERR_INVALID_ARG, "n_heads %d is not a multiple of n_kv_heads %d",
+                dm->n_heads, dm->n_kv_heads);
+  if (dm->n_heads / dm->n_kv_heads > 8)
+    return fail(HH_ERR_UNSUPPORTED, "more than 8 query heads per KV head");
+  if (dm->dtype == HH_BF16 ? dm->head_dim != 64 : (dm->head_dim != 32 && dm->head_dim != 64))
+    return fail(HH_ERR_UNSUPPORTED, "head_dim %d not supported for this dtype", dm->head_dim);
+  if (dm->d_state != 16) return fail(HH_ERR_UNSUPPORTED, "d_state %d (only 16)", dm->d_state);
+  if (dm->d_conv < 2 || dm->d_conv > 4)
+    return fail(HH_ERR_UNSUPPORTED, "d_conv %d (2..4 supported)", dm->d_conv);
+  if (dm->d_model % 8 || dm->d_inner % 8 || (dm->n_heads * dm->head_dim) % 8)
+    return fail(HH_ERR_UNSUPPORTED, "d_model, d_inner and n_heads*head_dim must be multiples of 8");
+  if (!(dm->rms_eps >= 0.0f) || dm->rms_eps > 1.0f)
+    return fail(HH_ERR_INVALID_ARG, "rms_eps must be in [0, 1]");
+  s.d = dm->d_model; s.H = dm->n_heads; s.G = dm->n_kv_heads; s.hd = dm->head_dim;
+  s.D = dm->d_inner; s.N = dm->d_state; s.k = dm->d_conv; s.m = dm->n_meta;
+  s.Wa = s.H * s.hd;
+  s.KV = kv_producer ? s.G * s.hd : 0;
+  s.n_in = s.Wa + 2 * s.KV + 3 * s.D + 2 * s.N;
+  s.dtype = dm->dtype;
+  s.es = dm->dtype == HH_BF16 ? 2 : 4;
+  s.eps = dm->rms_eps;
+  return HH_OK;
+}
+
+hh_status check_weights(const hh_weights *w, const Shape &s) {
+  if (!w) return fail(HH_ERR_INVALID_ARG, "weights is NULL");
+  if (!w->w_in || !w->dt_bias || !w->A || !w->conv_w || !w->conv_b || !w->beta_attn ||
+      !w->beta_ssm || !w->w_out)
+    return fail(HH_ERR_INVALID_ARG, "a weight pointer is NULL");
+  if (!aligned16(w->w_in) || !aligned16(w->w_out))
+    return fail(HH_ERR_INVALID_ARG, "w_in and w_out must be 16-byte aligned");
+  (void)s;
+  return HH_OK;
+}
+
+// ---- workspace layouts ----------------------------------------------------
+struct PrefillLayout {
+  size_t off[HH_WS_COUNT];
+  size_t total;
+  int chunk;
+};
+
+PrefillLayout prefill_layout(const Shape &s, int B, int n) {
+  PrefillLayout L;
+  const size_t T = (size_t)B * n;
+  size_t o = 0;
+  auto take = [&](int id, size_t bytes) { L.off[id] = o; o = up256(o + bytes); };
+  for (int i = 0; i < HH_WS_COUNT; ++i) L.off[i] = SIZE_MAX;
+  take(HH_WS_Q, T * s.Wa * s.es);
+  if (s.KV) {
+    take(HH_WS_K, (size_t)B * s.G * n * s.hd * s.es);
+    take(HH_WS_V, (size_t)B * s.G * n * s.hd * s.es);
+  }
+  take(HH_WS_XS, T * s.D * s.es);
+  take(HH_WS_Z, T * s.D * s.es);
+  take(HH_WS_DELTA, T * s.D * 4);
+  take(HH_WS_BC, T * 2 * s.N * 4);
+  take(HH_WS_O, T * s.Wa * s.es);
+  take(HH_WS_Y, T * s.D * s.es);
+  take(HH_WS_F, T * (s.Wa + s.D) * s.es);
+  take(HH_WS_SCAN, hh::scan_carry_bytes(B, n, s.D, s.N, &L.chunk));
+  L.total = o;
+  return L;
+}
+
+struct DecodeLayout {
+  size_t q, xs, z, dt, bc, o, y, f, part, total;
+  int nsplit;
+};
+
+DecodeLayout decode_layout(const Shape &s, int B, int max_real) {
+  DecodeLayout L;
+  size_t o = 0;
+  auto take = [&](size_t &dst, size_t bytes) { dst = o; o = up256(o + bytes); };
+  take(L.q, (size_t)B * s.Wa * s.es);
+  take(L.xs, (size_t)B * s.D * s.es);
+  take(L.z, (size_t)B * s.D * s.es);
+  take(L.dt, (size_t)B * s.D * 4);
+  take(L.bc, (size_t)B * 2 * s.N * 4);
+  take(L.o, (size_t)B * s.Wa * s.es);
+  take(L.y, (size_t)B * s.D * s.es);
+  take(L.f, (size_t)B * (s.Wa + s.D) * s.es);
+  take(L.part, hh::decode_attn_part_bytes(B, s.H, s.hd, s.m, max_real, nullptr, &L.nsplit));
+  L.total = o;
+  return L;
+}
+
+char *at(void *ws, size_t off) { return static_cast<char *>(ws) + off; }
+
+template <class T>
+hh_status run_inproj(const Shape &s, const hh_weights *w, const void *x, int M,
+                     const hh::InProjOut &e, hipStream_t st) {
+  hipError_t err = hh::launch_inproj<T>(static_cast<const T *>(x), M, s.d,
+                                        static_cast<const T *>(w->w_in), s.n_in, e, st);
+  return err == hipSuccess ? HH_OK : hip_fail(err, "input projection");
+}
+
+template <class T>
+hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, int n,
+                    const hh_meta *meta, int window, int is_global, void *out, hh_kv *kv,
+                    hh_ssm_state *state, void *ws, const PrefillLayout &L, hipStream_t st) {
+  const int rows = B * n;
+  const bool prod = w->kv_producer != 0;
+  void *kfull = prod ? ((kv && kv->full_k) ? kv->full_k : at(ws, L.off[HH_WS_K])) : kv->full_k;
+  void *vfull = prod ? ((kv && kv->full_v) ? kv->full_v : at(ws, L.off[HH_WS_V])) : kv->full_v;
+
+  hh::InProjOut e{};
+  e.mode = hh::EPI_PREFILL;
+  e.Wa = s.Wa; e.KV = s.KV; e.D = s.D; e.N = s.N; e.hd = s.hd; e.n_rows_per_seq = n;
+  e.q = at(ws, L.off[HH_WS_Q]);
+  e.k_full = kfull; e.v_full = vfull;
+  if (prod && kv && kv->cache_k) {
+    e.cache_k = kv->cache_k; e.cache_v = kv->cache_v; e.cap = kv->cap; e.is_ring = kv->is_ring;
+  }
+  e.xs = at(ws, L.off[HH_WS_XS]); e.z = at(ws, L.off[HH_WS_Z]);
+  e.dt = reinterpret_cast<float *>(at(ws, L.off[HH_WS_DELTA]));
+  e.bc = reinterpret_cast<float *>(at(ws, L.off[HH_WS_BC]));
+  e.dt_bias = w->dt_bias;
+  hh_status r = run_inproj<T>(s, w, x, rows, e, st);
+  if (r != HH_OK) return r;
+
+  hh::AttnArgs aa{};
+  aa.q = e.q; aa.k = kfull; aa.v = vfull; aa.mk = meta->k; aa.mv = meta->v;
+  aa.o = at(ws, L.off[HH_WS_O]);
+  aa.B = B; aa.n = n; aa.m = s.m; aa.H = s.H; aa.G = s.G; aa.hd = s.hd;
+  aa.window = window; aa.is_global = is_global;
+  hipError_t err = hh::launch_attention<T>(aa, st);
+  if (err != hipSuccess) return hip_fail(err, "attention");
+
+  hh::ScanArgs sa{};
+  sa.xs = e.xs; sa.z = e.z; sa.dt = e.dt; sa.bc = e.bc;
+  sa.A = w->A; sa.conv_w = w->conv_w; sa.conv_b = w->conv_b;
+  sa.h0 = meta->h0; sa.tail0 = meta->conv_tail;
+  sa.y = at(ws, L.off[HH_WS_Y]);
+  sa.h_out = state ? state->h : nullptr;
+  sa.tail_out = state ? state->conv : nullptr;
+  sa.carry = reinterpret_cast<float *>(at(ws, L.off[HH_WS_SCAN]));
+  sa.B = B; sa.n = n; sa.D = s.D; sa.N = s.N; sa.k = s.k; sa.chunk = L.chunk;
+  err = hh::launch_scan<T>(sa, st);
+  if (err != hipSuccess) return hip_fail(err, "selective scan");
+
+  hh::NormArgs na{};
+  na.o = aa.o; na.y = sa.y; na.beta_attn = w->beta_attn; na.beta_ssm = w->beta_ssm;
+  na.f = at(ws, L.off[HH_WS_F]);
+  na.rows = rows; na.Wa = s.Wa; na.D = s.D; na.eps = s.eps;
+  err = hh::launch_norm_fuse<T>(na, st);
+  if (err != hipSuccess) return hip_fail(err, "norm/average");
+
+  err = hh::launch_outproj<T>(static_cast<const T *>(na.f), rows, s.Wa + s.D,
+                              static_cast<const T *>(w->w_out), s.d, static_cast<T *>(out), st);
+  if (err != hipSuccess) return hip_fail(err, "output projection");
+
+  if (prod && kv && kv->len) {
+    err = hh::launch_set_len(kv->len, B, n, st);
+    if (err != hipSuccess) return hip_fail(err, "cache length");
+  }
+  return HH_OK;
+}
+
+template <class T>
+hh_status meta_prefix_t(const Shape &s, const hh_weights *w, const void *R, void *mk, void *mv,
+                        float *h0, void *tail, void *ws, const PrefillLayout &L, hipStream_t st) {
+  hh::InProjOut e{};
+  e.mode = hh::EPI_META;
+  e.Wa = s.Wa; e.KV = s.KV; e.D = s.D; e.N = s.N; e.hd = s.hd; e.n_rows_per_seq = s.m;
+  e.q = at(ws, L.off[HH_WS_Q]);
+  e.k_full = mk; e.v_full = mv;
+  e.xs = at(ws, L.off[HH_WS_XS]); e.z = at(ws, L.off[HH_WS_Z]);
+  e.dt = reinterpret_cast<float *>(at(ws, L.off[HH_WS_DELTA]));
+  e.bc = reinterpret_cast<float *>(at(ws, L.off[HH_WS_BC]));
+  e.dt_bias = w->dt_bias;
+  hh_status r = run_inproj<T>(s, w, R, s.m, e, st);
+  if (r != HH_OK) return r;
+  hh::ScanArgs sa{};
+  sa.xs = e.xs; sa.z = nullptr; sa.dt = e.dt; sa.bc = e.bc;
+  sa.A = w->A; sa.conv_w = w->conv_w; sa.conv_b = w->conv_b;
+  sa.h0 = nullptr; sa.tail0 = nullptr; sa.y = nullptr;
+  sa.h_out = h0; sa.tail_out = tail;
+  sa.carry = reinterpret_cast<float *>(at(ws, L.off[HH_WS_SCAN]));
+  sa.B = 1; sa.n = s.m; sa.D = s.D; sa.N = s.N; sa.k = s.k; sa.chunk = L.chunk;
+  hipError_t err = hh::launch_scan<T>(sa, st);
+  return err == hipSuccess ? HH_OK : hip_fail(err, "meta scan");
+}
+
+template <class T>
+hh_status decode_t(const Shape &s, const hh_weights *w, const void *x, int B, const hh_meta *meta,
+                   int window, int is_global, hh_kv *kv, hh_ssm_state *state, void *out, void *ws,
+                   const DecodeLayout &L, hipStream_t st) {
+  const bool prod = w->kv_producer != 0;
+  hh::InProjOut e{};
+  e.mode = hh::EPI_DECODE;
+  e.Wa = s.Wa; e.KV = s.KV; e.D = s.D; e.N = s.N; e.hd = s.hd; e.n_rows_per_seq = 1;
+  e.q = at(ws, L.q);
+  e.cache_k = kv->cache_k; e.cache_v = kv->cache_v; e.cap = kv->cap; e.is_ring = kv->is_ring;
+  e.len = kv->len;
+  e.xs = at(ws, L.xs); e.z = at(ws, L.z);
+  e.dt = reinterpret_cast<float *>(at(ws, L.dt));
+  e.bc = reinterpret_cast<float *>(at(ws, L.bc));
+  e.dt_bias = w->dt_bias;
+  hh_status r = run_inproj<T>(s, w, x, B, e, st);
+  if (r != HH_OK) return r;
+
+  hh::DecodeAttnArgs da{};
+  da.q = e.q; da.cache_k = kv->cache_k; da.cache_v = kv->cache_v;
+  da.mk = meta->k; da.mv = meta->v; da.len = kv->len; da.producer = prod ? 1 : 0;
+  da.o = at(ws, L.o);
+  da.part = reinterpret_cast<float *>(at(ws, L.part));
+  da.B = B; da.H = s.H; da.G = s.G; da.hd = s.hd; da.m = s.m; da.cap = kv->cap;
+  da.is_ring = kv->is_ring; da.window = window; da.is_global = is_global;
+  da.nsplit = L.nsplit;
+  hipError_t err = hh::launch_decode_attention<T>(da, st);
+  if (err != hipSuccess) return hip_fail(err, "decode attention");
+
+  hh::DecodeSsmArgs sa{};
+  sa.xs = e.xs; sa.z = e.z; sa.dt = e.dt; sa.bc = e.bc;
+  sa.A = w->A; sa.conv_w = w->conv_w; sa.conv_b = w->conv_b;
+  sa.h = state->h; sa.conv = state->conv; sa.y = at(ws, L.y);
+  sa.B = B; sa.D = s.D; sa.N = s.N; sa.k = s.k;
+  err = hh::launch_decode_ssm<T>(sa, st);
+  if (err != hipSuccess) return hip_fail(err, "decode SSM step");
+
+  hh::NormArgs na{};
+  na.o = da.o; na.y = sa.y; na.beta_attn = w->beta_attn; na.beta_ssm = w->beta_ssm;
+  na.f = at(ws, L.f);
+  na.rows = B; na.Wa = s.Wa; na.D = s.D; na.eps = s.eps;
+  err = hh::launch_norm_fuse<T>(na, st);
+  if (err != hipSuccess) return hip_fail(err, "decode norm/average");
+
+  err = hh::launch_outproj<T>(static_cast<const T *>(na.f), B, s.Wa + s.D,
+                              static_cast<const T *>(w->w_out), s.d, static_cast<T *>(out), st);
+  if (err != hipSuccess) return hip_fail(err, "decode output projection");
+  if (prod) {
+    err = hh::launch_bump_len(kv->len, B, kv->cap, kv->is_ring, st);
+    if (err != hipSuccess) return hip_fail(err, "cache length");
+  }
+  return HH_OK;
+}
+
+int max_real_keys(const hh_kv *kv, int window, int is_global) {
+  if (is_global || !kv->is_ring) return kv->cap;
+  return std::min(window, kv->cap);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *hh_version(void) { return "libhymba_hh 0.1.0 gfx950"; }
+
+const char *hh_last_error(void) { return g_err.c_str(); }
+
+size_t hh_prefill_workspace_layout(const hh_dims *dims, int32_t batch, int32_t seqlen,
+                                   int32_t kv_producer, size_t *offs) {
+  Shape s;
+  if (check_dims(dims, kv_producer, s) != HH_OK || batch <= 0 || seqlen <= 0) return 0;
+  PrefillLayout L = prefill_layout(s, batch, seqlen);
+  if (offs) std::memcpy(offs, L.off, sizeof L.off);
+  return L.total;
+}
+
+size_t hh_prefill_workspace_size(const hh_dims *dims, int32_t batch, int32_t seqlen,
+                                 int32_t kv_producer) {
+  return hh_prefill_workspace_layout(dims, batch, seqlen, kv_producer, nullptr);
+}
+
+size_t hh_meta_prefix_workspace_size(const hh_dims *dims, int32_t kv_producer) {
+  if (!dims || dims->n_meta <= 0) return 0;
+  return hh_prefill_workspace_layout(dims, 1, dims->n_meta, kv_producer, nullptr);
+}
+
+size_t hh_decode_workspace_size(const hh_dims *dims, int32_t batch, int32_t cap,
+                                int32_t kv_producer) {
+  Shape s;
+  if (check_dims(dims, kv_producer, s) != HH_OK || batch <= 0 || cap <= 0) return 0;
+  return decode_layout(s, batch, cap).total;
+}
+
+hh_status hh_meta_prefix(const hh_dims *dims, const hh_weights *w, const void *meta_tokens,
+                         void *meta_k, void *meta_v, float *h0, void *conv_tail, void *ws,
+                         size_t ws_bytes, void *stream) {
+  Shape s;
+  hh_status r = check_dims(dims, w ? w->kv_producer : 1, s);
+  if (r != HH_OK) return r;
+  if ((r = check_weights(w, s)) != HH_OK) return r;
+  if (s.m <= 0) return fail(HH_ERR_INVALID_ARG, "n_meta must be positive for hh_meta_prefix");
+  if (!aligned16(meta_tokens)) return fail(HH_ERR_INVALID_ARG, "meta_tokens NULL or not 16-byte aligned");
+  if (s.KV && (!meta_k || !meta_v)) return fail(HH_ERR_INVALID_ARG, "meta_k/meta_v NULL for a producer layer");
+  if (!h0 || !conv_tail) return fail(HH_ERR_INVALID_ARG, "h0/conv_tail NULL");
+  PrefillLayout L = prefill_layout(s, 1, s.m);
+  if (!ws || ws_bytes < L.total)
+    return fail(HH_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, L.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return s.dtype == HH_BF16 ? meta_prefix_t<hh::bf16>(s, w, meta_tokens, meta_k, meta_v, h0, conv_tail, ws, L, st)
+                            : meta_prefix_t<float>(s, w, meta_tokens, meta_k, meta_v, h0, conv_tail, ws, L, st);
+}
+
+hh_status hh_prefill(const hh_dims *dims, const hh_weights *w, const void *x, int32_t batch,
+                     int32_t seqlen, const hh_meta *meta, int32_t window, int32_t is_global,
+                     void *out, hh_kv *kv, hh_ssm_state *state, void *ws, size_t ws_bytes,
+                     void *stream) {
+  Shape s;
+  hh_status r = check_dims(dims, w ? w->kv_producer : 1, s);
+  if (r != HH_OK) return r;
+  if ((r = check_weights(w, s)) != HH_OK) return r;
+  if (batch <= 0 || seqlen <= 0) return fail(HH_ERR_INVALID_ARG, "batch and seqlen must be positive");
+  if ((long long)batch * seqlen > (1LL << 30))
+    return fail(HH_ERR_UNSUPPORTED, "batch*seqlen above 2^30 tokens");
+  if (!is_global && window < 1) return fail(HH_ERR_INVALID_ARG, "window must be >= 1");
+  if (!aligned16(x) || !aligned16(out)) return fail(HH_ERR_INVALID_ARG, "x/out NULL or not 16-byte aligned");
+  if (!meta) return fail(HH_ERR_INVALID_ARG, "meta is NULL");
+  if (s.m > 0 && (!aligned16(meta->k) || !aligned16(meta->v)))
+    return fail(HH_ERR_INVALID_ARG, "meta k/v NULL or not 16-byte aligned");
+  if (!w->kv_producer) {
+    if (!kv || !aligned16(kv->full_k) || !aligned16(kv->full_v))
+      return fail(HH_ERR_INVALID_ARG, "a consumer layer needs its producer's full_k/full_v");
+  }
+  if (w->kv_producer && kv) {
+    if ((kv->full_k && !aligned16(kv->full_k)) || (kv->full_v && !aligned16(kv->full_v)) ||
+        (!kv->full_k) != (!kv->full_v))
+      return fail(HH_ERR_INVALID_ARG, "full_k/full_v must both be NULL or both 16-byte aligned");
+    if ((!kv->cache_k) != (!kv->cache_v))
+      return fail(HH_ERR_INVALID_ARG, "cache_k/cache_v must both be set or both NULL");
+    if (kv->cache_k) {
+      if (kv->cap < 1) return fail(HH_ERR_INVALID_ARG, "cache cap must be >= 1");
+      if (kv->is_ring && is_global) return fail(HH_ERR_INVALID_ARG, "a global layer needs a linear cache");
+      if (kv->is_ring && window > kv->cap)
+        return fail(HH_ERR_INVALID_ARG, "ring cache cap %d below window %d", kv->cap, window);
+    }
+  }
+  PrefillLayout L = prefill_layout(s, batch, seqlen);
+  if (!ws || ws_bytes < L.total)
+    return fail(HH_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, L.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return s.dtype == HH_BF16
+             ? prefill_t<hh::bf16>(s, w, x, batch, seqlen, meta, window, is_global, out, kv, state, ws, L, st)
+             : prefill_t<float>(s, w, x, batch, seqlen, meta, window, is_global, out, kv, state, ws, L, st);
+}
+
+hh_status hh_decode_step(const hh_dims *dims, const hh_weights *w, const void *x_t, int32_t batch,
+                         const hh_meta *meta, int32_t window, int32_t is_global, hh_kv *kv,
+                         hh_ssm_state *state, void *out, void *ws, size_t ws_bytes, void *stream) {
+  Shape s;
+  hh_status r = check_dims(dims, w ? w->kv_producer : 1, s);
+  if (r != HH_OK) return r;
+  if ((r = check_weights(w, s)) != HH_OK) return r;
+  if (batch <= 0) return fail(HH_ERR_INVALID_ARG, "batch must be positive");
+  if (!is_global && window < 1) return fail(HH_ERR_INVALID_ARG, "window must be >= 1");
+  if (!aligned16(x_t) || !aligned16(out)) return fail(HH_ERR_INVALID_ARG, "x_t/out NULL or not 16-byte aligned");
+  if (!meta) return fail(HH_ERR_INVALID_ARG, "meta is NULL");
+  if (s.m > 0 && (!aligned16(meta->k) || !aligned16(meta->v)))
+    return fail(HH_ERR_INVALID_ARG, "meta k/v NULL or not 16-byte aligned");
+  if (!kv || !aligned16(kv->cache_k) || !aligned16(kv->cache_v) || !kv->len)
+    return fail(HH_ERR_INVALID_ARG, "decode needs cache_k, cache_v and len");
+  if (kv->cap < 1) return fail(HH_ERR_INVALID_ARG, "cache cap must be >= 1");
+  if (kv->is_ring && is_global) return fail(HH_ERR_INVALID_ARG, "a global layer needs a linear cache");
+  if (kv->is_ring && window > kv->cap)
+    return fail(HH_ERR_INVALID_ARG, "ring cache cap %d below window %d", kv->cap, window);
+  if (!state || !aligned16(state->h) || !state->conv)
+    return fail(HH_ERR_INVALID_ARG, "decode needs the SSM state h and conv");
+  DecodeLayout L = decode_layout(s, batch, max_real_keys(kv, window, is_global));
+  if (!ws || ws_bytes < L.total)
+    return fail(HH_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, L.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return s.dtype == HH_BF16
+             ? decode_t<hh::bf16>(s, w, x_t, batch, meta, window, is_global, kv, state, out, ws, L, st)
+             : decode_t<float>(s, w, x_t, batch, meta, window, is_global, kv, state, out, ws, L, st);
+}
+
+}  // extern "C"

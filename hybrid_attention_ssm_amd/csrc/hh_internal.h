@@ -1,0 +1,184 @@
+// Internal declarations shared by the HIP translation units of libhymba_hh.
+// Device helpers, the in-projection column map and the kernel launchers that
+// hh_api.cpp drives.  Not part of the public ABI (include/hh.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace hh {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---- scalar conversions ----------------------------------------------------
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+template <class T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+// round to nearest even (hardware v_cvt on gfx950)
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
+
+// ---- fast transcendental helpers (fp32) ------------------------------------
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
+// x * sigmoid(x) with sigmoid = 1 / (1 + 2^(-x log2 e)); saturates cleanly:
+// x -> -inf gives 2^(+inf) = inf, rcp(inf) = 0.
+__device__ __forceinline__ float silu_f(float x) {
+  return x * rcp_fast(1.0f + exp2_fast(-x * kLog2e));
+}
+// log(1 + e^v) without overflow: max(v, 0) + log1p(e^-|v|)
+__device__ __forceinline__ float softplus_f(float v) {
+  return fmaxf(v, 0.0f) + log1pf(__expf(-fabsf(v)));
+}
+
+// ---- the in-projection column map ------------------------------------------
+// Columns of P = X W_in^T: Q [0, Wa) | K [Wa, Wa+KV) | V [Wa+KV, Wa+2KV) |
+// xs (D) | z (D) | dt (D) | B (N) | C (N); KV = 0 for a consumer layer.
+enum EpiMode : int { EPI_PREFILL = 0, EPI_DECODE = 1, EPI_META = 2 };
+
+struct InProjOut {
+  int mode;
+  int Wa, KV, D, N, hd, n_rows_per_seq;  // n_rows_per_seq: seqlen (prefill) or m (meta)
+  void *q;                    // [rows, Wa]
+  void *k_full, *v_full;      // prefill: [B, G, n, hd]; meta: [G, m, hd]
+  void *cache_k, *cache_v;    // prefill/decode cache [B, G, cap, hd] (may be null)
+  int cap, is_ring;
+  const int32_t *len;         // decode: position of the new token per row
+  void *xs, *z;               // [rows, D]
+  float *dt;                  // [rows, D] softplus(dt + bias)
+  float *bc;                  // [rows, 2N] B then C
+  const float *dt_bias;       // [D]
+};
+
+template <class T>
+__device__ __forceinline__ void inproj_store(const InProjOut &e, int row, int col, float v) {
+  const int Wa = e.Wa, KV = e.KV, D = e.D;
+  if (col < Wa) {
+    reinterpret_cast<T *>(e.q)[(size_t)row * Wa + col] = from_f32<T>(v);
+    return;
+  }
+  col -= Wa;
+  if (col < 2 * KV) {
+    const bool isv = col >= KV;
+    const int c = isv ? col - KV : col;
+    const int g = c / e.hd, d = c - g * e.hd;
+    const int G = KV / e.hd;
+    const T tv = from_f32<T>(v);
+    if (e.mode == EPI_DECODE) {
+      const int p = e.len[row];
+      const int slot = e.is_ring ? p % e.cap : p;
+      if (p < 0 || (!e.is_ring && p >= e.cap)) return;
+      T *dst = reinterpret_cast<T *>(isv ? e.cache_v : e.cache_k);
+      dst[(((size_t)row * G + g) * e.cap + slot) * e.hd + d] = tv;
+      return;
+    }
+    const int n = e.n_rows_per_seq;
+    const int b = row / n, p = row - b * n;
+    T *full = reinterpret_cast<T *>(isv ? e.v_full : e.k_full);
+    full[(((size_t)b * G + g) * n + p) * e.hd + d] = tv;
+    if (e.mode == EPI_PREFILL && e.cache_k) {
+      bool keep;
+      int slot;
+      if (e.is_ring) { keep = p >= n - e.cap; slot = p % e.cap; }
+      else { keep = p < e.cap; slot = p; }
+      if (keep) {
+        T *dst = reinterpret_cast<T *>(isv ? e.cache_v : e.cache_k);
+        dst[(((size_t)b * G + g) * e.cap + slot) * e.hd + d] = tv;
+      }
+    }
+    return;
+  }
+  col -= 2 * KV;
+  if (col < D) { reinterpret_cast<T *>(e.xs)[(size_t)row * D + col] = from_f32<T>(v); return; }
+  col -= D;
+  if (col < D) { reinterpret_cast<T *>(e.z)[(size_t)row * D + col] = from_f32<T>(v); return; }
+  col -= D;
+  if (col < D) { e.dt[(size_t)row * D + col] = softplus_f(v + e.dt_bias[col]); return; }
+  col -= D;
+  e.bc[(size_t)row * 2 * e.N + col] = v;
+}
+
+// ---- launchers (each returns hipGetLastError() of its launches) ------------
+template <class T>
+hipError_t launch_inproj(const T *x, int M, int K, const T *w, int Ncols,
+                         const InProjOut &epi, hipStream_t s);
+template <class T>
+hipError_t launch_outproj(const T *f, int M, int K, const T *w, int Ncols, T *out,
+                          hipStream_t s);
+
+struct AttnArgs {
+  const void *q;           // [B*n, H*hd]
+  const void *k, *v;       // real keys [B, G, n, hd]
+  const void *mk, *mv;     // meta keys [G, m, hd]
+  void *o;                 // [B*n, H*hd]
+  int B, n, m, H, G, hd, window, is_global;
+};
+template <class T> hipError_t launch_attention(const AttnArgs &a, hipStream_t s);
+
+struct ScanArgs {
+  const void *xs, *z;      // [B*n, D] (z may be null: no gate, no Y)
+  const float *dt;         // [B*n, D]
+  const float *bc;         // [B*n, 2N]
+  const float *A;          // [D, N]
+  const float *conv_w;     // [D, k]
+  const float *conv_b;     // [D]
+  const float *h0;         // [D, N] initial state (null: zero)
+  const void *tail0;       // [k-1, D] conv history (null: zero)
+  void *y;                 // [B*n, D] (null: not written)
+  float *h_out;            // [B, D, N] (null: not written)
+  void *tail_out;          // [B, k-1, D] (null: not written)
+  float *carry;            // workspace for chunk carries
+  int B, n, D, N, k;
+  int chunk;               // time steps per chunk
+};
+template <class T> hipError_t launch_scan(const ScanArgs &a, hipStream_t s);
+size_t scan_carry_bytes(int B, int n, int D, int N, int *chunk_out);
+
+struct NormArgs {
+  const void *o;           // [rows, Wa]
+  const void *y;           // [rows, D]
+  const float *beta_attn, *beta_ssm;
+  void *f;                 // [rows, Wa + D]
+  int rows, Wa, D;
+  float eps;
+};
+template <class T> hipError_t launch_norm_fuse(const NormArgs &a, hipStream_t s);
+
+struct DecodeAttnArgs {
+  const void *q;           // [B, H*hd]
+  const void *cache_k, *cache_v;  // [B, G, cap, hd]
+  const void *mk, *mv;     // [G, m, hd]
+  const int32_t *len;
+  int producer;            // 1: new token at len[b]; 0: at len[b]-1
+  void *o;                 // [B, H*hd]
+  float *part;             // split partials
+  int B, H, G, hd, m, cap, is_ring, window, is_global, split, nsplit;
+};
+template <class T> hipError_t launch_decode_attention(const DecodeAttnArgs &a, hipStream_t s);
+size_t decode_attn_part_bytes(int B, int H, int hd, int m, int max_real,
+                              int *split_out, int *nsplit_out);
+
+struct DecodeSsmArgs {
+  const void *xs, *z;      // [B, D]
+  const float *dt, *bc;    // [B, D], [B, 2N]
+  const float *A, *conv_w, *conv_b;
+  float *h;                // [B, D, N] in/out
+  void *conv;              // [B, k-1, D] in/out
+  void *y;                 // [B, D]
+  int B, D, N, k;
+};
+template <class T> hipError_t launch_decode_ssm(const DecodeSsmArgs &a, hipStream_t s);
+
+hipError_t launch_set_len(int32_t *len, int B, int value, hipStream_t s);
+hipError_t launch_bump_len(int32_t *len, int B, int cap, int is_ring, hipStream_t s);
+
+}  // namespace hh

@@ -1,0 +1,71 @@
+// Fusion of the two branches (Hymba paper §2.1 Eq. (3) with the "average"
+// of its text and the mean fusion of Appendix B):
+//   F = 1/2 [beta_attn * O / rms(O) || beta_ssm * Y / rms(Y)],
+//   rms(v) = sqrt(mean(v^2) + eps), statistics in fp32.
+// One wavefront per token row; the two halves are written side by side so a
+// single output projection over [H*hd + D] columns follows.
+#include "hh_internal.h"
+
+namespace hh {
+
+namespace {
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+template <class T> struct Vec;
+template <> struct Vec<bf16> { static constexpr int W = 8; typedef bf16x8 type; };
+template <> struct Vec<float> { static constexpr int W = 4; typedef f32x4 type; };
+
+template <class T>
+__device__ __forceinline__ float sumsq(const T *p, int n, int lane) {
+  constexpr int W = Vec<T>::W;
+  typedef typename Vec<T>::type V;
+  float s = 0.0f;
+  for (int i = lane * W; i < n; i += 64 * W) {
+    const V v = *reinterpret_cast<const V *>(p + i);
+#pragma unroll
+    for (int e = 0; e < W; ++e) { const float f = to_f32(v[e]); s = fmaf(f, f, s); }
+  }
+  return wave_sum(s);
+}
+
+template <class T>
+__device__ __forceinline__ void scaled(const T *p, const float *beta, float r, T *dst, int n, int lane) {
+  constexpr int W = Vec<T>::W;
+  typedef typename Vec<T>::type V;
+  for (int i = lane * W; i < n; i += 64 * W) {
+    const V v = *reinterpret_cast<const V *>(p + i);
+    V o;
+#pragma unroll
+    for (int e = 0; e < W; ++e) o[e] = from_f32<T>(0.5f * beta[i + e] * to_f32(v[e]) * r);
+    *reinterpret_cast<V *>(dst + i) = o;
+  }
+}
+}  // namespace
+
+template <class T>
+__global__ void __launch_bounds__(256) norm_fuse(NormArgs a) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= a.rows) return;
+  const T *o = reinterpret_cast<const T *>(a.o) + (size_t)row * a.Wa;
+  const T *y = reinterpret_cast<const T *>(a.y) + (size_t)row * a.D;
+  T *f = reinterpret_cast<T *>(a.f) + (size_t)row * (a.Wa + a.D);
+  const float ro = 1.0f / sqrtf(sumsq(o, a.Wa, lane) / (float)a.Wa + a.eps);
+  const float ry = 1.0f / sqrtf(sumsq(y, a.D, lane) / (float)a.D + a.eps);
+  scaled(o, a.beta_attn, ro, f, a.Wa, lane);
+  scaled(y, a.beta_ssm, ry, f + a.Wa, a.D, lane);
+}
+
+template <class T>
+hipError_t launch_norm_fuse(const NormArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(norm_fuse<T>, dim3((a.rows + 3) / 4), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+template hipError_t launch_norm_fuse<float>(const NormArgs &, hipStream_t);
+template hipError_t launch_norm_fuse<bf16>(const NormArgs &, hipStream_t);
+
+}  // namespace hh

@@ -1,0 +1,227 @@
+// SSM heads of the hybrid-head layer, prefill
+// (Hymba paper §2.1 Eq. (2): the Mamba selective scan with input-dependent
+// Delta, B, C and the output gate G; the conv1d + SiLU on the SSM input and
+// SiLU on the gate follow Mamba, which the paper adopts for its SSM heads).
+//
+//   u_t = SiLU(conv_b + sum_j conv_w[j] * xs_{t-(k-1)+j})
+//   h_t = exp(Delta_t A) * h_{t-1} + Delta_t u_t B_t      (per channel, N states)
+//   y_t = h_t . C_t,   Y_t = y_t * SiLU(z_t)
+//
+// One lane owns one channel and keeps its N = 16 states in registers; B_t and
+// C_t are the same for every channel, so each wavefront reads them as uniform
+// (scalar) loads while xs, Delta and z are read coalesced across 64 channels.
+// exp(Delta A) is evaluated as 2^(Delta * A log2 e).
+//
+// Time is cut into chunks so that a single sequence fills the GPU:
+//   pass 1 (chunks 0..C-2): scan each chunk from a zero state; keep its end
+//          state and sum(Delta) (the chunk's total decay is exp(A sum Delta));
+//   pass 2: per channel, combine the chunk summaries in order starting from
+//          the meta state h0: H_c = exp(A S_c) H_{c-1} + h_c;
+//   pass 3 (all chunks): rescan each chunk from its true incoming state and
+//          write Y; the last chunk writes the final state and conv history.
+// With one chunk only pass 3 runs.
+#include "hh_internal.h"
+
+namespace hh {
+
+namespace {
+constexpr int NS = 16;      // SSM state size
+constexpr int KC = 4;       // conv taps held (shorter kernels are zero-padded)
+constexpr int TB = 8;       // time steps loaded per batch
+
+struct ChanParams {
+  float A2[NS];             // A * log2(e)
+  float w[KC];              // conv taps, w[KC-1] multiplies the current row
+  float bias;
+};
+
+__device__ __forceinline__ void load_params(const ScanArgs &a, int c, ChanParams &p) {
+#pragma unroll
+  for (int s = 0; s < NS; ++s) p.A2[s] = a.A[(size_t)c * NS + s] * kLog2e;
+#pragma unroll
+  for (int j = 0; j < KC; ++j) {
+    const int src = j - (KC - a.k);          // zero-pad taps in front
+    p.w[j] = src >= 0 ? a.conv_w[(size_t)c * a.k + src] : 0.0f;
+  }
+  p.bias = a.conv_b[c];
+}
+
+// history: hist[0] = xs_{t0-1}, hist[1] = xs_{t0-2}, hist[2] = xs_{t0-3}
+template <class T>
+__device__ __forceinline__ void load_history(const ScanArgs &a, int b, int c, int t0, float hist[KC - 1]) {
+  const T *xs = reinterpret_cast<const T *>(a.xs);
+  const T *tail = reinterpret_cast<const T *>(a.tail0);
+#pragma unroll
+  for (int j = 0; j < KC - 1; ++j) {
+    const int pos = t0 - 1 - j;
+    float v = 0.0f;
+    if (pos >= 0) v = to_f32(xs[((size_t)b * a.n + pos) * a.D + c]);
+    else if (tail && (a.k - 1) + pos >= 0) v = to_f32(tail[(size_t)((a.k - 1) + pos) * a.D + c]);
+    hist[j] = v;
+  }
+}
+
+// The scan over [t0, t1) of sequence b for channel c.  MODE 0: summary
+// (end state and sum of Delta); MODE 1: output (Y, and final state/history).
+template <class T, int MODE>
+__device__ __forceinline__ void scan_range(const ScanArgs &a, int b, int c, int t0, int t1,
+                                           const ChanParams &p, float h[NS], float hist[KC - 1],
+                                           float &dsum) {
+  const T *xs = reinterpret_cast<const T *>(a.xs);
+  const T *z = reinterpret_cast<const T *>(a.z);
+  T *y = reinterpret_cast<T *>(a.y);
+  const size_t D = a.D;
+  for (int tb = t0; tb < t1; tb += TB) {
+    float xv[TB], dv[TB], zv[TB];
+#pragma unroll
+    for (int i = 0; i < TB; ++i) {
+      const int t = tb + i;
+      const size_t idx = ((size_t)b * a.n + t) * D + c;
+      const bool in = t < t1;
+      xv[i] = in ? to_f32(xs[idx]) : 0.0f;
+      dv[i] = in ? a.dt[idx] : 0.0f;
+      if (MODE == 1) zv[i] = (in && z) ? to_f32(z[idx]) : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < TB; ++i) {
+      const int t = tb + i;
+      if (t >= t1) break;
+      const float cv = p.bias + p.w[3] * xv[i] + p.w[2] * hist[0] + p.w[1] * hist[1] + p.w[0] * hist[2];
+      hist[2] = hist[1];
+      hist[1] = hist[0];
+      hist[0] = xv[i];
+      const float u = silu_f(cv);
+      const float dt = dv[i];
+      const float du = dt * u;
+      const float *bc = a.bc + ((size_t)b * a.n + t) * (2 * NS);
+      float acc = 0.0f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const float decay = exp2_fast(dt * p.A2[s]);
+        h[s] = fmaf(decay, h[s], du * bc[s]);
+        if (MODE == 1) acc = fmaf(bc[NS + s], h[s], acc);
+      }
+      if (MODE == 0) dsum += dt;
+      if (MODE == 1 && y) y[((size_t)b * a.n + t) * D + c] = from_f32<T>(acc * silu_f(zv[i]));
+    }
+  }
+}
+
+}  // namespace
+
+// pass 1: summaries of chunks 0..C-2.  grid (C-1, ceil(D/64), B), 64 threads
+template <class T>
+__global__ void __launch_bounds__(64) scan_pass1(ScanArgs a) {
+  const int ck = blockIdx.x, b = blockIdx.z;
+  const int c = blockIdx.y * 64 + threadIdx.x;
+  if (c >= a.D) return;
+  const int nc = (a.n + a.chunk - 1) / a.chunk;
+  ChanParams p;
+  load_params(a, c, p);
+  const int t0 = ck * a.chunk, t1 = min(a.n, t0 + a.chunk);
+  float hist[KC - 1];
+  load_history<T>(a, b, c, t0, hist);
+  float h[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) h[s] = 0.0f;
+  float dsum = 0.0f;
+  scan_range<T, 0>(a, b, c, t0, t1, p, h, hist, dsum);
+  // carry layout: [B][nc][NS][D] states, then [B][nc][D] delta sums
+  float *hs = a.carry + ((size_t)b * nc + ck) * NS * a.D;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) hs[(size_t)s * a.D + c] = h[s];
+  float *ds = a.carry + (size_t)a.B * nc * NS * a.D;
+  ds[((size_t)b * nc + ck) * a.D + c] = dsum;
+}
+
+// pass 2: chunk carries in order.  grid (ceil(D/64), B)
+__global__ void __launch_bounds__(64) scan_pass2(ScanArgs a) {
+  const int b = blockIdx.y;
+  const int c = blockIdx.x * 64 + threadIdx.x;
+  if (c >= a.D) return;
+  const int nc = (a.n + a.chunk - 1) / a.chunk;
+  float A2[NS], H[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    A2[s] = a.A[(size_t)c * NS + s] * kLog2e;
+    H[s] = a.h0 ? a.h0[(size_t)c * NS + s] : 0.0f;
+  }
+  const float *ds = a.carry + (size_t)a.B * nc * NS * a.D;
+  for (int ck = 0; ck + 1 < nc; ++ck) {
+    float *hs = a.carry + ((size_t)b * nc + ck) * NS * a.D;
+    const float S = ds[((size_t)b * nc + ck) * a.D + c];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      H[s] = fmaf(exp2_fast(A2[s] * S), H[s], hs[(size_t)s * a.D + c]);
+      hs[(size_t)s * a.D + c] = H[s];   // state entering chunk ck+1
+    }
+  }
+}
+
+// pass 3: outputs of every chunk.  grid (C, ceil(D/64), B)
+template <class T>
+__global__ void __launch_bounds__(64) scan_pass3(ScanArgs a) {
+  const int ck = blockIdx.x, b = blockIdx.z;
+  const int c = blockIdx.y * 64 + threadIdx.x;
+  if (c >= a.D) return;
+  const int nc = (a.n + a.chunk - 1) / a.chunk;
+  ChanParams p;
+  load_params(a, c, p);
+  const int t0 = ck * a.chunk, t1 = min(a.n, t0 + a.chunk);
+  float hist[KC - 1];
+  load_history<T>(a, b, c, t0, hist);
+  float h[NS];
+  if (ck == 0) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) h[s] = a.h0 ? a.h0[(size_t)c * NS + s] : 0.0f;
+  } else {
+    const float *hs = a.carry + ((size_t)b * nc + ck - 1) * NS * a.D;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) h[s] = hs[(size_t)s * a.D + c];
+  }
+  float dsum = 0.0f;
+  scan_range<T, 1>(a, b, c, t0, t1, p, h, hist, dsum);
+  if (ck == nc - 1) {
+    if (a.h_out) {
+      float *ho = a.h_out + ((size_t)b * a.D + c) * NS;
+#pragma unroll
+      for (int s = 0; s < NS; s += 4)
+        *reinterpret_cast<float4 *>(ho + s) = make_float4(h[s], h[s + 1], h[s + 2], h[s + 3]);
+    }
+    if (a.tail_out) {
+      T *to = reinterpret_cast<T *>(a.tail_out) + (size_t)b * (a.k - 1) * a.D;
+      for (int j = 0; j < a.k - 1; ++j) to[(size_t)j * a.D + c] = from_f32<T>(hist[a.k - 2 - j]);
+    }
+  }
+}
+
+size_t scan_carry_bytes(int B, int n, int D, int N, int *chunk_out) {
+  // enough (channel-wave x chunk) work items to fill 256 CUs several times
+  const int cw = (D + 63) / 64;
+  const long waves = (long)B * cw;
+  int nc = (int)((4096 + waves - 1) / waves);
+  nc = std::max(1, std::min(nc, (n + 63) / 64));
+  int chunk = (n + nc - 1) / nc;
+  chunk = (chunk + 7) / 8 * 8;
+  if (chunk < 8) chunk = 8;
+  nc = (n + chunk - 1) / chunk;
+  if (chunk_out) *chunk_out = chunk;
+  return (size_t)B * nc * (N + 1) * D * sizeof(float);
+}
+
+template <class T>
+hipError_t launch_scan(const ScanArgs &a, hipStream_t s) {
+  const int nc = (a.n + a.chunk - 1) / a.chunk;
+  const int cw = (a.D + 63) / 64;
+  if (nc > 1) {
+    hipLaunchKernelGGL(scan_pass1<T>, dim3(nc - 1, cw, a.B), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(scan_pass2, dim3(cw, a.B), dim3(64), 0, s, a);
+  }
+  hipLaunchKernelGGL(scan_pass3<T>, dim3(nc, cw, a.B), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+template hipError_t launch_scan<float>(const ScanArgs &, hipStream_t);
+template hipError_t launch_scan<bf16>(const ScanArgs &, hipStream_t);
+
+}  // namespace hh

@@ -1,0 +1,223 @@
+/*
+ * libhymba_hh -- the Hymba hybrid-head layer on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every tensor argument is a DEVICE pointer to row-major memory owned
+ * by the caller; the library never allocates, frees or keeps a pointer after a
+ * call returns.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ * stream) and the calls return without synchronising.
+ *
+ * Errors: a call returns HH_OK or an error code and never throws.  Arguments
+ * are validated on the host BEFORE anything is enqueued, so on an error no
+ * buffer has been touched; hh_last_error() then holds a message (per thread).
+ * HH_ERR_HIP reports a failed kernel launch; output buffers may then be
+ * partially written.
+ *
+ * What the layer computes (the method of "Hymba: A Hybrid-head Architecture
+ * for Small Language Models", arXiv 2411.13676, and the authors' OpenReview
+ * replies on implementation details):
+ *   X~ = [R; X]                   meta tokens R prepended          (§2.3, Eq. 4)
+ *   P  = X~ W_in^T                one fused input projection       (§2.1)
+ *        columns Q | K | V | xs | z | dt | B | C  (K, V absent in a KV-sharing
+ *        consumer layer, which reads its producer's K/V)  (reply on cache
+ *        optimisation; §2.2 cross-layer KV sharing)
+ *   O  = softmax(Q K^T / sqrt(hd)) V per head, grouped-query (head h reads KV
+ *        head h / (H/G)), over all meta keys plus the real keys j with
+ *        i - W < j <= i (sliding window) or j <= i (global layer)
+ *        (§2.1 Eq. 1, §2.2, reply on the "A-shape" mask and the 1/sqrt(d) scale)
+ *   u  = SiLU(causal depthwise conv_k(xs) + conv_b)
+ *   Delta = softplus(dt + dt_bias)
+ *   h_t = exp(Delta_t A) h_{t-1} + Delta_t u_t B_t,  y_t = h_t . C_t,
+ *   Y  = y * SiLU(z)                                        (§2.1 Eq. 2)
+ *   F  = 1/2 [beta_attn * rmsnorm(O) || beta_ssm * rmsnorm(Y)]
+ *   out = F W_out^T                                         (§2.1 Eq. 3)
+ * The meta rows depend on nothing but the weights, so their part (meta K/V,
+ * SSM state and conv history after the meta rows) is computed once by
+ * hh_meta_prefix and reused (§2.3: computed offline, a learned cache
+ * initialisation).
+ *
+ * Storage types: `dtype` (HH_F32 or HH_BF16) is the element type of x, out,
+ * meta tokens, W_in, W_out, K/V buffers and caches, and the conv history.
+ * dt_bias, A, conv_w, conv_b, the betas and the SSM state h are always fp32.
+ * The bf16 path accumulates in fp32 and keeps Delta, B, C, softmax, norms and
+ * the SSM state in fp32.
+ *
+ * Supported shapes: head_dim 32 or 64 (bf16: 64); n_heads a multiple of
+ * n_kv_heads with at most 8 query heads per KV head; d_state 16; d_conv 2..4;
+ * d_model, n_heads*head_dim + d_inner and d_inner multiples of 8.
+ */
+#ifndef HH_H
+#define HH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { HH_F32 = 0, HH_BF16 = 1 } hh_dtype;
+
+typedef enum {
+  HH_OK = 0,
+  HH_ERR_INVALID_ARG = 1,  /* null pointer, bad size, inconsistent shape */
+  HH_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. head_dim 128) */
+  HH_ERR_WORKSPACE = 3,    /* ws_bytes smaller than the *_workspace_size */
+  HH_ERR_HIP = 4           /* a HIP launch failed */
+} hh_status;
+
+/* Layer shape.  n_heads = H query heads, n_kv_heads = G query groups,
+ * d_inner = D SSM channels, d_state = N, d_conv = k taps, n_meta = m. */
+typedef struct {
+  int32_t d_model, n_heads, n_kv_heads, head_dim;
+  int32_t d_inner, d_state, d_conv, n_meta;
+  int32_t dtype;   /* hh_dtype */
+  float rms_eps;   /* epsilon inside the RMS norm of both branches */
+} hh_dims;
+
+/* One layer's parameters (all device pointers, read only).
+ *   w_in      [n_in, d_model] dtype, rows Q (H*hd) | K (G*hd) | V (G*hd) |
+ *             xs (D) | z (D) | dt (D) | B (N) | C (N); the K and V rows are
+ *             absent when kv_producer == 0 (n_in = H*hd + 3D + 2N).
+ *   dt_bias   [D] fp32       A [D, N] fp32 (negative)
+ *   conv_w    [D, k] fp32 (tap k-1 multiplies the current row)   conv_b [D] fp32
+ *   beta_attn [H*hd] fp32    beta_ssm [D] fp32
+ *   w_out     [d_model, H*hd + D] dtype
+ *   kv_producer: 1 = computes and stores K/V; 0 = KV-sharing consumer. */
+typedef struct {
+  const void *w_in;
+  const float *dt_bias;
+  const float *A;
+  const float *conv_w;
+  const float *conv_b;
+  const float *beta_attn;
+  const float *beta_ssm;
+  const void *w_out;
+  int32_t kv_producer;
+} hh_weights;
+
+/* A layer's meta-token part, shared by every sequence (pinned, read only).
+ *   k, v       [G, m, hd] dtype: meta keys/values (a consumer layer passes
+ *              its producer's)
+ *   h0         [D, N] fp32: SSM state after the m meta rows
+ *   conv_tail  [k-1, D] dtype: xs of the last k-1 meta rows (oldest first) */
+typedef struct {
+  const void *k, *v;
+  const float *h0;
+  const void *conv_tail;
+} hh_meta;
+
+/* K/V of real tokens.
+ *   full_k, full_v  [B, G, seqlen, hd] dtype: prefill K/V of every real
+ *                   token.  A producer writes them (NULL: kept in the
+ *                   workspace only); a consumer reads its producer's here.
+ *   cache_k, cache_v [B, G, cap, hd] dtype: decode cache.  Real position p
+ *                   lives in slot p % cap when is_ring, else slot p.  Prefill
+ *                   by a producer fills the slots of the last min(seqlen, cap)
+ *                   positions (ring) or of positions < seqlen (linear); NULL
+ *                   skips the cache.
+ *   len             [B] int32: real positions held.  Prefill by a producer sets
+ *                   it to seqlen (NULL skips).  Decode: a producer appends at
+ *                   position len[b] and then increments len[b]; a consumer
+ *                   attends up to position len[b]-1 (the token its producer
+ *                   appended this step) and writes nothing.  A producer's
+ *                   decode on a linear cache with len[b] >= cap writes no slot
+ *                   and leaves len[b] unchanged for that sequence.
+ *   cap, is_ring    slots per sequence and head; ring caches need window <= cap. */
+typedef struct {
+  void *full_k, *full_v;
+  void *cache_k, *cache_v;
+  int32_t *len;
+  int32_t cap;
+  int32_t is_ring;
+} hh_kv;
+
+/* Per-sequence SSM state.
+ *   h     [B, D, N] fp32
+ *   conv  [B, k-1, D] dtype: xs of the last k-1 positions, oldest first. */
+typedef struct {
+  float *h;
+  void *conv;
+} hh_ssm_state;
+
+/* Library version string, e.g. "libhymba_hh 0.1.0 gfx950". */
+const char *hh_version(void);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *hh_last_error(void);
+
+/* Bytes of device workspace hh_meta_prefix needs (0 on invalid dims). */
+size_t hh_meta_prefix_workspace_size(const hh_dims *dims, int32_t kv_producer);
+
+/* The meta-token part of one layer (paper §2.3: fixed meta tokens, computed
+ * offline).  meta_tokens [m, d_model] dtype.  Writes meta_k/meta_v
+ * [G, m, hd] dtype (producer layers only; ignored and may be NULL for a
+ * consumer), h0 [D, N] fp32 (state after the meta rows, from a zero state)
+ * and conv_tail [k-1, D] dtype (xs of the last k-1 meta rows; zero rows in
+ * front when m < k-1). */
+hh_status hh_meta_prefix(const hh_dims *dims, const hh_weights *w,
+                         const void *meta_tokens, void *meta_k, void *meta_v,
+                         float *h0, void *conv_tail, void *ws, size_t ws_bytes,
+                         void *stream);
+
+/* Bytes of device workspace hh_prefill needs (0 on invalid arguments). */
+size_t hh_prefill_workspace_size(const hh_dims *dims, int32_t batch,
+                                 int32_t seqlen, int32_t kv_producer);
+
+/* Prefill of `seqlen` real tokens per sequence after the meta tokens
+ * (paper §2.1 Eqs. 1-3 over X~ of §2.3 Eq. 4).
+ *   x      [B, seqlen, d_model] dtype
+ *   meta   the layer's hh_meta (its h0 and conv_tail start the SSM branch)
+ *   window sliding-window length W >= 1 (ignored when is_global)
+ *   out    [B, seqlen, d_model] dtype
+ *   kv     see hh_kv (producer writes, consumer reads full_k/full_v)
+ *   state  if not NULL: receives h after the last token and the conv history
+ *          (either member may be NULL to skip it). */
+hh_status hh_prefill(const hh_dims *dims, const hh_weights *w, const void *x,
+                     int32_t batch, int32_t seqlen, const hh_meta *meta,
+                     int32_t window, int32_t is_global, void *out, hh_kv *kv,
+                     hh_ssm_state *state, void *ws, size_t ws_bytes,
+                     void *stream);
+
+/* Bytes of device workspace hh_decode_step needs for `batch` sequences whose
+ * cache has `cap` slots (0 on invalid arguments). */
+size_t hh_decode_workspace_size(const hh_dims *dims, int32_t batch, int32_t cap,
+                                int32_t kv_producer);
+
+/* One new token per sequence (generation with the KV cache and SSM state;
+ * authors' replies: KV-sharing groups of two consecutive sliding-window layers,
+ * meta K/V precomputed and pinned).
+ *   x_t    [B, d_model] dtype;  out [B, d_model] dtype
+ *   meta   pinned meta K/V of the cache (shared by all sequences)
+ *   kv     cache_k/cache_v/len/cap/is_ring used (full_* ignored)
+ *   state  h and conv read and updated in place (both required). */
+hh_status hh_decode_step(const hh_dims *dims, const hh_weights *w,
+                         const void *x_t, int32_t batch, const hh_meta *meta,
+                         int32_t window, int32_t is_global, hh_kv *kv,
+                         hh_ssm_state *state, void *out, void *ws,
+                         size_t ws_bytes, void *stream);
+
+/* Workspace regions of hh_prefill, for inspecting intermediate results after
+ * a call (test and debugging aid).  Fills offs[HH_WS_COUNT] with byte offsets
+ * (SIZE_MAX for a region that is not used) and returns the total size. */
+enum {
+  HH_WS_Q = 0,   /* [B*n, H*hd] dtype */
+  HH_WS_K,       /* [B, G, n, hd] dtype (used when full_k is NULL) */
+  HH_WS_V,
+  HH_WS_XS,      /* [B*n, D] dtype */
+  HH_WS_Z,       /* [B*n, D] dtype */
+  HH_WS_DELTA,   /* [B*n, D] fp32, softplus applied */
+  HH_WS_BC,      /* [B*n, 2N] fp32: B then C */
+  HH_WS_O,       /* [B*n, H*hd] dtype attention output */
+  HH_WS_Y,       /* [B*n, D] dtype gated SSM output */
+  HH_WS_F,       /* [B*n, H*hd + D] dtype fused features */
+  HH_WS_SCAN,    /* scan chunk carries */
+  HH_WS_COUNT
+};
+size_t hh_prefill_workspace_layout(const hh_dims *dims, int32_t batch,
+                                   int32_t seqlen, int32_t kv_producer,
+                                   size_t *offs);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HH_H */

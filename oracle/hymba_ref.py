@@ -149,9 +149,17 @@ def selective_scan(u, delta, A, Bm, Cm, h):
     T, D = u.shape
     y = np.empty((T, D))
     h = np.array(h, dtype=F64, copy=True)
+    decay = np.empty_like(h)
+    inject = np.empty_like(h)
     for t in range(T):
-        h = np.exp(delta[t][:, None] * A) * h + (delta[t] * u[t])[:, None] * Bm[t][None, :]
-        y[t] = h @ Cm[t]
+        # the same arithmetic as h = exp(delta_t A) h + (delta_t u_t) B_t,
+        # written into reused buffers
+        np.multiply(delta[t][:, None], A, out=decay)
+        np.exp(decay, out=decay)
+        np.multiply(decay, h, out=h)
+        np.multiply((delta[t] * u[t])[:, None], Bm[t][None, :], out=inject)
+        np.add(h, inject, out=h)
+        np.dot(h, Cm[t], out=y[t])
     return y, h
 
 

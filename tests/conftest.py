@@ -28,3 +28,12 @@ def hh():
         pytest.skip("no GPU visible")
     from hybrid_attention_ssm_amd import binding
     return binding
+
+
+def pytest_collection_modifyitems(config, items):
+    if gpu_available():
+        return
+    skip = pytest.mark.skip(reason="no GPU visible on this host")
+    for item in items:
+        if "gpu" in item.keywords:
+            item.add_marker(skip)

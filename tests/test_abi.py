@@ -1,0 +1,119 @@
+"""The C ABI on a host without a GPU: the library loads, exports every entry
+point include/hh.h declares, sizes workspaces, and rejects bad arguments
+before launching anything (fake, never-dereferenced device pointers)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from hybrid_attention_ssm_amd import binding as hb
+from hybrid_attention_ssm_amd.configs import CFG0_TINY, CFG1_SWA_8K, HYMBA_1P5B, TINY
+from dataclasses import replace
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hh.h")
+FAKE = 0x10000   # 16-byte aligned, never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^[a-z_ ]+\**\s*\**(hh_[a-z_]+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["hh_prefill", "hh_decode_step", "hh_meta_prefix", "hh_prefill_workspace_size",
+              "hh_decode_workspace_size", "hh_meta_prefix_workspace_size", "hh_last_error",
+              "hh_version", "hh_prefill_workspace_layout"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = hb.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert "gfx950" in hb.hh_version()
+
+
+def _weights(kv_producer=1):
+    return hb.HHWeights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, kv_producer)
+
+
+def _call_prefill(dims, B=1, n=64, window=16, ws_bytes=1 << 40, w=None, x=FAKE, meta=None, kv=None):
+    d = hb.hh_dims(dims)
+    w = w or _weights()
+    meta = meta or hb.HHMeta(FAKE, FAKE, FAKE, FAKE)
+    st = hb.HHSsmState(None, None)
+    return hb.lib().hh_prefill(ctypes.byref(d), ctypes.byref(w), x, B, n, ctypes.byref(meta),
+                               window, 0, FAKE, ctypes.byref(kv) if kv else None,
+                               ctypes.byref(st), FAKE, ws_bytes, None)
+
+
+def test_workspace_sizes():
+    s1 = hb.hh_prefill_workspace_size(TINY, 1, 64)
+    s2 = hb.hh_prefill_workspace_size(TINY, 2, 64)
+    assert 0 < s1 < s2
+    lay = hb.hh_prefill_workspace_layout(TINY, 1, 64)
+    assert lay["total"] == s1
+    offs = sorted(v for k, v in lay.items() if k != "total" and v is not None)
+    assert offs == sorted(set(offs)) and all(o % 256 == 0 for o in offs)
+    # consumer layers keep no K/V of their own
+    lc = hb.hh_prefill_workspace_layout(TINY, 1, 64, kv_producer=False)
+    assert lc["K"] is None and lc["V"] is None
+    assert hb.hh_decode_workspace_size(HYMBA_1P5B, 128, 8192) > hb.hh_decode_workspace_size(HYMBA_1P5B, 128, 1024)
+    assert hb.hh_prefill_workspace_size(replace(TINY, head_dim=48), 1, 64) == 0
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(head_dim=128), 2), (dict(d_state=8), 2), (dict(d_conv=5), 2), (dict(n_kv_heads=3), 1),
+    (dict(d_model=60), 2), (dict(n_heads=0), 1), (dict(eps=-1.0), 1)])
+def test_bad_dims_rejected(change, status):
+    assert _call_prefill(replace(TINY, **change)) == status
+    assert hb.hh_last_error() != ""
+
+
+def test_bf16_needs_head_dim_64():
+    assert _call_prefill(replace(TINY, dtype="bf16")) == 2
+    assert "head_dim" in hb.hh_last_error()
+
+
+def test_bad_arguments_rejected():
+    assert _call_prefill(TINY, n=0) == 1
+    assert _call_prefill(TINY, window=0) == 1
+    assert _call_prefill(TINY, x=FAKE + 2) == 1                       # misaligned
+    assert _call_prefill(TINY, w=hb.HHWeights(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1)) == 1
+    # consumer without its producer's K/V
+    assert _call_prefill(TINY, w=_weights(0)) == 1
+    # ring cache smaller than the window
+    kv = hb.HHKV(None, None, FAKE, FAKE, FAKE, 8, 1)
+    assert _call_prefill(TINY, window=16, kv=kv) == 1
+    assert "ring" in hb.hh_last_error()
+
+
+def test_small_workspace_rejected():
+    need = hb.hh_prefill_workspace_size(TINY, 1, 64)
+    assert _call_prefill(TINY, ws_bytes=need - 1) == 3
+
+
+def test_decode_validation():
+    d = hb.hh_dims(TINY)
+    w = _weights()
+    meta = hb.HHMeta(FAKE, FAKE, FAKE, FAKE)
+    st = hb.HHSsmState(FAKE, FAKE)
+    kv = hb.HHKV(None, None, FAKE, FAKE, None, 16, 1)          # len missing
+    r = hb.lib().hh_decode_step(ctypes.byref(d), ctypes.byref(w), FAKE, 4, ctypes.byref(meta),
+                                16, 0, ctypes.byref(kv), ctypes.byref(st), FAKE, FAKE, 1 << 40, None)
+    assert r == 1
+    kv = hb.HHKV(None, None, FAKE, FAKE, FAKE, 16, 1)
+    r = hb.lib().hh_decode_step(ctypes.byref(d), ctypes.byref(w), FAKE, 4, ctypes.byref(meta),
+                                16, 1, ctypes.byref(kv), ctypes.byref(st), FAKE, FAKE, 1 << 40, None)
+    assert r == 1 and "linear" in hb.hh_last_error()
+
+
+def test_meta_prefix_validation():
+    d = hb.hh_dims(replace(TINY, n_meta=0))
+    w = _weights()
+    r = hb.lib().hh_meta_prefix(ctypes.byref(d), ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                FAKE, 1 << 40, None)
+    assert r == 1

@@ -1,0 +1,160 @@
+"""GPU parity of the decode path and bit-exact cache indexing.
+
+* prefill(n0) + k x hh_decode_step == oracle prefill(n0 + k) (outputs, SSM
+  state, conv history, cache slots), across ring wrap-around and for global
+  (linear) caches, for producer and KV-sharing consumer layers.
+* Selection-matrix K/V projections with small-integer inputs make every
+  cached K/V value an exact copy of an input entry, so the slot <-> position
+  mapping is compared bit for bit, including slots that must stay untouched.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from hybrid_attention_ssm_amd import binding as hb
+from hybrid_attention_ssm_amd.configs import TINY, LayerDims, PrefillWorkload
+from hybrid_attention_ssm_amd.synth import prefill_inputs
+from oracle import hymba_ref as ref
+from tests.harness import TOL, np_of, rel_err, run_prefill
+
+pytestmark = pytest.mark.gpu
+
+SMALL_BF16 = LayerDims(d_model=256, n_heads=8, n_kv_heads=2, head_dim=64, d_inner=512,
+                       d_state=16, d_conv=4, n_meta=128, dtype="bf16")
+
+
+def _decode_steps(dims, got, x_new, window, is_global, cap, consumer=None):
+    """Run hh_decode_step for each new token of x_new [B, k, d] on GPU state `got`."""
+    sd = hb.storage_dtype(dims)
+    B, k, d = x_new.shape
+    outs = []
+    layer = got["layer"]
+    kv = hb.make_kv(None, None, got["cache_k"], got["cache_v"], got["len"], cap, not is_global)
+    meta = hb.make_meta(got["meta"]["k"], got["meta"]["v"], None, None)
+    for s in range(k):
+        xt = hb.to_device(x_new[:, s], sd)
+        out = torch.empty(B, d, dtype=sd, device="cuda")
+        hb.hh_decode_step(layer, xt, meta, window, is_global, kv, got["h"], got["conv"], out)
+        if consumer is not None:
+            cl, ch, cc, cx = consumer
+            cout = torch.empty(B, d, dtype=sd, device="cuda")
+            hb.hh_decode_step(cl, hb.to_device(cx[:, s], sd), meta, window, is_global, kv, ch, cc, cout)
+            torch.cuda.synchronize()
+            outs.append((np_of(out), np_of(cout)))
+        else:
+            torch.cuda.synchronize()
+            outs.append(np_of(out))
+    return outs
+
+
+@pytest.mark.parametrize("dims,n0,steps,window,is_global,cap", [
+    (TINY, 10, 12, 8, False, 8),          # ring of 8 wraps during decode
+    (TINY, 20, 5, 16, True, 32),          # linear cache
+    (SMALL_BF16, 60, 9, 64, False, 64),   # bf16 ring wrap
+    (SMALL_BF16, 130, 4, 64, True, 160),
+])
+def test_prefill_then_decode_matches_longer_prefill(dims, n0, steps, window, is_global, cap):
+    B = 2
+    inp = prefill_inputs(PrefillWorkload("pd", n0 + steps, dims, B, n0 + steps, window, is_global))
+    x = inp["x"]
+    print(f"case {dims.dtype} n0={n0} steps={steps} W={window} global={is_global} cap={cap}", flush=True)
+    z = np.zeros((B, dims.n_kv_heads, cap, dims.head_dim))
+    want = ref.prefill(dims.as_dict(), inp["weights"], inp["R"], x, window, is_global,
+                       cache=dict(k=z, v=z, is_ring=not is_global))
+    got = run_prefill(dims, inp["weights"], inp["R"], x[:, :n0], window, is_global,
+                      cache_cap=cap, cache_ring=not is_global)
+    outs = _decode_steps(dims, got, x[:, n0:], window, is_global, cap)
+    tol = TOL[dims.dtype]
+    for s, o in enumerate(outs):
+        e = rel_err(o, want["out"][:, n0 + s])
+        assert e <= tol, f"step {s}: {e}"
+    assert rel_err(np_of(got["h"]), want["h"]) <= tol
+    assert rel_err(np_of(got["conv"]), want["conv_tail"]) <= tol
+    assert rel_err(np_of(got["cache_k"]), want["cache_k"]) <= tol
+    assert rel_err(np_of(got["cache_v"]), want["cache_v"]) <= tol
+    assert (got["len"].cpu().numpy() == n0 + steps).all()
+
+
+@pytest.mark.parametrize("dims", [TINY, SMALL_BF16])
+def test_consumer_decode_reads_producer_cache(dims):
+    """Producer then consumer per token (shared cache), vs the oracle."""
+    B, n0, steps, window = 2, 30, 6, 16
+    cap = window
+    wp = PrefillWorkload("p", 41, dims, B, n0 + steps, window, False)
+    ip = prefill_inputs(wp)
+    ic = prefill_inputs(replace(wp, seed=42), kv_producer=False)
+    mp = ref.meta_prefix(dims.as_dict(), ip["weights"], ip["R"])
+    mc = ref.meta_prefix(dims.as_dict(), ic["weights"], ip["R"])
+    z = np.zeros((B, dims.n_kv_heads, cap, dims.head_dim))
+    pre_p = ref.prefill(dims.as_dict(), ip["weights"], ip["R"], ip["x"][:, :n0], window, False,
+                        cache=dict(k=z, v=z, is_ring=True))
+    pre_c = ref.prefill(dims.as_dict(), ic["weights"], ip["R"], ic["x"][:, :n0], window, False,
+                        shared_kv=(pre_p["K_all"], pre_p["V_all"]))
+    gp = run_prefill(dims, ip["weights"], ip["R"], ip["x"][:, :n0], window, False, cache_cap=cap)
+    gc = run_prefill(dims, ic["weights"], ip["R"], ic["x"][:, :n0], window, False, producer=gp)
+    outs = _decode_steps(dims, gp, ip["x"][:, n0:], window, False, cap,
+                         consumer=(gc["layer"], gc["h"], gc["conv"], ic["x"][:, n0:]))
+    cache = dict(k=pre_p["cache_k"], v=pre_p["cache_v"], len=np.full(B, n0), is_ring=True)
+    hp, cp, hc, cc = pre_p["h"], pre_p["conv_tail"], pre_c["h"], pre_c["conv_tail"]
+    tol = TOL[dims.dtype]
+    for s in range(steps):
+        rp = ref.decode_step(dims.as_dict(), ip["weights"], ip["x"][:, n0 + s], mp["k"], mp["v"],
+                             window, False, cache, hp, cp)
+        cache = dict(k=rp["cache_k"], v=rp["cache_v"], len=rp["len"], is_ring=True)
+        rc = ref.decode_step(dims.as_dict(), ic["weights"], ic["x"][:, n0 + s], mp["k"], mp["v"],
+                             window, False, cache, hc, cc)
+        hp, cp, hc, cc = rp["h"], rp["conv"], rc["h"], rc["conv"]
+        assert rel_err(outs[s][0], rp["out"]) <= tol
+        assert rel_err(outs[s][1], rc["out"]) <= tol
+    assert rel_err(np_of(gc["h"]), hc) <= tol
+    assert (gp["len"].cpu().numpy() == n0 + steps).all()
+
+
+def _selection_layer(dims, rng, n, B):
+    """Integer inputs and one-hot K/V projection rows: K, V copy input entries."""
+    w = prefill_inputs(PrefillWorkload("s", 5, dims, B, n, 8, False))["weights"]
+    d, Wa, KV = dims.d_model, dims.attn_width, dims.n_kv_heads * dims.head_dim
+    w_in = w["w_in"].copy()
+    w_in[Wa:Wa + 2 * KV] = 0.0
+    for r in range(KV):
+        w_in[Wa + r, r % d] = 1.0                 # K[g, e] = x[(g*hd + e) % d]
+        w_in[Wa + KV + r, (r + 97) % d] = 1.0     # V[g, e] = x[(g*hd + e + 97) % d]
+    w["w_in"] = w_in
+    x = rng.integers(-8, 9, size=(B, n, d)).astype(np.float32)
+    R = rng.integers(-8, 9, size=(dims.n_meta, d)).astype(np.float32)
+    return w, x, R
+
+
+@pytest.mark.parametrize("dims,is_global,n0,steps,cap,window", [
+    (SMALL_BF16, False, 150, 5, 64, 64),
+    (SMALL_BF16, True, 70, 6, 100, 0),
+    (TINY, False, 37, 11, 10, 10),
+])
+def test_cache_indexing_bit_exact(dims, is_global, n0, steps, cap, window):
+    rng = np.random.default_rng(123)
+    B = 3
+    w, x, R = _selection_layer(dims, rng, n0 + steps, B)
+    sentinel = 1000.0
+    fill = np.full((B, dims.n_kv_heads, cap, dims.head_dim), sentinel)
+    want = ref.prefill(dims.as_dict(), w, R, x[:, :n0], window, is_global,
+                       cache=dict(k=fill, v=fill, is_ring=not is_global))
+    got = run_prefill(dims, w, R, x[:, :n0], window, is_global, cache_cap=cap,
+                      cache_ring=not is_global, cache_fill=sentinel)
+    assert np.array_equal(np_of(got["cache_k"]), want["cache_k"])
+    assert np.array_equal(np_of(got["cache_v"]), want["cache_v"])
+    assert np.array_equal(np_of(got["full_k"]), want["k_full"])
+    mp = ref.meta_prefix(dims.as_dict(), w, R)
+    assert np.array_equal(np_of(got["meta"]["k"]), mp["k"])
+    _decode_steps(dims, got, x[:, n0:], window, is_global, cap)
+    cache = dict(k=want["cache_k"], v=want["cache_v"], len=np.full(B, n0), is_ring=not is_global)
+    h, conv = want["h"], want["conv_tail"]
+    for s in range(steps):
+        r = ref.decode_step(dims.as_dict(), w, x[:, n0 + s], mp["k"], mp["v"], window, is_global,
+                            cache, h, conv)
+        cache = dict(k=r["cache_k"], v=r["cache_v"], len=r["len"], is_ring=not is_global)
+        h, conv = r["h"], r["conv"]
+    assert np.array_equal(np_of(got["cache_k"]), cache["k"])
+    assert np.array_equal(np_of(got["cache_v"]), cache["v"])
+    assert np.array_equal(got["len"].cpu().numpy(), cache["len"])

@@ -1,0 +1,126 @@
+"""GPU parity: libhymba_hh (through its C ABI) against the CPU oracle.
+
+Element-by-element comparisons on seeded synthetic inputs at sizes the
+oracle finishes in seconds, spanning several tiles with ragged tails.
+Bar: max|gpu - oracle| <= tol * rms(oracle), tol = 1e-4 (fp32 path) and 3e-2
+(bf16 path, fp32 accumulation); cache indexing bit-exact.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from hybrid_attention_ssm_amd import binding as hb
+from hybrid_attention_ssm_amd.configs import (CFG0_TINY, HYMBA_1P5B, TINY, LayerDims,
+                                              PrefillWorkload)
+from hybrid_attention_ssm_amd.synth import prefill_inputs
+from oracle import hymba_ref as ref
+from tests.harness import TOL, np_of, rel_err, run_prefill
+
+pytestmark = pytest.mark.gpu
+
+SMALL_BF16 = LayerDims(d_model=256, n_heads=8, n_kv_heads=2, head_dim=64, d_inner=512,
+                       d_state=16, d_conv=4, n_meta=128, dtype="bf16")
+SMALL_BF16_G5 = LayerDims(d_model=320, n_heads=10, n_kv_heads=2, head_dim=64, d_inner=640,
+                          d_state=16, d_conv=4, n_meta=100, dtype="bf16")
+
+
+def _check_prefill(dims, B, n, window, is_global, seed, kv_producer=True, cache_cap=None):
+    w = PrefillWorkload("t", seed, dims, B, n, window, is_global)
+    inp = prefill_inputs(w)
+    tol = TOL[dims.dtype]
+    print(f"case dims={dims.dtype} d={dims.d_model} H={dims.n_heads} G={dims.n_kv_heads} "
+          f"B={B} n={n} W={window} global={is_global} seed={seed}", flush=True)
+    cache = None
+    if cache_cap:
+        z = np.zeros((B, dims.n_kv_heads, cache_cap, dims.head_dim))
+        cache = dict(k=z, v=z, is_ring=not is_global)
+    want = ref.prefill(dims.as_dict(), inp["weights"], inp["R"], inp["x"], window, is_global,
+                       cache=cache)
+    got = run_prefill(dims, inp["weights"], inp["R"], inp["x"], window, is_global,
+                      cache_cap=cache_cap, cache_ring=not is_global)
+    e_out = rel_err(np_of(got["out"]), want["out"])
+    e_h = rel_err(np_of(got["h"]), want["h"])
+    e_tail = rel_err(np_of(got["conv"]), want["conv_tail"])
+    e_k = rel_err(np_of(got["full_k"]), want["k_full"])
+    e_v = rel_err(np_of(got["full_v"]), want["v_full"])
+    print(f"  err out={e_out:.2e} h={e_h:.2e} tail={e_tail:.2e} k={e_k:.2e} v={e_v:.2e}", flush=True)
+    assert e_out <= tol and e_h <= tol and e_tail <= tol and e_k <= tol and e_v <= tol
+    if cache_cap:
+        assert rel_err(np_of(got["cache_k"]), want["cache_k"]) <= tol
+        assert rel_err(np_of(got["cache_v"]), want["cache_v"]) <= tol
+        assert (got["len"].cpu().numpy() == n).all()
+    return inp, want, got
+
+
+def test_cfg0_tiny_f32_swa():
+    w = CFG0_TINY
+    _check_prefill(w.dims, w.batch, w.seqlen, w.window, w.is_global, w.seed, cache_cap=w.window)
+
+
+@pytest.mark.parametrize("B,n,window,is_global", [
+    (1, 64, 16, True), (2, 37, 5, False), (3, 100, 200, False), (1, 1, 16, False), (2, 70, 1, False)])
+def test_tiny_f32_variants(B, n, window, is_global):
+    _check_prefill(TINY, B, n, window, is_global, seed=100 + n)
+
+
+def test_tiny_f32_head_dim_64_and_gqa():
+    dims = replace(TINY, d_model=128, n_heads=6, n_kv_heads=2, head_dim=64, d_inner=96,
+                   n_meta=7, d_conv=3)
+    _check_prefill(dims, 2, 45, 9, False, seed=7, cache_cap=12)
+
+
+@pytest.mark.parametrize("dims,B,n,window,is_global", [
+    (SMALL_BF16, 1, 300, 100, False), (SMALL_BF16, 2, 130, 64, False),
+    (SMALL_BF16, 1, 200, 100, True), (SMALL_BF16_G5, 1, 333, 77, False),
+    (SMALL_BF16_G5, 1, 96, 1, False)])
+def test_bf16_small(dims, B, n, window, is_global):
+    _check_prefill(dims, B, n, window, is_global, seed=n, cache_cap=128 if not is_global else 512)
+
+
+def test_bf16_hymba_shapes_short_sequence():
+    """The 1.5B layer shapes (d 1600, 25/5 heads, D 3200, 128 meta) at n = 200."""
+    _check_prefill(HYMBA_1P5B, 1, 200, 64, False, seed=1)
+
+
+@pytest.mark.parametrize("dims", [TINY, SMALL_BF16])
+def test_consumer_layer_reads_producer_kv(dims):
+    """A KV-sharing consumer attends over its producer's K/V (and meta K/V)."""
+    B, n, window = 2, 90, 20
+    wp = PrefillWorkload("p", 31, dims, B, n, window, False)
+    inp_p = prefill_inputs(wp)
+    inp_c = prefill_inputs(replace(wp, seed=32), kv_producer=False)
+    prod_ref = ref.prefill(dims.as_dict(), inp_p["weights"], inp_p["R"], inp_p["x"], window, False)
+    x_c = inp_c["x"]
+    cons_ref = ref.prefill(dims.as_dict(), inp_c["weights"], inp_p["R"], x_c, window, False,
+                           shared_kv=(prod_ref["K_all"], prod_ref["V_all"]))
+    prod = run_prefill(dims, inp_p["weights"], inp_p["R"], inp_p["x"], window, False)
+    cons = run_prefill(dims, inp_c["weights"], inp_p["R"], x_c, window, False, producer=prod)
+    tol = TOL[dims.dtype]
+    e = rel_err(np_of(cons["out"]), cons_ref["out"])
+    print(f"consumer err {e:.2e}", flush=True)
+    assert e <= tol
+    assert rel_err(np_of(cons["h"]), cons_ref["h"]) <= tol
+
+
+def test_meta_prefix_matches_oracle():
+    for dims, seed in ((TINY, 3), (SMALL_BF16, 4)):
+        inp = prefill_inputs(PrefillWorkload("m", seed, dims, 1, 8, 4, False))
+        from tests.harness import run_meta_prefix
+        _, meta = run_meta_prefix(dims, inp["weights"], inp["R"])
+        want = ref.meta_prefix(dims.as_dict(), inp["weights"], inp["R"])
+        tol = TOL[dims.dtype]
+        assert rel_err(np_of(meta["k"]), want["k"]) <= tol
+        assert rel_err(np_of(meta["v"]), want["v"]) <= tol
+        assert rel_err(np_of(meta["h0"]), want["h0"]) <= tol
+        assert rel_err(np_of(meta["conv_tail"]), want["conv_tail"]) <= tol
+
+
+def test_deterministic_rerun():
+    """Same inputs twice: bit-identical outputs (no races between workgroups)."""
+    dims = SMALL_BF16
+    inp = prefill_inputs(PrefillWorkload("d", 9, dims, 1, 257, 64, False))
+    a = run_prefill(dims, inp["weights"], inp["R"], inp["x"], 64, False)
+    b = run_prefill(dims, inp["weights"], inp["R"], inp["x"], 64, False)
+    assert torch.equal(a["out"], b["out"]) and torch.equal(a["h"], b["h"])
