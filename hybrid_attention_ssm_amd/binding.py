@@ -216,7 +216,7 @@ def hh_meta_prefix(layer: DeviceLayer, meta_tokens: torch.Tensor, out: Optional[
                          dims.d_state, dims.d_conv)
     if out is None:
         out = {"h0": torch.empty(D, N, dtype=torch.float32, device=dev),
-               "conv_tail": torch.empty(k - 1, D, dtype=sd, device=dev)}
+               "conv_tail": torch.empty(k - 1, D, dtype=torch.float32, device=dev)}
         if layer.kv_producer:
             out["k"] = torch.empty(G, m, hd, dtype=sd, device=dev)
             out["v"] = torch.empty(G, m, hd, dtype=sd, device=dev)

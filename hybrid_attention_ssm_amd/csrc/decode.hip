@@ -206,14 +206,13 @@ __global__ void __launch_bounds__(256) decode_ssm_step(DecodeSsmArgs a) {
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (long)a.B * a.D) return;
   const int b = (int)(idx / a.D), c = (int)(idx % a.D);
-  const T *xs = reinterpret_cast<const T *>(a.xs);
   const T *z = reinterpret_cast<const T *>(a.z);
-  T *conv = reinterpret_cast<T *>(a.conv) + (size_t)b * (a.k - 1) * a.D;
-  const float x = to_f32(xs[idx]);
+  float *conv = a.conv + (size_t)b * (a.k - 1) * a.D;
+  const float x = a.xs[idx];
   // window: conv rows (oldest first) then the current xs; tap j multiplies window[j]
   float cv = a.conv_b[c];
   float win[4];
-  for (int j = 0; j < a.k - 1; ++j) win[j] = to_f32(conv[(size_t)j * a.D + c]);
+  for (int j = 0; j < a.k - 1; ++j) win[j] = conv[(size_t)j * a.D + c];
   win[a.k - 1] = x;
   for (int j = 0; j < a.k; ++j) cv = fmaf(a.conv_w[(size_t)c * a.k + j], win[j], cv);
   const float u = silu_f(cv);
@@ -237,7 +236,7 @@ __global__ void __launch_bounds__(256) decode_ssm_step(DecodeSsmArgs a) {
 #pragma unroll
   for (int s = 0; s < NS; s += 4)
     *reinterpret_cast<float4 *>(hp + s) = make_float4(h[s], h[s + 1], h[s + 2], h[s + 3]);
-  for (int j = 0; j < a.k - 1; ++j) conv[(size_t)j * a.D + c] = from_f32<T>(win[j + 1]);
+  for (int j = 0; j < a.k - 1; ++j) conv[(size_t)j * a.D + c] = win[j + 1];
   reinterpret_cast<T *>(a.y)[idx] = from_f32<T>(y * silu_f(to_f32(z[idx])));
 }
 

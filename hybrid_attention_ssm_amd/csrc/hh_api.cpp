@@ -101,7 +101,7 @@ PrefillLayout prefill_layout(const Shape &s, int B, int n) {
     take(HH_WS_K, (size_t)B * s.G * n * s.hd * s.es);
     take(HH_WS_V, (size_t)B * s.G * n * s.hd * s.es);
   }
-  take(HH_WS_XS, T * s.D * s.es);
+  take(HH_WS_XS, T * s.D * 4);
   take(HH_WS_Z, T * s.D * s.es);
   take(HH_WS_DELTA, T * s.D * 4);
   take(HH_WS_BC, T * 2 * s.N * 4);
@@ -123,7 +123,7 @@ DecodeLayout decode_layout(const Shape &s, int B, int max_real) {
   size_t o = 0;
   auto take = [&](size_t &dst, size_t bytes) { dst = o; o = up256(o + bytes); };
   take(L.q, (size_t)B * s.Wa * s.es);
-  take(L.xs, (size_t)B * s.D * s.es);
+  take(L.xs, (size_t)B * s.D * 4);
   take(L.z, (size_t)B * s.D * s.es);
   take(L.dt, (size_t)B * s.D * 4);
   take(L.bc, (size_t)B * 2 * s.N * 4);
@@ -162,7 +162,7 @@ hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, i
   if (prod && kv && kv->cache_k) {
     e.cache_k = kv->cache_k; e.cache_v = kv->cache_v; e.cap = kv->cap; e.is_ring = kv->is_ring;
   }
-  e.xs = at(ws, L.off[HH_WS_XS]); e.z = at(ws, L.off[HH_WS_Z]);
+  e.xs = reinterpret_cast<float *>(at(ws, L.off[HH_WS_XS])); e.z = at(ws, L.off[HH_WS_Z]);
   e.dt = reinterpret_cast<float *>(at(ws, L.off[HH_WS_DELTA]));
   e.bc = reinterpret_cast<float *>(at(ws, L.off[HH_WS_BC]));
   e.dt_bias = w->dt_bias;
@@ -209,13 +209,13 @@ hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, i
 
 template <class T>
 hh_status meta_prefix_t(const Shape &s, const hh_weights *w, const void *R, void *mk, void *mv,
-                        float *h0, void *tail, void *ws, const PrefillLayout &L, hipStream_t st) {
+                        float *h0, float *tail, void *ws, const PrefillLayout &L, hipStream_t st) {
   hh::InProjOut e{};
   e.mode = hh::EPI_META;
   e.Wa = s.Wa; e.KV = s.KV; e.D = s.D; e.N = s.N; e.hd = s.hd; e.n_rows_per_seq = s.m;
   e.q = at(ws, L.off[HH_WS_Q]);
   e.k_full = mk; e.v_full = mv;
-  e.xs = at(ws, L.off[HH_WS_XS]); e.z = at(ws, L.off[HH_WS_Z]);
+  e.xs = reinterpret_cast<float *>(at(ws, L.off[HH_WS_XS])); e.z = at(ws, L.off[HH_WS_Z]);
   e.dt = reinterpret_cast<float *>(at(ws, L.off[HH_WS_DELTA]));
   e.bc = reinterpret_cast<float *>(at(ws, L.off[HH_WS_BC]));
   e.dt_bias = w->dt_bias;
@@ -243,7 +243,7 @@ hh_status decode_t(const Shape &s, const hh_weights *w, const void *x, int B, co
   e.q = at(ws, L.q);
   e.cache_k = kv->cache_k; e.cache_v = kv->cache_v; e.cap = kv->cap; e.is_ring = kv->is_ring;
   e.len = kv->len;
-  e.xs = at(ws, L.xs); e.z = at(ws, L.z);
+  e.xs = reinterpret_cast<float *>(at(ws, L.xs)); e.z = at(ws, L.z);
   e.dt = reinterpret_cast<float *>(at(ws, L.dt));
   e.bc = reinterpret_cast<float *>(at(ws, L.bc));
   e.dt_bias = w->dt_bias;
@@ -326,7 +326,7 @@ size_t hh_decode_workspace_size(const hh_dims *dims, int32_t batch, int32_t cap,
 }
 
 hh_status hh_meta_prefix(const hh_dims *dims, const hh_weights *w, const void *meta_tokens,
-                         void *meta_k, void *meta_v, float *h0, void *conv_tail, void *ws,
+                         void *meta_k, void *meta_v, float *h0, float *conv_tail, void *ws,
                          size_t ws_bytes, void *stream) {
   Shape s;
   hh_status r = check_dims(dims, w ? w->kv_producer : 1, s);

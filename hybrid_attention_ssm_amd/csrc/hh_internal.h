@@ -53,7 +53,8 @@ struct InProjOut {
   void *cache_k, *cache_v;    // prefill/decode cache [B, G, cap, hd] (may be null)
   int cap, is_ring;
   const int32_t *len;         // decode: position of the new token per row
-  void *xs, *z;               // [rows, D]
+  float *xs;                  // [rows, D] fp32 (SSM input features)
+  void *z;                    // [rows, D]
   float *dt;                  // [rows, D] softplus(dt + bias)
   float *bc;                  // [rows, 2N] B then C
   const float *dt_bias;       // [D]
@@ -98,7 +99,7 @@ __device__ __forceinline__ void inproj_store(const InProjOut &e, int row, int co
     return;
   }
   col -= 2 * KV;
-  if (col < D) { reinterpret_cast<T *>(e.xs)[(size_t)row * D + col] = from_f32<T>(v); return; }
+  if (col < D) { e.xs[(size_t)row * D + col] = v; return; }
   col -= D;
   if (col < D) { reinterpret_cast<T *>(e.z)[(size_t)row * D + col] = from_f32<T>(v); return; }
   col -= D;
@@ -125,17 +126,18 @@ struct AttnArgs {
 template <class T> hipError_t launch_attention(const AttnArgs &a, hipStream_t s);
 
 struct ScanArgs {
-  const void *xs, *z;      // [B*n, D] (z may be null: no gate, no Y)
+  const float *xs;         // [B*n, D] fp32
+  const void *z;           // [B*n, D] (null: no gate, no Y)
   const float *dt;         // [B*n, D]
   const float *bc;         // [B*n, 2N]
   const float *A;          // [D, N]
   const float *conv_w;     // [D, k]
   const float *conv_b;     // [D]
   const float *h0;         // [D, N] initial state (null: zero)
-  const void *tail0;       // [k-1, D] conv history (null: zero)
+  const float *tail0;      // [k-1, D] fp32 conv history (null: zero)
   void *y;                 // [B*n, D] (null: not written)
   float *h_out;            // [B, D, N] (null: not written)
-  void *tail_out;          // [B, k-1, D] (null: not written)
+  float *tail_out;         // [B, k-1, D] fp32 (null: not written)
   float *carry;            // workspace for chunk carries
   int B, n, D, N, k;
   int chunk;               // time steps per chunk
@@ -168,11 +170,12 @@ size_t decode_attn_part_bytes(int B, int H, int hd, int m, int max_real,
                               int *split_out, int *nsplit_out);
 
 struct DecodeSsmArgs {
-  const void *xs, *z;      // [B, D]
+  const float *xs;         // [B, D] fp32
+  const void *z;           // [B, D]
   const float *dt, *bc;    // [B, D], [B, 2N]
   const float *A, *conv_w, *conv_b;
   float *h;                // [B, D, N] in/out
-  void *conv;              // [B, k-1, D] in/out
+  float *conv;             // [B, k-1, D] fp32 in/out
   void *y;                 // [B, D]
   int B, D, N, k;
 };

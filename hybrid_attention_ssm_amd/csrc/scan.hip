@@ -49,14 +49,14 @@ __device__ __forceinline__ void load_params(const ScanArgs &a, int c, ChanParams
 // history: hist[0] = xs_{t0-1}, hist[1] = xs_{t0-2}, hist[2] = xs_{t0-3}
 template <class T>
 __device__ __forceinline__ void load_history(const ScanArgs &a, int b, int c, int t0, float hist[KC - 1]) {
-  const T *xs = reinterpret_cast<const T *>(a.xs);
-  const T *tail = reinterpret_cast<const T *>(a.tail0);
+  const float *xs = a.xs;
+  const float *tail = a.tail0;
 #pragma unroll
   for (int j = 0; j < KC - 1; ++j) {
     const int pos = t0 - 1 - j;
     float v = 0.0f;
-    if (pos >= 0) v = to_f32(xs[((size_t)b * a.n + pos) * a.D + c]);
-    else if (tail && (a.k - 1) + pos >= 0) v = to_f32(tail[(size_t)((a.k - 1) + pos) * a.D + c]);
+    if (pos >= 0) v = xs[((size_t)b * a.n + pos) * a.D + c];
+    else if (tail && (a.k - 1) + pos >= 0) v = tail[(size_t)((a.k - 1) + pos) * a.D + c];
     hist[j] = v;
   }
 }
@@ -67,7 +67,7 @@ template <class T, int MODE>
 __device__ __forceinline__ void scan_range(const ScanArgs &a, int b, int c, int t0, int t1,
                                            const ChanParams &p, float h[NS], float hist[KC - 1],
                                            float &dsum) {
-  const T *xs = reinterpret_cast<const T *>(a.xs);
+  const float *xs = a.xs;
   const T *z = reinterpret_cast<const T *>(a.z);
   T *y = reinterpret_cast<T *>(a.y);
   const size_t D = a.D;
@@ -78,7 +78,7 @@ __device__ __forceinline__ void scan_range(const ScanArgs &a, int b, int c, int 
       const int t = tb + i;
       const size_t idx = ((size_t)b * a.n + t) * D + c;
       const bool in = t < t1;
-      xv[i] = in ? to_f32(xs[idx]) : 0.0f;
+      xv[i] = in ? xs[idx] : 0.0f;
       dv[i] = in ? a.dt[idx] : 0.0f;
       if (MODE == 1) zv[i] = (in && z) ? to_f32(z[idx]) : 0.0f;
     }
@@ -189,8 +189,8 @@ __global__ void __launch_bounds__(64) scan_pass3(ScanArgs a) {
         *reinterpret_cast<float4 *>(ho + s) = make_float4(h[s], h[s + 1], h[s + 2], h[s + 3]);
     }
     if (a.tail_out) {
-      T *to = reinterpret_cast<T *>(a.tail_out) + (size_t)b * (a.k - 1) * a.D;
-      for (int j = 0; j < a.k - 1; ++j) to[(size_t)j * a.D + c] = from_f32<T>(hist[a.k - 2 - j]);
+      float *to = a.tail_out + (size_t)b * (a.k - 1) * a.D;
+      for (int j = 0; j < a.k - 1; ++j) to[(size_t)j * a.D + c] = hist[a.k - 2 - j];
     }
   }
 }

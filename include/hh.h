@@ -36,10 +36,10 @@
  * initialisation).
  *
  * Storage types: `dtype` (HH_F32 or HH_BF16) is the element type of x, out,
- * meta tokens, W_in, W_out, K/V buffers and caches, and the conv history.
- * dt_bias, A, conv_w, conv_b, the betas and the SSM state h are always fp32.
- * The bf16 path accumulates in fp32 and keeps Delta, B, C, softmax, norms and
- * the SSM state in fp32.
+ * meta tokens, W_in, W_out and the K/V buffers and caches.  dt_bias, A,
+ * conv_w, conv_b, the betas and the whole SSM state (h and the conv history)
+ * are always fp32.  The bf16 path accumulates in fp32 and keeps the SSM input
+ * features, Delta, B, C, softmax, norms and the SSM state in fp32.
  *
  * Supported shapes: head_dim 32 or 64 (bf16: 64); n_heads a multiple of
  * n_kv_heads with at most 8 query heads per KV head; d_state 16; d_conv 2..4;
@@ -99,11 +99,11 @@ typedef struct {
  *   k, v       [G, m, hd] dtype: meta keys/values (a consumer layer passes
  *              its producer's)
  *   h0         [D, N] fp32: SSM state after the m meta rows
- *   conv_tail  [k-1, D] dtype: xs of the last k-1 meta rows (oldest first) */
+ *   conv_tail  [k-1, D] fp32: xs of the last k-1 meta rows (oldest first) */
 typedef struct {
   const void *k, *v;
   const float *h0;
-  const void *conv_tail;
+  const float *conv_tail;
 } hh_meta;
 
 /* K/V of real tokens.
@@ -133,10 +133,10 @@ typedef struct {
 
 /* Per-sequence SSM state.
  *   h     [B, D, N] fp32
- *   conv  [B, k-1, D] dtype: xs of the last k-1 positions, oldest first. */
+ *   conv  [B, k-1, D] fp32: xs of the last k-1 positions, oldest first. */
 typedef struct {
   float *h;
-  void *conv;
+  float *conv;
 } hh_ssm_state;
 
 /* Library version string, e.g. "libhymba_hh 0.1.0 gfx950". */
@@ -152,11 +152,11 @@ size_t hh_meta_prefix_workspace_size(const hh_dims *dims, int32_t kv_producer);
  * offline).  meta_tokens [m, d_model] dtype.  Writes meta_k/meta_v
  * [G, m, hd] dtype (producer layers only; ignored and may be NULL for a
  * consumer), h0 [D, N] fp32 (state after the meta rows, from a zero state)
- * and conv_tail [k-1, D] dtype (xs of the last k-1 meta rows; zero rows in
+ * and conv_tail [k-1, D] fp32 (xs of the last k-1 meta rows; zero rows in
  * front when m < k-1). */
 hh_status hh_meta_prefix(const hh_dims *dims, const hh_weights *w,
                          const void *meta_tokens, void *meta_k, void *meta_v,
-                         float *h0, void *conv_tail, void *ws, size_t ws_bytes,
+                         float *h0, float *conv_tail, void *ws, size_t ws_bytes,
                          void *stream);
 
 /* Bytes of device workspace hh_prefill needs (0 on invalid arguments). */
@@ -203,7 +203,7 @@ enum {
   HH_WS_Q = 0,   /* [B*n, H*hd] dtype */
   HH_WS_K,       /* [B, G, n, hd] dtype (used when full_k is NULL) */
   HH_WS_V,
-  HH_WS_XS,      /* [B*n, D] dtype */
+  HH_WS_XS,      /* [B*n, D] fp32 SSM input features */
   HH_WS_Z,       /* [B*n, D] dtype */
   HH_WS_DELTA,   /* [B*n, D] fp32, softplus applied */
   HH_WS_BC,      /* [B*n, 2N] fp32: B then C */

@@ -51,7 +51,7 @@ def run_prefill(dims: LayerDims, weights: dict, R, x, window, is_global, produce
     xt = hb.to_device(x, sd)
     out = torch.empty(B, n, d, dtype=sd, device=dev)
     h = torch.empty(B, D, N, dtype=torch.float32, device=dev)
-    conv = torch.empty(B, k - 1, D, dtype=sd, device=dev)
+    conv = torch.empty(B, k - 1, D, dtype=torch.float32, device=dev)
     keep = dict(layer=layer, meta=meta, x=xt, out=out, h=h, conv=conv)
     if layer.kv_producer:
         mk, mv = meta["k"], meta["v"]
