@@ -1,0 +1,336 @@
+#!/usr/bin/env python3
+"""Benchmark of libhymba_hh on one MI355X.
+
+Headline step: one hh_prefill of the Hymba-1.5B-shaped sliding-window
+hybrid-head layer over 8192 tokens (batch 1, d_model 1600, 25/5 heads of 64,
+128 meta tokens, window 1024, d_inner 3200, state 16, conv 4), bf16 storage
+with fp32 accumulation, inputs already resident in HBM.  Reported beside it:
+the batch-128 decode step (SWA producer + SWA consumer sharing one ring KV
+cache + a global layer over 8192 cached positions).
+
+Prints ONE JSON line.  Per-kernel durations come from HIP events recorded
+by the library on the stream it launches on (hh_timing_*); the headline time
+is a separate event-bracketed loop without those per-stage events.
+
+  python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--only prefill|decode]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK = 2.5166e15   # dense bf16 FLOP/s, MI355X
+HBM_PEAK = 8.0e12            # bytes/s, MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (what the method must do; masked-out attention pairs and
+# padding are not counted)
+# ---------------------------------------------------------------------------
+def prefill_flops(dims, B, n, window, is_global, kv_producer=True):
+    m = dims.n_meta
+    T = B * n
+    inproj = 2.0 * T * dims.d_model * dims.n_in(kv_producer)
+    if is_global:
+        real_pairs = n * (n + 1) // 2
+    else:
+        W = window
+        real_pairs = sum(min(t + 1, W) for t in range(n)) if n <= 65536 else None
+    pairs = B * (m * n + real_pairs)
+    attention = 4.0 * dims.head_dim * dims.n_heads * pairs
+    outproj = 2.0 * T * dims.fused_width * dims.d_model
+    return dict(inproj=inproj, attention=attention, outproj=outproj,
+                total=inproj + attention + outproj)
+
+
+def decode_bytes(dims, B, layers, p, window, ring_cap, global_cap):
+    """Algorithmic HBM bytes of one decode step over `layers` (list of
+    (is_global, kv_producer)); p = position of the new token."""
+    es = 2
+    G, hd, m, D, N, k, d = (dims.n_kv_heads, dims.head_dim, dims.n_meta, dims.d_inner,
+                            dims.d_state, dims.d_conv, dims.d_model)
+    tot = 0.0
+    attn = 0.0
+    for is_global, prod in layers:
+        w = dims.n_in(prod) * d * es + d * dims.fused_width * es
+        small = 4 * (D + D * N + D * k + D + dims.attn_width + D)
+        ssm = B * D * N * 4 * 2 + B * (k - 1) * D * 4 * 2
+        io = B * d * es * 2
+        keys = (p + 1) if is_global else min(window, p + 1)
+        kv_read = B * G * keys * hd * es * 2 + G * m * hd * es * 2
+        append = B * G * hd * es * 2 if prod else 0
+        tot += w + small + ssm + io + kv_read + append
+        attn += kv_read
+    return tot, attn
+
+
+# ---------------------------------------------------------------------------
+def bench_prefill(args, hb, torch):
+    from hybrid_attention_ssm_amd.configs import CFG1_SWA_8K
+    from hybrid_attention_ssm_amd.synth import prefill_inputs
+    w = CFG1_SWA_8K
+    dims = w.dims
+    B, n, W = w.batch, w.seqlen, w.window
+    log(f"[bench] prefill setup {w.name}")
+    inp = prefill_inputs(w)
+    sd = hb.storage_dtype(dims)
+    dev = "cuda"
+    layer = hb.upload_weights(dims, inp["weights"])
+    meta = hb.hh_meta_prefix(layer, hb.to_device(inp["R"], sd))
+    x = hb.to_device(inp["x"], sd)
+    G, hd, D, N, k = dims.n_kv_heads, dims.head_dim, dims.d_inner, dims.d_state, dims.d_conv
+    out = torch.empty(B, n, dims.d_model, dtype=sd, device=dev)
+    full_k = torch.empty(B, G, n, hd, dtype=sd, device=dev)
+    full_v = torch.empty_like(full_k)
+    ck = torch.zeros(B, G, W, hd, dtype=sd, device=dev)
+    cv = torch.zeros_like(ck)
+    length = torch.zeros(B, dtype=torch.int32, device=dev)
+    h = torch.empty(B, D, N, dtype=torch.float32, device=dev)
+    conv = torch.empty(B, k - 1, D, dtype=torch.float32, device=dev)
+    ws = torch.empty(hb.hh_prefill_workspace_size(dims, B, n), dtype=torch.uint8, device=dev)
+    kv = hb.make_kv(full_k, full_v, ck, cv, length, W, True)
+    ms = hb.make_meta(meta["k"], meta["v"], meta["h0"], meta["conv_tail"])
+
+    def step():
+        hb.hh_prefill(layer, x, ms, W, False, out, kv=kv, state_h=h, state_conv=conv, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(args.steps):
+        step()
+    s1.record()
+    torch.cuda.synchronize()
+    ms_step = s0.elapsed_time(s1) / args.steps
+    # per-stage event timing over another K steps
+    hb.hh_timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    stages = hb.hh_timing_read()
+    hb.hh_timing_enable(False)
+    fl = prefill_flops(dims, B, n, W, False)
+    st_ms = {name: tot / cnt for name, (cnt, tot) in stages.items()}
+    log(f"[bench] prefill {ms_step:.3f} ms/step; stages " +
+        ", ".join(f"{k}={v * 1e3:.1f}us" for k, v in st_ms.items()))
+    return dict(workload=w.name, dims=dims, B=B, n=n, W=W, ms_step=ms_step, stages=st_ms,
+                flops=fl, inp=inp)
+
+
+def bench_decode(args, hb, torch):
+    from hybrid_attention_ssm_amd.configs import CFG3_DECODE
+    from hybrid_attention_ssm_amd.synth import decode_inputs
+    w = CFG3_DECODE
+    dims = w.dims
+    B, W = w.batch, w.window
+    log(f"[bench] decode setup {w.name}")
+    inp = decode_inputs(w)
+    sd = hb.storage_dtype(dims)
+    dev = "cuda"
+    slack = args.warmup + 2 * args.steps + 2
+    caches = {}
+    for name, c in inp["caches"].items():
+        cap = c["cap"] if c["is_ring"] else c["cap"] + slack   # the linear cache grows one per step
+        kk = torch.zeros(B, dims.n_kv_heads, cap, dims.head_dim, dtype=sd, device=dev)
+        vv = torch.zeros_like(kk)
+        kk[:, :, :c["cap"]] = hb.to_device(c["k"], sd)
+        vv[:, :, :c["cap"]] = hb.to_device(c["v"], sd)
+        ln = hb.to_device(c["len"], torch.int32)
+        caches[name] = dict(k=kk, v=vv, len=ln, cap=cap, is_ring=c["is_ring"],
+                            mk=hb.to_device(c["meta_k"], sd), mv=hb.to_device(c["meta_v"], sd))
+        caches[name]["kv"] = hb.make_kv(None, None, kk, vv, ln, cap, c["is_ring"])
+        caches[name]["meta"] = hb.make_meta(caches[name]["mk"], caches[name]["mv"], None, None)
+    layers = []
+    for lay in inp["layers"]:
+        spec = lay["spec"]
+        layers.append(dict(
+            spec=spec, layer=hb.upload_weights(dims, lay["weights"]),
+            h=hb.to_device(lay["h"], torch.float32), conv=hb.to_device(lay["conv"], torch.float32),
+            x=hb.to_device(lay["x_t"], sd),
+            out=torch.empty(B, dims.d_model, dtype=sd, device=dev)))
+    wsz = max(hb.hh_decode_workspace_size(dims, B, caches[L["spec"].cache]["cap"],
+                                          L["spec"].kv_producer) for L in layers)
+    ws = torch.empty(wsz, dtype=torch.uint8, device=dev)
+
+    def step():
+        for L in layers:
+            c = caches[L["spec"].cache]
+            hb.hh_decode_step(L["layer"], L["x"], c["meta"], W, L["spec"].is_global, c["kv"],
+                              L["h"], L["conv"], L["out"], ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    p_first = int(caches["global"]["len"][0].item())
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(args.steps):
+        step()
+    s1.record()
+    torch.cuda.synchronize()
+    ms_step = s0.elapsed_time(s1) / args.steps
+    hb.hh_timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    stages = hb.hh_timing_read()
+    hb.hh_timing_enable(False)
+    specs = [(L["spec"].is_global, L["spec"].kv_producer) for L in layers]
+    p_mid = p_first + args.steps // 2          # mean position over the timed steps
+    tot_bytes, attn_bytes = decode_bytes(dims, B, specs, p_mid, W, W, w.global_cap)
+    # the stage loop ran at positions p_first + steps .. p_first + 2 steps - 1
+    _, attn_bytes_stage = decode_bytes(dims, B, specs, p_first + args.steps + args.steps // 2,
+                                       W, W, w.global_cap)
+    st = {name: (cnt, tot) for name, (cnt, tot) in stages.items()}
+    log(f"[bench] decode {ms_step:.3f} ms/step; stages " +
+        ", ".join(f"{k}={v[1] / v[0] * 1e3:.1f}us x{v[0]}" for k, v in st.items()))
+    return dict(workload=w.name, B=B, ms_step=ms_step, stages=st, bytes=tot_bytes,
+                attn_bytes_step=attn_bytes_stage, inp=inp, context=p_first)
+
+
+# ---------------------------------------------------------------------------
+def cpu_baseline(pre, dec, args):
+    """The CPU oracle (as it stands) on a bounded sample of each workload."""
+    import numpy as np
+    from oracle import hymba_ref as ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    res = {}
+    if pre is not None:
+        inp = pre["inp"]
+        ns = args.cpu_sample_tokens
+        dims = pre["dims"]
+        t0 = time.perf_counter()
+        ref.prefill(dims.as_dict(), inp["weights"], inp["R"], inp["x"][:, :ns], pre["W"], False)
+        dt = time.perf_counter() - t0
+        res["prefill"] = dict(value=ns / dt, seconds=dt,
+                              sample=f"oracle prefill of the first {ns} of the 8192 tokens "
+                                     f"(same layer, meta rows included), fp64")
+    if dec is not None:
+        from hybrid_attention_ssm_amd.configs import CFG3_DECODE
+        w = CFG3_DECODE
+        inp = dec["inp"]
+        S = np.arange(args.cpu_sample_seqs)
+        t0 = time.perf_counter()
+        caches = {name: dict(k=c["k"][S], v=c["v"][S], len=c["len"][S], is_ring=c["is_ring"])
+                  for name, c in inp["caches"].items()}
+        for lay in inp["layers"]:
+            spec = lay["spec"]
+            c = inp["caches"][spec.cache]
+            r = ref.decode_step(w.dims.as_dict(), lay["weights"], lay["x_t"][S], c["meta_k"],
+                                c["meta_v"], w.window, spec.is_global, caches[spec.cache],
+                                lay["h"][S], lay["conv"][S])
+            if spec.kv_producer:
+                caches[spec.cache] = dict(k=r["cache_k"], v=r["cache_v"], len=r["len"],
+                                          is_ring=c["is_ring"])
+        dt = time.perf_counter() - t0
+        res["decode"] = dict(value=len(S) / dt, seconds=dt,
+                             sample=f"oracle decode step (3 layers) for {len(S)} of the 128 "
+                                    f"sequences, fp64")
+    res["cores"] = threads
+    res["cpu"] = platform.processor() or platform.machine()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", choices=["prefill", "decode", "both"], default="both")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-sample-seqs", type=int, default=4)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus}, WORLD_SIZE "
+              f"{world} requested); the layer's multi-GPU sharding is a design note, not built.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from hybrid_attention_ssm_amd import binding as hb
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    hb.lib()
+
+    pre = bench_prefill(args, hb, torch) if args.only in ("prefill", "both") else None
+    dec = bench_decode(args, hb, torch) if args.only in ("decode", "both") else None
+
+    rec = {"metric": "hybrid-head layer prefill tok/s @8k + decode tok/s @B128; % of MFMA/HBM peak",
+           "higher_is_better": True, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "unit": "tok/s"}
+    if pre is not None:
+        fl = pre["flops"]
+        toks = pre["B"] * pre["n"] / (pre["ms_step"] * 1e-3)
+        t_in = pre["stages"].get("inproj")
+        rec.update(value=toks, ms_per_step=pre["ms_step"])
+        rec["config"] = {"workload": f"{pre['workload']}: Hymba-1.5B-shaped SWA hybrid-head "
+                                     f"layer prefill (d 1600, 25/5 heads x 64, 128 meta, W 1024, "
+                                     f"d_inner 3200, N 16, conv 4)",
+                         "global_batch": pre["B"], "seq_len": pre["n"], "parallelism": "none"}
+        rec["mfma_frac_layer"] = fl["total"] / (pre["ms_step"] * 1e-3) / MFMA_BF16_PEAK
+        rec["algorithmic_gflop_per_step"] = fl["total"] / 1e9
+        rec["stage_us"] = {k: v * 1e3 for k, v in pre["stages"].items()}
+        if t_in:
+            ach = fl["inproj"] / (t_in * 1e-3)
+            rec["roofline"] = {"kernel": "inproj (gemm_bf16_mfma, split epilogue)", "bound": "mfma",
+                               "achieved": ach / 1e12, "peak": MFMA_BF16_PEAK / 1e12,
+                               "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK, "traffic": None,
+                               "flop_per_launch": fl["inproj"], "avg_launch_us": t_in * 1e3}
+    if dec is not None:
+        B = dec["B"]
+        st = dec["stages"]
+        d = {"workload": f"{dec['workload']}: 3 layers per step (SWA producer + SWA consumer "
+                         f"sharing a 1024-slot ring cache, global layer over the full cache), "
+                         f"context {dec['context']}+",
+             "value": B / (dec["ms_step"] * 1e-3), "unit": "tok/s", "ms_per_step": dec["ms_step"],
+             "hbm_frac_step": dec["bytes"] / (dec["ms_step"] * 1e-3) / HBM_PEAK,
+             "algorithmic_bytes_per_step": dec["bytes"],
+             "stage_us": {k: v[1] / v[0] * 1e3 for k, v in st.items()}}
+        if "decode_attention" in st:
+            cnt, tot = st["decode_attention"]
+            steps = cnt / 3.0
+            ach = dec["attn_bytes_step"] * steps / (tot * 1e-3)
+            d["roofline"] = {"kernel": "decode_attention (split-K + combine), 3 layers",
+                             "bound": "hbm", "achieved": ach / 1e9, "peak": HBM_PEAK / 1e9,
+                             "unit": "GB/s", "frac": ach / HBM_PEAK, "traffic": None}
+        rec["decode"] = d
+        if pre is None:
+            rec.update(value=d["value"], ms_per_step=d["ms_per_step"],
+                       config={"workload": d["workload"], "global_batch": B, "seq_len": 1,
+                               "parallelism": "none"})
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        cb = cpu_baseline(pre, dec, args)
+        main_key = "prefill" if pre is not None else "decode"
+        rec["cpu_baseline"] = {"value": cb[main_key]["value"], "unit": "tok/s", "cores": cb["cores"],
+                               "kind": "oracle", "sample": cb[main_key]["sample"],
+                               "seconds": cb[main_key]["seconds"], "cpu": cb["cpu"]}
+        if pre is not None and "decode" in cb:
+            rec["cpu_baseline"]["decode"] = cb["decode"]
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

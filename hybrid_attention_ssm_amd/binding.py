@@ -51,6 +51,10 @@ class HHSsmState(ctypes.Structure):
     _fields_ = [("h", _vp), ("conv", _vp)]
 
 
+class HHStageTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", _i32), ("total_ms", ctypes.c_double)]
+
+
 class HHError(RuntimeError):
     def __init__(self, fn, status, msg):
         super().__init__(f"{fn}: {STATUS.get(status, status)}: {msg}")
@@ -88,6 +92,10 @@ def lib() -> ctypes.CDLL:
         L.hh_decode_step.restype = ctypes.c_int
         L.hh_decode_step.argtypes = [P(HHDims), P(HHWeights), _vp, _i32, P(HHMeta), _i32, _i32,
                                      P(HHKV), P(HHSsmState), _vp, _vp, ctypes.c_size_t, _vp]
+        L.hh_timing_enable.restype = ctypes.c_int
+        L.hh_timing_enable.argtypes = [_i32]
+        L.hh_timing_read.restype = _i32
+        L.hh_timing_read.argtypes = [ctypes.POINTER(HHStageTime), _i32]
         _lib = L
     return _lib
 
@@ -276,3 +284,16 @@ def hh_decode_step(layer: DeviceLayer, x_t: torch.Tensor, meta: HHMeta, window: 
 
 def to_device(a: np.ndarray, dtype: torch.dtype, device="cuda") -> torch.Tensor:
     return torch.as_tensor(np.ascontiguousarray(a)).to(device=device, dtype=dtype).contiguous()
+
+
+def hh_timing_enable(on: bool = True) -> None:
+    _check("hh_timing_enable", lib().hh_timing_enable(int(bool(on))))
+
+
+def hh_timing_read(max_stages: int = 32) -> dict:
+    """{stage: (launches, total_ms)} since the last read; clears the record."""
+    buf = (HHStageTime * max_stages)()
+    n = lib().hh_timing_read(buf, max_stages)
+    if n < 0:
+        raise HHError("hh_timing_read", 4, "HIP error while reading stage events")
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(n)}

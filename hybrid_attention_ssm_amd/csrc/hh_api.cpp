@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "../../include/hh.h"
 #include "hh_internal.h"
@@ -25,6 +26,42 @@ hh_status fail(hh_status st, const char *fmt, ...) {
   g_err = buf;
   return st;
 }
+
+// ---- optional per-stage event timing ---------------------------------------
+struct TimingRec {
+  const char *stage;
+  hipEvent_t start, stop;
+};
+struct Timing {
+  bool on = false;
+  std::vector<TimingRec> recs;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t get() {
+    if (!pool.empty()) { hipEvent_t e = pool.back(); pool.pop_back(); return e; }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+thread_local Timing g_timing;
+
+// Brackets one stage's launches with events when timing is enabled.
+struct Stage {
+  hipStream_t st;
+  TimingRec rec{nullptr, nullptr, nullptr};
+  Stage(hipStream_t s, const char *name) : st(s) {
+    if (!g_timing.on) return;
+    rec.stage = name;
+    rec.start = g_timing.get();
+    rec.stop = g_timing.get();
+    if (rec.start) hipEventRecord(rec.start, st);
+  }
+  ~Stage() {
+    if (!rec.stage || !rec.start || !rec.stop) return;
+    hipEventRecord(rec.stop, st);
+    g_timing.recs.push_back(rec);
+  }
+};
 
 hh_status hip_fail(hipError_t e, const char *where) {
   return fail(HH_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
@@ -140,6 +177,8 @@ char *at(void *ws, size_t off) { return static_cast<char *>(ws) + off; }
 template <class T>
 hh_status run_inproj(const Shape &s, const hh_weights *w, const void *x, int M,
                      const hh::InProjOut &e, hipStream_t st) {
+  Stage sg(st, e.mode == hh::EPI_DECODE ? "decode_inproj"
+              : e.mode == hh::EPI_META ? "meta_inproj" : "inproj");
   hipError_t err = hh::launch_inproj<T>(static_cast<const T *>(x), M, s.d,
                                         static_cast<const T *>(w->w_in), s.n_in, e, st);
   return err == hipSuccess ? HH_OK : hip_fail(err, "input projection");
@@ -174,7 +213,11 @@ hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, i
   aa.o = at(ws, L.off[HH_WS_O]);
   aa.B = B; aa.n = n; aa.m = s.m; aa.H = s.H; aa.G = s.G; aa.hd = s.hd;
   aa.window = window; aa.is_global = is_global;
-  hipError_t err = hh::launch_attention<T>(aa, st);
+  hipError_t err;
+  {
+    Stage sg(st, "attention");
+    err = hh::launch_attention<T>(aa, st);
+  }
   if (err != hipSuccess) return hip_fail(err, "attention");
 
   hh::ScanArgs sa{};
@@ -186,18 +229,27 @@ hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, i
   sa.tail_out = state ? state->conv : nullptr;
   sa.carry = reinterpret_cast<float *>(at(ws, L.off[HH_WS_SCAN]));
   sa.B = B; sa.n = n; sa.D = s.D; sa.N = s.N; sa.k = s.k; sa.chunk = L.chunk;
-  err = hh::launch_scan<T>(sa, st);
+  {
+    Stage sg(st, "scan");
+    err = hh::launch_scan<T>(sa, st);
+  }
   if (err != hipSuccess) return hip_fail(err, "selective scan");
 
   hh::NormArgs na{};
   na.o = aa.o; na.y = sa.y; na.beta_attn = w->beta_attn; na.beta_ssm = w->beta_ssm;
   na.f = at(ws, L.off[HH_WS_F]);
   na.rows = rows; na.Wa = s.Wa; na.D = s.D; na.eps = s.eps;
-  err = hh::launch_norm_fuse<T>(na, st);
+  {
+    Stage sg(st, "norm");
+    err = hh::launch_norm_fuse<T>(na, st);
+  }
   if (err != hipSuccess) return hip_fail(err, "norm/average");
 
-  err = hh::launch_outproj<T>(static_cast<const T *>(na.f), rows, s.Wa + s.D,
-                              static_cast<const T *>(w->w_out), s.d, static_cast<T *>(out), st);
+  {
+    Stage sg(st, "outproj");
+    err = hh::launch_outproj<T>(static_cast<const T *>(na.f), rows, s.Wa + s.D,
+                                static_cast<const T *>(w->w_out), s.d, static_cast<T *>(out), st);
+  }
   if (err != hipSuccess) return hip_fail(err, "output projection");
 
   if (prod && kv && kv->len) {
@@ -258,7 +310,11 @@ hh_status decode_t(const Shape &s, const hh_weights *w, const void *x, int B, co
   da.B = B; da.H = s.H; da.G = s.G; da.hd = s.hd; da.m = s.m; da.cap = kv->cap;
   da.is_ring = kv->is_ring; da.window = window; da.is_global = is_global;
   da.nsplit = L.nsplit;
-  hipError_t err = hh::launch_decode_attention<T>(da, st);
+  hipError_t err;
+  {
+    Stage sg(st, "decode_attention");
+    err = hh::launch_decode_attention<T>(da, st);
+  }
   if (err != hipSuccess) return hip_fail(err, "decode attention");
 
   hh::DecodeSsmArgs sa{};
@@ -266,18 +322,27 @@ hh_status decode_t(const Shape &s, const hh_weights *w, const void *x, int B, co
   sa.A = w->A; sa.conv_w = w->conv_w; sa.conv_b = w->conv_b;
   sa.h = state->h; sa.conv = state->conv; sa.y = at(ws, L.y);
   sa.B = B; sa.D = s.D; sa.N = s.N; sa.k = s.k;
-  err = hh::launch_decode_ssm<T>(sa, st);
+  {
+    Stage sg(st, "decode_ssm");
+    err = hh::launch_decode_ssm<T>(sa, st);
+  }
   if (err != hipSuccess) return hip_fail(err, "decode SSM step");
 
   hh::NormArgs na{};
   na.o = da.o; na.y = sa.y; na.beta_attn = w->beta_attn; na.beta_ssm = w->beta_ssm;
   na.f = at(ws, L.f);
   na.rows = B; na.Wa = s.Wa; na.D = s.D; na.eps = s.eps;
-  err = hh::launch_norm_fuse<T>(na, st);
+  {
+    Stage sg(st, "decode_norm");
+    err = hh::launch_norm_fuse<T>(na, st);
+  }
   if (err != hipSuccess) return hip_fail(err, "decode norm/average");
 
-  err = hh::launch_outproj<T>(static_cast<const T *>(na.f), B, s.Wa + s.D,
-                              static_cast<const T *>(w->w_out), s.d, static_cast<T *>(out), st);
+  {
+    Stage sg(st, "decode_outproj");
+    err = hh::launch_outproj<T>(static_cast<const T *>(na.f), B, s.Wa + s.D,
+                                static_cast<const T *>(w->w_out), s.d, static_cast<T *>(out), st);
+  }
   if (err != hipSuccess) return hip_fail(err, "decode output projection");
   if (prod) {
     err = hh::launch_bump_len(kv->len, B, kv->cap, kv->is_ring, st);
@@ -298,6 +363,37 @@ extern "C" {
 const char *hh_version(void) { return "libhymba_hh 0.1.0 gfx950"; }
 
 const char *hh_last_error(void) { return g_err.c_str(); }
+
+hh_status hh_timing_enable(int32_t on) {
+  g_timing.on = on != 0;
+  return HH_OK;
+}
+
+int32_t hh_timing_read(hh_stage_time *out, int32_t max_stages) {
+  std::vector<hh_stage_time> agg;
+  int32_t rc = 0;
+  for (TimingRec &r : g_timing.recs) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess)
+      rc = -1;
+    size_t i = 0;
+    while (i < agg.size() && std::strcmp(agg[i].name, r.stage) != 0) ++i;
+    if (i == agg.size()) {
+      hh_stage_time t{};
+      std::snprintf(t.name, sizeof t.name, "%s", r.stage);
+      agg.push_back(t);
+    }
+    agg[i].launches += 1;
+    agg[i].total_ms += ms;
+    g_timing.pool.push_back(r.start);
+    g_timing.pool.push_back(r.stop);
+  }
+  g_timing.recs.clear();
+  if (rc < 0) return rc;
+  const int32_t n = std::min<int32_t>((int32_t)agg.size(), max_stages);
+  for (int32_t i = 0; i < n && out; ++i) out[i] = agg[i];
+  return n;
+}
 
 size_t hh_prefill_workspace_layout(const hh_dims *dims, int32_t batch, int32_t seqlen,
                                    int32_t kv_producer, size_t *offs) {

@@ -217,6 +217,21 @@ size_t hh_prefill_workspace_layout(const hh_dims *dims, int32_t batch,
                                    int32_t seqlen, int32_t kv_producer,
                                    size_t *offs);
 
+/* Per-stage GPU timing (measurement aid, off by default).  While enabled on
+ * the calling thread, each kernel stage an entry point enqueues (in-proj GEMM,
+ * attention, scan, norm/average, out-proj GEMM, decode kernels) is bracketed
+ * by HIP events recorded on the caller's stream.  hh_timing_read waits for the
+ * recorded events, writes up to max_stages per-stage summaries (launches and
+ * summed milliseconds, stages in first-seen order), clears the record and
+ * returns the number of stages written, or -1 on a HIP error. */
+typedef struct {
+  char name[32];
+  int32_t launches;
+  double total_ms;
+} hh_stage_time;
+hh_status hh_timing_enable(int32_t on);
+int32_t hh_timing_read(hh_stage_time *out, int32_t max_stages);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,132 @@
+"""Full-size parity: the five workloads at their real shapes, in the launch
+configuration the benchmark times, checked on sampled outputs.
+
+Prefill (8k SWA, 8k global, 2 x 32k SWA): the oracle runs the literal
+projection and the full sequential scan (every state is needed), and
+per-query attention only for the sampled rows; compared are the layer output
+at those rows, the final SSM state and conv history of every sequence, and
+the K/V rows (full buffer and ring-cache slots) of the sampled positions.
+Decode (batch 128, 3 layers): the oracle steps a sample of sequences through
+the same three layers; compared are their outputs, states and the appended
+cache slots, and every other cache slot must be unchanged bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+from hybrid_attention_ssm_amd import binding as hb
+from hybrid_attention_ssm_amd.configs import (CFG1_SWA_8K, CFG2_GLOBAL_8K, CFG3_DECODE,
+                                              CFG4_SWA_32K)
+from hybrid_attention_ssm_amd.synth import decode_inputs, prefill_inputs
+from oracle import hymba_ref as ref
+from tests.harness import TOL, np_of, rel_err, run_prefill
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def _rows(n, W, seed, extra=16):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 2, 31, 32, 63, 64, 127, 128, W - 1, W, W + 1, n // 2, n - 65, n - 2, n - 1]
+    r = set(int(v) for v in fixed if 0 <= v < n)
+    r.update(int(v) for v in rng.choice(n, extra, replace=False))
+    return np.array(sorted(r))
+
+
+@pytest.mark.parametrize("w", [CFG1_SWA_8K, CFG2_GLOBAL_8K, CFG4_SWA_32K], ids=lambda w: w.name)
+def test_prefill_full_size(w):
+    dims = w.dims
+    print(f"case {w.name} B={w.batch} n={w.seqlen}", flush=True)
+    inp = prefill_inputs(w)
+    ring = not w.is_global
+    cap = w.window if ring else w.seqlen
+    got = run_prefill(dims, inp["weights"], inp["R"], inp["x"], w.window, w.is_global,
+                      cache_cap=cap, cache_ring=ring)
+    out = np_of(got["out"])
+    h = np_of(got["h"])
+    conv = np_of(got["conv"])
+    fk, fv = got["full_k"], got["full_v"]
+    ck, cv = got["cache_k"], got["cache_v"]
+    rows = _rows(w.seqlen, w.window, w.seed)
+    tol = TOL[dims.dtype]
+    for b in range(w.batch):
+        want = ref.prefill(dims.as_dict(), inp["weights"], inp["R"], inp["x"][b:b + 1],
+                           w.window, w.is_global, rows=rows)
+        e_out = rel_err(out[b, rows], want["out"][0])
+        e_h = rel_err(h[b], want["h"][0])
+        e_c = rel_err(conv[b], want["conv_tail"][0])
+        e_k = rel_err(np_of(fk[b][:, rows]), want["k_full"][0][:, rows])
+        e_v = rel_err(np_of(fv[b][:, rows]), want["v_full"][0][:, rows])
+        print(f"  b={b} err out={e_out:.2e} h={e_h:.2e} conv={e_c:.2e} k={e_k:.2e} v={e_v:.2e}",
+              flush=True)
+        assert max(e_out, e_h, e_c, e_k, e_v) <= tol
+        # cache slot of each sampled position that the cache keeps: same bits
+        # as that position's row of the full K/V buffer
+        keep = rows[rows >= w.seqlen - cap] if ring else rows[rows < cap]
+        slots = keep % cap if ring else keep
+        assert torch.equal(ck[b][:, slots], fk[b][:, keep])
+        assert torch.equal(cv[b][:, slots], fv[b][:, keep])
+    assert (got["len"].cpu().numpy() == w.seqlen).all()
+
+
+def test_decode_full_size():
+    w = CFG3_DECODE
+    dims = w.dims
+    B = w.batch
+    print(f"case {w.name}", flush=True)
+    inp = decode_inputs(w)
+    sd = hb.storage_dtype(dims)
+    caches = {}
+    before = {}
+    for name, c in inp["caches"].items():
+        kk, vv = hb.to_device(c["k"], sd), hb.to_device(c["v"], sd)
+        ln = hb.to_device(c["len"], torch.int32)
+        mk, mv = hb.to_device(c["meta_k"], sd), hb.to_device(c["meta_v"], sd)
+        caches[name] = dict(k=kk, v=vv, len=ln, mk=mk, mv=mv,
+                            kv=hb.make_kv(None, None, kk, vv, ln, c["cap"], c["is_ring"]),
+                            meta=hb.make_meta(mk, mv, None, None))
+        before[name] = (kk.clone(), vv.clone())
+    outs, states = [], []
+    for lay in inp["layers"]:
+        spec = lay["spec"]
+        c = caches[spec.cache]
+        layer = hb.upload_weights(dims, lay["weights"])
+        h = hb.to_device(lay["h"], torch.float32)
+        cv = hb.to_device(lay["conv"], torch.float32)
+        out = torch.empty(B, dims.d_model, dtype=sd, device="cuda")
+        hb.hh_decode_step(layer, hb.to_device(lay["x_t"], sd), c["meta"], w.window, spec.is_global,
+                          c["kv"], h, cv, out)
+        torch.cuda.synchronize()
+        outs.append(np_of(out))
+        states.append((np_of(h), np_of(cv), layer))
+    S = np.array([0, 1, 63, 64, 100, 127])
+    ocaches = {name: dict(k=c["k"][S].astype(np.float64), v=c["v"][S].astype(np.float64),
+                          len=c["len"][S], is_ring=c["is_ring"]) for name, c in inp["caches"].items()}
+    tol = TOL[dims.dtype]
+    p = w.context
+    for i, lay in enumerate(inp["layers"]):
+        spec = lay["spec"]
+        c = inp["caches"][spec.cache]
+        r = ref.decode_step(dims.as_dict(), lay["weights"], lay["x_t"][S], c["meta_k"], c["meta_v"],
+                            w.window, spec.is_global, ocaches[spec.cache], lay["h"][S], lay["conv"][S])
+        e_out = rel_err(outs[i][S], r["out"])
+        e_h = rel_err(states[i][0][S], r["h"])
+        e_c = rel_err(states[i][1][S], r["conv"])
+        print(f"  layer {i} ({spec.cache}, producer={spec.kv_producer}) err out={e_out:.2e} "
+              f"h={e_h:.2e} conv={e_c:.2e}", flush=True)
+        assert max(e_out, e_h, e_c) <= tol
+        if spec.kv_producer:
+            ocaches[spec.cache] = dict(k=r["cache_k"], v=r["cache_v"], len=r["len"],
+                                       is_ring=c["is_ring"])
+    for name, c in inp["caches"].items():
+        slot = p % c["cap"] if c["is_ring"] else p
+        g = caches[name]
+        k0, v0 = before[name]
+        # the appended slot matches the oracle within tolerance ...
+        assert rel_err(np_of(g["k"][S][:, :, slot]), ocaches[name]["k"][:, :, slot]) <= tol
+        assert rel_err(np_of(g["v"][S][:, :, slot]), ocaches[name]["v"][:, :, slot]) <= tol
+        # ... and no other slot changed
+        mask = torch.ones(c["cap"], dtype=torch.bool, device="cuda")
+        mask[slot] = False
+        assert torch.equal(g["k"][:, :, mask], k0[:, :, mask])
+        assert torch.equal(g["v"][:, :, mask], v0[:, :, mask])
+        assert (g["len"].cpu().numpy() == p + 1).all()
