@@ -142,20 +142,36 @@ gemm_bf16_mfma(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, in
     __syncthreads();
   }
 
-  // 32x32 accumulator layout: lane holds column lane%32; register r holds
-  // row 8*(r/4) + 4*(lane/32) + r%4.
+  // Epilogue.  32x32 accumulator layout: lane holds column lane%32, register
+  // r holds row 8*(r/4) + 4*(lane/32) + r%4.  Each wave stages one 32-row
+  // strip of its tile through LDS (static register indexing keeps the
+  // accumulators in registers), then reads it back row-major so that every
+  // lane hands 8 consecutive columns to the epilogue.
+  constexpr int SROW = Cfg::WN + 8;             // padded strip row (floats)
+  constexpr int LPR = Cfg::WN / 8;              // lanes per strip row
+  constexpr int RPI = 64 / LPR;                 // strip rows per pass
+  float *strip = reinterpret_cast<float *>(smem) + wave * 32 * SROW;
 #pragma unroll
-  for (int i = 0; i < Cfg::TM; ++i)
+  for (int i = 0; i < Cfg::TM; ++i) {
 #pragma unroll
-    for (int j = 0; j < Cfg::TN; ++j) {
-      const int col = n0 + wn * Cfg::WN + j * 32 + lr;
-      if (col >= N) continue;
+    for (int j = 0; j < Cfg::TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * Cfg::WM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-        if (row < M) epi(row, col, acc[i][j][r]);
-      }
+      for (int r = 0; r < 16; ++r)
+        strip[(8 * (r >> 2) + 4 * lh + (r & 3)) * SROW + j * 32 + lr] = acc[i][j][r];
+    __syncthreads();
+#pragma unroll 1
+    for (int it = 0; it < 32 / RPI; ++it) {
+      const int rr = it * RPI + lane / LPR;
+      const int cc = (lane % LPR) * 8;
+      const float4 a = *reinterpret_cast<const float4 *>(strip + rr * SROW + cc);
+      const float4 b = *reinterpret_cast<const float4 *>(strip + rr * SROW + cc + 4);
+      const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      const int row = m0 + wm * Cfg::WM + i * 32 + rr;
+      const int col = n0 + wn * Cfg::WN + cc;
+      if (row < M && col < N) epi.store8(row, col, v);
     }
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -215,6 +231,9 @@ struct InProjEpi {
   __device__ __forceinline__ void operator()(int row, int col, float v) const {
     inproj_store<T>(e, row, col, v);
   }
+  __device__ __forceinline__ void store8(int row, int col, const float v[8]) const {
+    inproj_store8<T>(e, row, col, v);
+  }
 };
 
 template <class T>
@@ -223,6 +242,9 @@ struct StoreEpi {
   int ld;
   __device__ __forceinline__ void operator()(int row, int col, float v) const {
     out[(size_t)row * ld + col] = from_f32<T>(v);
+  }
+  __device__ __forceinline__ void store8(int row, int col, const float v[8]) const {
+    store8_T(out + (size_t)row * ld + col, v);
   }
 };
 

@@ -35,9 +35,14 @@ __device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcp
 __device__ __forceinline__ float silu_f(float x) {
   return x * rcp_fast(1.0f + exp2_fast(-x * kLog2e));
 }
-// log(1 + e^v) without overflow: max(v, 0) + log1p(e^-|v|)
+// log(1 + e^v) without overflow: max(v, 0) + log1p(t), t = e^-|v| in (0, 1].
+// log1p(t) = log(u) * t / (u - 1) with u = fl(1 + t) cancels the rounding of
+// 1 + t (Kahan's correction), so small t keeps full relative accuracy.
 __device__ __forceinline__ float softplus_f(float v) {
-  return fmaxf(v, 0.0f) + log1pf(__expf(-fabsf(v)));
+  const float t = __expf(-fabsf(v));
+  const float u = 1.0f + t;
+  const float l1p = (u == 1.0f) ? t : __logf(u) * __fdividef(t, u - 1.0f);
+  return fmaxf(v, 0.0f) + l1p;
 }
 
 // ---- the in-projection column map ------------------------------------------
@@ -106,6 +111,70 @@ __device__ __forceinline__ void inproj_store(const InProjOut &e, int row, int co
   if (col < D) { e.dt[(size_t)row * D + col] = softplus_f(v + e.dt_bias[col]); return; }
   col -= D;
   e.bc[(size_t)row * 2 * e.N + col] = v;
+}
+
+// Store 8 consecutive columns col..col+7 of one row (col % 8 == 0).  Every
+// column-block boundary of the map is a multiple of 8, so the 8 values always
+// belong to one block and are written with vector stores.
+template <class T>
+__device__ __forceinline__ void store8_T(T *dst, const float v[8]) {
+  if constexpr (sizeof(T) == 2) {
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (bf16)v[e];
+    *reinterpret_cast<bf16x8 *>(dst) = o;
+  } else {
+    *reinterpret_cast<float4 *>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4 *>(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+template <class T>
+__device__ __forceinline__ void inproj_store8(const InProjOut &e, int row, int col, const float v[8]) {
+  const int Wa = e.Wa, KV = e.KV, D = e.D;
+  if (col < Wa) { store8_T(reinterpret_cast<T *>(e.q) + (size_t)row * Wa + col, v); return; }
+  col -= Wa;
+  if (col < 2 * KV) {
+    const bool isv = col >= KV;
+    const int c = isv ? col - KV : col;
+    const int g = c / e.hd, d = c - g * e.hd;
+    const int G = KV / e.hd;
+    if (e.mode == EPI_DECODE) {
+      const int p = e.len[row];
+      if (p < 0 || (!e.is_ring && p >= e.cap)) return;
+      const int slot = e.is_ring ? p % e.cap : p;
+      T *dst = reinterpret_cast<T *>(isv ? e.cache_v : e.cache_k);
+      store8_T(dst + (((size_t)row * G + g) * e.cap + slot) * e.hd + d, v);
+      return;
+    }
+    const int n = e.n_rows_per_seq;
+    const int b = row / n, p = row - b * n;
+    T *full = reinterpret_cast<T *>(isv ? e.v_full : e.k_full);
+    store8_T(full + (((size_t)b * G + g) * n + p) * e.hd + d, v);
+    if (e.mode == EPI_PREFILL && e.cache_k) {
+      const bool keep = e.is_ring ? (p >= n - e.cap) : (p < e.cap);
+      if (keep) {
+        const int slot = e.is_ring ? p % e.cap : p;
+        T *dst = reinterpret_cast<T *>(isv ? e.cache_v : e.cache_k);
+        store8_T(dst + (((size_t)b * G + g) * e.cap + slot) * e.hd + d, v);
+      }
+    }
+    return;
+  }
+  col -= 2 * KV;
+  if (col < D) { store8_T(e.xs + (size_t)row * D + col, v); return; }
+  col -= D;
+  if (col < D) { store8_T(reinterpret_cast<T *>(e.z) + (size_t)row * D + col, v); return; }
+  col -= D;
+  if (col < D) {
+    float sp[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sp[i] = softplus_f(v[i] + e.dt_bias[col + i]);
+    store8_T(e.dt + (size_t)row * D + col, sp);
+    return;
+  }
+  col -= D;
+  store8_T(e.bc + (size_t)row * 2 * e.N + col, v);
 }
 
 // ---- launchers (each returns hipGetLastError() of its launches) ------------

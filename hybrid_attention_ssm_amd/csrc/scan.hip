@@ -134,26 +134,36 @@ __global__ void __launch_bounds__(64) scan_pass1(ScanArgs a) {
   ds[((size_t)b * nc + ck) * a.D + c] = dsum;
 }
 
-// pass 2: chunk carries in order.  grid (ceil(D/64), B)
-__global__ void __launch_bounds__(64) scan_pass2(ScanArgs a) {
+// pass 2: chunk carries in order.  One lane per (channel, state) recurrence;
+// the loads of a group of chunks do not depend on the carry, so they are
+// issued together.  grid (ceil(N*D/256), B), 256 threads
+__global__ void __launch_bounds__(256) scan_pass2(ScanArgs a) {
+  constexpr int U = 8;
   const int b = blockIdx.y;
-  const int c = blockIdx.x * 64 + threadIdx.x;
-  if (c >= a.D) return;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= NS * a.D) return;
+  const int s = idx / a.D, c = idx - s * a.D;
   const int nc = (a.n + a.chunk - 1) / a.chunk;
-  float A2[NS], H[NS];
+  const float A2 = a.A[(size_t)c * NS + s] * kLog2e;
+  float H = a.h0 ? a.h0[(size_t)c * NS + s] : 0.0f;
+  const float *ds = a.carry + (size_t)a.B * nc * NS * a.D + (size_t)b * nc * a.D + c;
+  float *hs = a.carry + ((size_t)b * nc * NS + s) * a.D + c;
+  const size_t hstride = (size_t)NS * a.D;
+  for (int c0 = 0; c0 + 1 < nc; c0 += U) {
+    float Sv[U], hv[U];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    A2[s] = a.A[(size_t)c * NS + s] * kLog2e;
-    H[s] = a.h0 ? a.h0[(size_t)c * NS + s] : 0.0f;
-  }
-  const float *ds = a.carry + (size_t)a.B * nc * NS * a.D;
-  for (int ck = 0; ck + 1 < nc; ++ck) {
-    float *hs = a.carry + ((size_t)b * nc + ck) * NS * a.D;
-    const float S = ds[((size_t)b * nc + ck) * a.D + c];
+    for (int u = 0; u < U; ++u) {
+      const int ck = c0 + u;
+      const bool in = ck + 1 < nc;
+      Sv[u] = in ? ds[(size_t)ck * a.D] : 0.0f;
+      hv[u] = in ? hs[ck * hstride] : 0.0f;
+    }
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      H[s] = fmaf(exp2_fast(A2[s] * S), H[s], hs[(size_t)s * a.D + c]);
-      hs[(size_t)s * a.D + c] = H[s];   // state entering chunk ck+1
+    for (int u = 0; u < U; ++u) {
+      const int ck = c0 + u;
+      if (ck + 1 >= nc) break;
+      H = fmaf(exp2_fast(A2 * Sv[u]), H, hv[u]);
+      hs[ck * hstride] = H;               // state entering chunk ck+1
     }
   }
 }
@@ -215,7 +225,7 @@ hipError_t launch_scan(const ScanArgs &a, hipStream_t s) {
   const int cw = (a.D + 63) / 64;
   if (nc > 1) {
     hipLaunchKernelGGL(scan_pass1<T>, dim3(nc - 1, cw, a.B), dim3(64), 0, s, a);
-    hipLaunchKernelGGL(scan_pass2, dim3(cw, a.B), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(scan_pass2, dim3((NS * a.D + 255) / 256, a.B), dim3(256), 0, s, a);
   }
   hipLaunchKernelGGL(scan_pass3<T>, dim3(nc, cw, a.B), dim3(64), 0, s, a);
   return hipGetLastError();
