@@ -65,27 +65,28 @@ gemm_bf16_mfma(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, in
   const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
   const int lr = lane & 31, lh = lane >> 5;
 
+  // Global -> register staging with buffer loads.  Each operand gets a buffer
+  // descriptor based at the tile's first row whose size ends at the last
+  // valid row, so rows past M (or N) read as zero in hardware; the k offset is
+  // a uniform (SGPR) offset.  K is a multiple of BK on this path (checked on
+  // the host).
   uint4 ra[Cfg::A_PER_T], rb[Cfg::B_PER_T];
+  static_assert(Cfg::A_CHUNKS % Cfg::NT == 0 && Cfg::B_CHUNKS % Cfg::NT == 0, "tile/threads");
+  constexpr int ROWS_PER_PASS = Cfg::NT / 8;
+  const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(A + (size_t)m0 * K), (short)0, (M - m0) * K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(B + (size_t)n0 * K), (short)0, (N - n0) * K * 2, 0x00020000);
+  const int voff = ((tid >> 3) * K + (tid & 7) * 8) * 2;
+  const int vstep = ROWS_PER_PASS * K * 2;
   auto gload = [&](int kt) {
-    const int k0 = kt * Cfg::BK;
+    const int koff = kt * Cfg::BK * 2;
 #pragma unroll
-    for (int i = 0; i < Cfg::A_PER_T; ++i) {
-      const int c = tid + i * Cfg::NT;
-      const int r = c >> 3, gk = k0 + (c & 7) * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (c < Cfg::A_CHUNKS && m0 + r < M && gk < K)
-        v = *reinterpret_cast<const uint4 *>(A + (size_t)(m0 + r) * K + gk);
-      ra[i] = v;
-    }
+    for (int i = 0; i < Cfg::A_PER_T; ++i)
+      ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsA, voff + i * vstep, koff, 0));
 #pragma unroll
-    for (int i = 0; i < Cfg::B_PER_T; ++i) {
-      const int c = tid + i * Cfg::NT;
-      const int r = c >> 3, gk = k0 + (c & 7) * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (c < Cfg::B_CHUNKS && n0 + r < N && gk < K)
-        v = *reinterpret_cast<const uint4 *>(B + (size_t)(n0 + r) * K + gk);
-      rb[i] = v;
-    }
+    for (int i = 0; i < Cfg::B_PER_T; ++i)
+      rb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsB, voff + i * vstep, koff, 0));
   };
   auto sstore = [&](int buf) {
     uint4 *sA = smem + buf * Cfg::STAGE;
@@ -93,12 +94,12 @@ gemm_bf16_mfma(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, in
 #pragma unroll
     for (int i = 0; i < Cfg::A_PER_T; ++i) {
       const int c = tid + i * Cfg::NT;
-      if (c < Cfg::A_CHUNKS) sA[swz(c >> 3, c & 7)] = ra[i];
+      sA[swz(c >> 3, c & 7)] = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < Cfg::B_PER_T; ++i) {
       const int c = tid + i * Cfg::NT;
-      if (c < Cfg::B_CHUNKS) sB[swz(c >> 3, c & 7)] = rb[i];
+      sB[swz(c >> 3, c & 7)] = rb[i];
     }
   };
 
@@ -110,35 +111,46 @@ gemm_bf16_mfma(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, in
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int ktiles = (K + Cfg::BK - 1) / Cfg::BK;
+  // MFMA operand fragments, double-buffered across the 16-wide k-steps so the
+  // LDS reads of step ks+1 are in flight while step ks's MFMAs issue.
+  bf16x8 af[2][Cfg::TM], bfr[2][Cfg::TN];
+  auto fload = [&](const uint4 *sA, const uint4 *sB, int ks, int slot) {
+#pragma unroll
+    for (int i = 0; i < Cfg::TM; ++i)
+      af[slot][i] = __builtin_bit_cast(bf16x8, sA[swz(wm * Cfg::WM + i * 32 + lr, ks * 2 + lh)]);
+#pragma unroll
+    for (int j = 0; j < Cfg::TN; ++j)
+      bfr[slot][j] = __builtin_bit_cast(bf16x8, sB[swz(wn * Cfg::WN + j * 32 + lr, ks * 2 + lh)]);
+  };
+
+  // One basic block per k-tile (no branches), so the scheduling barriers fix
+  // the order: next tile's global loads, then for each 16-wide k-step the
+  // operand reads of the following step and the MFMAs of this one, then the
+  // staged tile goes to the idle LDS buffer.  On the last tile the loads
+  // repeat that tile and land in the idle buffer, which nobody reads again.
+  const int ktiles = K / Cfg::BK;
   gload(0);
   sstore(0);
   __syncthreads();
   for (int kt = 0; kt < ktiles; ++kt) {
-    const bool more = kt + 1 < ktiles;
-    if (more) gload(kt + 1);
+    gload(min(kt + 1, ktiles - 1));
     const uint4 *sA = smem + (kt & 1) * Cfg::STAGE;
     const uint4 *sB = sA + Cfg::A_CHUNKS;
+    fload(sA, sB, 0, 0);
 #pragma unroll
     for (int ks = 0; ks < Cfg::BK / 16; ++ks) {
-      bf16x8 af[Cfg::TM], bfr[Cfg::TN];
-#pragma unroll
-      for (int i = 0; i < Cfg::TM; ++i) {
-        const uint4 v = sA[swz(wm * Cfg::WM + i * 32 + lr, ks * 2 + lh)];
-        af[i] = __builtin_bit_cast(bf16x8, v);
-      }
-#pragma unroll
-      for (int j = 0; j < Cfg::TN; ++j) {
-        const uint4 v = sB[swz(wn * Cfg::WN + j * 32 + lr, ks * 2 + lh)];
-        bfr[j] = __builtin_bit_cast(bf16x8, v);
-      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks + 1 < Cfg::BK / 16) fload(sA, sB, ks + 1, (ks + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < Cfg::TM; ++i)
 #pragma unroll
         for (int j = 0; j < Cfg::TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j],
+                                                              acc[i][j], 0, 0, 0);
     }
-    if (more) sstore((kt + 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    sstore((kt + 1) & 1);
     __syncthreads();
   }
 
@@ -151,6 +163,11 @@ gemm_bf16_mfma(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, in
   constexpr int LPR = Cfg::WN / 8;              // lanes per strip row
   constexpr int RPI = 64 / LPR;                 // strip rows per pass
   float *strip = reinterpret_cast<float *>(smem) + wave * 32 * SROW;
+  // a lane stores the same 8 columns for every row: resolve them once
+  const int cc = (lane % LPR) * 8;
+  const int gcol = n0 + wn * Cfg::WN + cc;
+  const bool col_ok = gcol < N;
+  const typename Epi::Col ci = epi.col_info(col_ok ? gcol : 0);
 #pragma unroll
   for (int i = 0; i < Cfg::TM; ++i) {
 #pragma unroll
@@ -162,16 +179,179 @@ gemm_bf16_mfma(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, in
 #pragma unroll 1
     for (int it = 0; it < 32 / RPI; ++it) {
       const int rr = it * RPI + lane / LPR;
-      const int cc = (lane % LPR) * 8;
       const float4 a = *reinterpret_cast<const float4 *>(strip + rr * SROW + cc);
       const float4 b = *reinterpret_cast<const float4 *>(strip + rr * SROW + cc + 4);
       const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
       const int row = m0 + wm * Cfg::WM + i * 32 + rr;
-      const int col = n0 + wn * Cfg::WN + cc;
-      if (row < M && col < N) epi.store8(row, col, v);
+      if (row < M && col_ok) epi.store8(row, ci, v);
     }
     __syncthreads();
   }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA kernel, operands streamed straight into LDS
+//
+// buffer_load_dwordx4 ... lds writes lane l's 16 bytes at the instruction's
+// LDS base + 16*l, so each lane fetches the global chunk that belongs at its
+// (swizzled) LDS slot.  k-tiles are 32 wide and STAGES deep: the loads of
+// tile kt+STAGES-1 are issued while tile kt is multiplied, giving the global
+// reads STAGES-1 tiles of MFMA time to land.  Waits and barriers are explicit
+// (s_waitcnt vmcnt + s_barrier) so nothing drains the load pipeline.
+// ---------------------------------------------------------------------------
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_>
+struct LdsCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
+  static constexpr int BK = 32;                      // bf16 per k-tile row (64 B)
+  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+  static constexpr int NWAVES = WAVES_M * WAVES_N;
+  static constexpr int NT = NWAVES * 64;
+  static constexpr int TM = WM / 32, TN = WN / 32;
+  static constexpr int A_UNITS = BM * 4, B_UNITS = BN * 4;   // 16-byte units
+  static constexpr int STAGE = A_UNITS + B_UNITS;
+  static constexpr int A_INS = A_UNITS / 64 / NWAVES;        // load instrs per wave
+  static constexpr int B_INS = B_UNITS / 64 / NWAVES;
+  static_assert(A_INS * 64 * NWAVES == A_UNITS && B_INS * 64 * NWAVES == B_UNITS, "tile");
+};
+
+// slot of 16-byte chunk c (0..3) of 64-byte row `row`: 16 rows read with the
+// same c land on 16 distinct 16-byte bank groups
+__device__ __forceinline__ int swz4(int row, int c) { return row * 4 + (c ^ ((row >> 2) & 3)); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  // gfx9 s_waitcnt immediate: vmcnt[3:0] at bits 3:0, vmcnt[5:4] at 15:14;
+  // expcnt (6:4) and lgkmcnt (11:8) left at their maxima (no wait)
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <class Cfg, class Epi>
+__global__ void __launch_bounds__(Cfg::NT)
+gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int N, int K, Epi epi) {
+  // the body uses LDS-DMA builtins that exist only for the device target; the
+  // host pass needs just the launch stub
+#if defined(__HIP_DEVICE_COMPILE__)
+  __shared__ uint4 smem[Cfg::STAGES * Cfg::STAGE];
+  int tm, tn;
+  if (!tile_of((M + Cfg::BM - 1) / Cfg::BM, (N + Cfg::BN - 1) / Cfg::BN, tm, tn)) return;
+  const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
+  const int lr = lane & 31, lh = lane >> 5;
+
+  // buffers based at the tile's first row; rows past M (N) read as zero
+  const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(A + (size_t)m0 * K), (short)0, (M - m0) * K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(B + (size_t)n0 * K), (short)0, (N - n0) * K * 2, 0x00020000);
+  int voffA[Cfg::A_INS], voffB[Cfg::B_INS];
+#pragma unroll
+  for (int j = 0; j < Cfg::A_INS; ++j) {
+    const int u = (wave * Cfg::A_INS + j) * 64 + lane;
+    const int row = u >> 2, kc = (u & 3) ^ ((row >> 2) & 3);
+    voffA[j] = (row * K + kc * 8) * 2;
+  }
+#pragma unroll
+  for (int j = 0; j < Cfg::B_INS; ++j) {
+    const int u = (wave * Cfg::B_INS + j) * 64 + lane;
+    const int row = u >> 2, kc = (u & 3) ^ ((row >> 2) & 3);
+    voffB[j] = (row * K + kc * 8) * 2;
+  }
+  typedef __attribute__((address_space(3))) void lds_void;
+  auto issue = [&](int kt, int st) {
+    const int soff = kt * Cfg::BK * 2;
+    uint4 *base = smem + st * Cfg::STAGE;
+#pragma unroll
+    for (int j = 0; j < Cfg::A_INS; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsA, (lds_void *)(base + (wave * Cfg::A_INS + j) * 64), 16, voffA[j], soff, 0, 0);
+#pragma unroll
+    for (int j = 0; j < Cfg::B_INS; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsB, (lds_void *)(base + Cfg::A_UNITS + (wave * Cfg::B_INS + j) * 64), 16, voffB[j],
+          soff, 0, 0);
+  };
+
+  f32x16 acc[Cfg::TM][Cfg::TN];
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  bf16x8 af[2][Cfg::TM], bfr[2][Cfg::TN];
+  auto fload = [&](const uint4 *sA, const uint4 *sB, int ks, int slot) {
+#pragma unroll
+    for (int i = 0; i < Cfg::TM; ++i)
+      af[slot][i] = __builtin_bit_cast(bf16x8, sA[swz4(wm * Cfg::WM + i * 32 + lr, ks * 2 + lh)]);
+#pragma unroll
+    for (int j = 0; j < Cfg::TN; ++j)
+      bfr[slot][j] = __builtin_bit_cast(bf16x8, sB[swz4(wn * Cfg::WN + j * 32 + lr, ks * 2 + lh)]);
+  };
+
+  const int ktiles = K / Cfg::BK;
+  const int klast = ktiles - 1;
+#pragma unroll
+  for (int st = 0; st < Cfg::STAGES - 1; ++st) issue(min(st, klast), st);
+  constexpr int PER_TILE = Cfg::A_INS + Cfg::B_INS;
+  for (int kt = 0; kt < ktiles; ++kt) {
+    wait_vmcnt<(Cfg::STAGES - 2) * PER_TILE>();   // this wave's loads of tile kt have landed
+    __builtin_amdgcn_s_barrier();               // ... and every other wave's
+    __builtin_amdgcn_sched_barrier(0);
+    // refill the stage every wave finished reading before this barrier
+    const int nt = kt + Cfg::STAGES - 1;
+    issue(min(nt, klast), nt % Cfg::STAGES);
+    const uint4 *sA = smem + (kt % Cfg::STAGES) * Cfg::STAGE;
+    const uint4 *sB = sA + Cfg::A_UNITS;
+    fload(sA, sB, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    fload(sA, sB, 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  constexpr int SROW = Cfg::WN + 8;
+  constexpr int LPR = Cfg::WN / 8;
+  constexpr int RPI = 64 / LPR;
+  static_assert(Cfg::NWAVES * 32 * SROW * 4 <= (int)sizeof(smem), "epilogue strip fits");
+  float *strip = reinterpret_cast<float *>(smem) + wave * 32 * SROW;
+  // a lane stores the same 8 columns for every row: resolve them once
+  const int cc = (lane % LPR) * 8;
+  const int gcol = n0 + wn * Cfg::WN + cc;
+  const bool col_ok = gcol < N;
+  const typename Epi::Col ci = epi.col_info(col_ok ? gcol : 0);
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        strip[(8 * (r >> 2) + 4 * lh + (r & 3)) * SROW + j * 32 + lr] = acc[i][j][r];
+    __syncthreads();
+#pragma unroll 1
+    for (int it = 0; it < 32 / RPI; ++it) {
+      const int rr = it * RPI + lane / LPR;
+      const float4 a = *reinterpret_cast<const float4 *>(strip + rr * SROW + cc);
+      const float4 b = *reinterpret_cast<const float4 *>(strip + rr * SROW + cc + 4);
+      const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      const int row = m0 + wm * Cfg::WM + i * 32 + rr;
+      if (row < M && col_ok) epi.store8(row, ci, v);
+    }
+    __syncthreads();
+  }
+#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -231,8 +411,10 @@ struct InProjEpi {
   __device__ __forceinline__ void operator()(int row, int col, float v) const {
     inproj_store<T>(e, row, col, v);
   }
-  __device__ __forceinline__ void store8(int row, int col, const float v[8]) const {
-    inproj_store8<T>(e, row, col, v);
+  typedef ColInfo Col;
+  __device__ __forceinline__ Col col_info(int col) const { return inproj_col(e, col); }
+  __device__ __forceinline__ void store8(int row, const Col &ci, const float v[8]) const {
+    inproj_store8<T>(e, row, ci, v);
   }
 };
 
@@ -243,7 +425,9 @@ struct StoreEpi {
   __device__ __forceinline__ void operator()(int row, int col, float v) const {
     out[(size_t)row * ld + col] = from_f32<T>(v);
   }
-  __device__ __forceinline__ void store8(int row, int col, const float v[8]) const {
+  typedef int Col;
+  __device__ __forceinline__ Col col_info(int col) const { return col; }
+  __device__ __forceinline__ void store8(int row, const Col &col, const float v[8]) const {
     store8_T(out + (size_t)row * ld + col, v);
   }
 };
@@ -258,13 +442,26 @@ static hipError_t run_bf16(const bf16 *A, int M, int K, const bf16 *B, int N, co
   return hipGetLastError();
 }
 
+template <class Cfg, class Epi>
+static hipError_t run_lds(const bf16 *A, int M, int K, const bf16 *B, int N, const Epi &epi,
+                          hipStream_t s) {
+  const int tiles = ((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
+  const int grid = (tiles + 7) / 8 * 8;
+  hipLaunchKernelGGL((gemm_bf16_lds<Cfg, Epi>), dim3(grid), dim3(Cfg::NT), 0, s, A, B, M, N, K,
+                     epi);
+  return hipGetLastError();
+}
+
 using CfgLarge = GemmCfg<256, 256, 128, 128>;
+// 256x256 tile, 8 waves of 128x64 (two per SIMD, so one wave's LDS waits and
+// barriers hide behind the other's MFMAs), 3 LDS stages (96 KB)
+using CfgLds = LdsCfg<256, 256, 128, 64, 3>;
 using CfgSmall = GemmCfg<128, 64, 64, 32>;
 
 template <class Epi>
 static hipError_t run_bf16_auto(const bf16 *A, int M, int K, const bf16 *B, int N, const Epi &epi,
                                 hipStream_t s) {
-  if (M >= 1024) return run_bf16<CfgLarge>(A, M, K, B, N, epi, s);
+  if (M >= 1024) return run_lds<CfgLds>(A, M, K, B, N, epi, s);
   return run_bf16<CfgSmall>(A, M, K, B, N, epi, s);
 }
 

@@ -96,6 +96,9 @@ hh_status check_dims(const hh_dims *dm, int kv_producer, Shape &s) {
     return fail(HH_ERR_UNSUPPORTED, "d_conv %d (2..4 supported)", dm->d_conv);
   if (dm->d_model % 8 || dm->d_inner % 8 || (dm->n_heads * dm->head_dim) % 8)
     return fail(HH_ERR_UNSUPPORTED, "d_model, d_inner and n_heads*head_dim must be multiples of 8");
+  if (dm->dtype == HH_BF16 && (dm->d_model % 64 || (dm->n_heads * dm->head_dim + dm->d_inner) % 64))
+    return fail(HH_ERR_UNSUPPORTED, "bf16 path needs d_model and n_heads*head_dim + d_inner "
+                                    "to be multiples of 64");
   if (!(dm->rms_eps >= 0.0f) || dm->rms_eps > 1.0f)
     return fail(HH_ERR_INVALID_ARG, "rms_eps must be in [0, 1]");
   s.d = dm->d_model; s.H = dm->n_heads; s.G = dm->n_kv_heads; s.hd = dm->head_dim;

@@ -129,52 +129,88 @@ __device__ __forceinline__ void store8_T(T *dst, const float v[8]) {
   }
 }
 
-template <class T>
-__device__ __forceinline__ void inproj_store8(const InProjOut &e, int row, int col, const float v[8]) {
+// Column-side part of an 8-column group (col % 8 == 0), resolved once per
+// lane: which block of the map the columns fall in, the offset inside it and,
+// for the Delta block, the biases.
+struct ColInfo {
+  int seg;       // 0 Q, 1 K, 2 V, 3 xs, 4 z, 5 dt, 6 B|C
+  int c;         // column offset inside the block
+  int g, d;      // K/V: head and position inside the head
+  float bias[8];
+};
+
+__device__ __forceinline__ ColInfo inproj_col(const InProjOut &e, int col) {
+  ColInfo ci{};
   const int Wa = e.Wa, KV = e.KV, D = e.D;
-  if (col < Wa) { store8_T(reinterpret_cast<T *>(e.q) + (size_t)row * Wa + col, v); return; }
+  if (col < Wa) { ci.seg = 0; ci.c = col; return ci; }
   col -= Wa;
   if (col < 2 * KV) {
-    const bool isv = col >= KV;
-    const int c = isv ? col - KV : col;
-    const int g = c / e.hd, d = c - g * e.hd;
-    const int G = KV / e.hd;
-    if (e.mode == EPI_DECODE) {
-      const int p = e.len[row];
-      if (p < 0 || (!e.is_ring && p >= e.cap)) return;
-      const int slot = e.is_ring ? p % e.cap : p;
-      T *dst = reinterpret_cast<T *>(isv ? e.cache_v : e.cache_k);
-      store8_T(dst + (((size_t)row * G + g) * e.cap + slot) * e.hd + d, v);
-      return;
-    }
-    const int n = e.n_rows_per_seq;
-    const int b = row / n, p = row - b * n;
-    T *full = reinterpret_cast<T *>(isv ? e.v_full : e.k_full);
-    store8_T(full + (((size_t)b * G + g) * n + p) * e.hd + d, v);
-    if (e.mode == EPI_PREFILL && e.cache_k) {
-      const bool keep = e.is_ring ? (p >= n - e.cap) : (p < e.cap);
-      if (keep) {
-        const int slot = e.is_ring ? p % e.cap : p;
-        T *dst = reinterpret_cast<T *>(isv ? e.cache_v : e.cache_k);
-        store8_T(dst + (((size_t)b * G + g) * e.cap + slot) * e.hd + d, v);
-      }
-    }
-    return;
+    ci.seg = col < KV ? 1 : 2;
+    ci.c = col < KV ? col : col - KV;
+    ci.g = ci.c / e.hd;
+    ci.d = ci.c - ci.g * e.hd;
+    return ci;
   }
   col -= 2 * KV;
-  if (col < D) { store8_T(e.xs + (size_t)row * D + col, v); return; }
+  if (col < D) { ci.seg = 3; ci.c = col; return ci; }
   col -= D;
-  if (col < D) { store8_T(reinterpret_cast<T *>(e.z) + (size_t)row * D + col, v); return; }
+  if (col < D) { ci.seg = 4; ci.c = col; return ci; }
   col -= D;
   if (col < D) {
-    float sp[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) sp[i] = softplus_f(v[i] + e.dt_bias[col + i]);
-    store8_T(e.dt + (size_t)row * D + col, sp);
-    return;
+    ci.seg = 5; ci.c = col;
+    const float4 b0 = *reinterpret_cast<const float4 *>(e.dt_bias + col);
+    const float4 b1 = *reinterpret_cast<const float4 *>(e.dt_bias + col + 4);
+    ci.bias[0] = b0.x; ci.bias[1] = b0.y; ci.bias[2] = b0.z; ci.bias[3] = b0.w;
+    ci.bias[4] = b1.x; ci.bias[5] = b1.y; ci.bias[6] = b1.z; ci.bias[7] = b1.w;
+    return ci;
   }
-  col -= D;
-  store8_T(e.bc + (size_t)row * 2 * e.N + col, v);
+  ci.seg = 6; ci.c = col - D;
+  return ci;
+}
+
+template <class T>
+__device__ __forceinline__ void inproj_store8(const InProjOut &e, int row, const ColInfo &ci,
+                                              const float v[8]) {
+  const int Wa = e.Wa, D = e.D;
+  switch (ci.seg) {
+    case 0: store8_T(reinterpret_cast<T *>(e.q) + (size_t)row * Wa + ci.c, v); return;
+    case 1:
+    case 2: {
+      const bool isv = ci.seg == 2;
+      const int G = e.KV / e.hd;
+      if (e.mode == EPI_DECODE) {
+        const int p = e.len[row];
+        if (p < 0 || (!e.is_ring && p >= e.cap)) return;
+        const int slot = e.is_ring ? p % e.cap : p;
+        T *dst = reinterpret_cast<T *>(isv ? e.cache_v : e.cache_k);
+        store8_T(dst + (((size_t)row * G + ci.g) * e.cap + slot) * e.hd + ci.d, v);
+        return;
+      }
+      const int n = e.n_rows_per_seq;
+      const int b = row / n, p = row - b * n;
+      T *full = reinterpret_cast<T *>(isv ? e.v_full : e.k_full);
+      store8_T(full + (((size_t)b * G + ci.g) * n + p) * e.hd + ci.d, v);
+      if (e.mode == EPI_PREFILL && e.cache_k) {
+        const bool keep = e.is_ring ? (p >= n - e.cap) : (p < e.cap);
+        if (keep) {
+          const int slot = e.is_ring ? p % e.cap : p;
+          T *dst = reinterpret_cast<T *>(isv ? e.cache_v : e.cache_k);
+          store8_T(dst + (((size_t)b * G + ci.g) * e.cap + slot) * e.hd + ci.d, v);
+        }
+      }
+      return;
+    }
+    case 3: store8_T(e.xs + (size_t)row * D + ci.c, v); return;
+    case 4: store8_T(reinterpret_cast<T *>(e.z) + (size_t)row * D + ci.c, v); return;
+    case 5: {
+      float sp[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sp[i] = softplus_f(v[i] + ci.bias[i]);
+      store8_T(e.dt + (size_t)row * D + ci.c, sp);
+      return;
+    }
+    default: store8_T(e.bc + (size_t)row * 2 * e.N + ci.c, v); return;
+  }
 }
 
 // ---- launchers (each returns hipGetLastError() of its launches) ------------

@@ -43,7 +43,8 @@
  *
  * Supported shapes: head_dim 32 or 64 (bf16: 64); n_heads a multiple of
  * n_kv_heads with at most 8 query heads per KV head; d_state 16; d_conv 2..4;
- * d_model, n_heads*head_dim + d_inner and d_inner multiples of 8.
+ * d_model, n_heads*head_dim + d_inner and d_inner multiples of 8 (bf16: d_model
+ * and n_heads*head_dim + d_inner multiples of 64).
  */
 #ifndef HH_H
 #define HH_H
