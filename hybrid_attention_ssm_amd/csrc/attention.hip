@@ -12,8 +12,8 @@
 // staged in LDS serves every head of the group.  Scores are computed
 // transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16), which leaves one query
 // per lane column: the online-softmax statistics are per-lane scalars and the
-// probabilities are already in the B-operand layout of O^T = V^T P^T.  V is
-// transposed into LDS as it is staged.  Only the key tiles that intersect the
+// probabilities are already in the B-operand layout of O^T = V^T P^T.  V^T
+// fragments come from transposing LDS reads.  Only the key tiles that intersect the
 // window band (plus the meta tiles) are visited; masking is applied only on
 // tiles that cross a boundary.
 //
@@ -39,31 +39,40 @@ __device__ __forceinline__ float wave_sum32(float v) { return v + __shfl_xor(v, 
 
 }  // namespace
 
-template <int NW>
-__global__ void __launch_bounds__(NW * 64)
-attn_prefill_bf16(AttnArgs a) {
-  constexpr int NT = NW * 64;
-  constexpr int K_PER_T = (TILE_CHUNKS + NT - 1) / NT;
-  constexpr int V_PER_T = (256 + NT - 1) / NT;
-  __shared__ uint4 sK[2][TILE_CHUNKS];
-  __shared__ uint4 sVt[2][TILE_CHUNKS];
+// K and V tiles are streamed into LDS as they lie in memory (64 keys x 128 B,
+// 16-byte chunks XOR-swizzled per row) by buffer_load ... lds, STAGES tiles
+// deep.  The V^T operand of O^T = V^T P^T is read with ds_read_b64_tr_b16:
+// inside each 16-lane group, lane j receives element j%4 of the 8-byte loads
+// addressed by lanes 4k + j/4 (k = 0..3), so lane l addressing key row
+// 16ks + 4(l/32) + (l%16)/4 (+8) and columns 32dblk + 16((l/16)%2) + 4(l%4)
+// hands every lane the 4 consecutive keys of its own d = 32dblk + l%32.
+constexpr int ASTAGES = 3;
+constexpr int TILE_UNITS = BKV * HD / 8;     // 512 16-byte units per K (or V) tile
 
-  const int hpg = NW;
+template <int NW>
+__global__ void __launch_bounds__(NW * 64, 2)
+attn_prefill_bf16(AttnArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __shared__ uint4 sK[ASTAGES][TILE_UNITS];
+  __shared__ uint4 sV[ASTAGES][TILE_UNITS];
+
   const int nqt = (a.n + BQ - 1) / BQ;
   const int qt = nqt - 1 - (int)blockIdx.x;  // heaviest (latest) query tiles first
   const int g = blockIdx.y, b = blockIdx.z;
   const int q0 = qt * BQ;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int lr = lane & 31, lh = lane >> 5;
-  const int h = g * hpg + wave;
-  const int qpos = q0 + lr;                 // this lane's query (column)
+  const int h = g * NW + wave;
+  const int qpos = q0 + lr;
   const bf16 *Q = reinterpret_cast<const bf16 *>(a.q);
   const bf16 *Kr = reinterpret_cast<const bf16 *>(a.k) + (size_t)(b * a.G + g) * a.n * HD;
   const bf16 *Vr = reinterpret_cast<const bf16 *>(a.v) + (size_t)(b * a.G + g) * a.n * HD;
   const bf16 *Km = reinterpret_cast<const bf16 *>(a.mk) + (size_t)g * a.m * HD;
   const bf16 *Vm = reinterpret_cast<const bf16 *>(a.mv) + (size_t)g * a.m * HD;
   const int Wa = a.H * HD;
+
 
   // Q^T fragments (B operand of S^T = K Q^T): lane holds query lr, dims 16kk+8lh..+7
   bf16x8 qf[4];
@@ -75,71 +84,64 @@ attn_prefill_bf16(AttnArgs a) {
     qf[kk] = __builtin_bit_cast(bf16x8, v);
   }
 
-  // tile schedule: meta tiles, then the real tiles meeting [q0-W+1, q0+BQ-1]
   const int n_meta_t = (a.m + BKV - 1) / BKV;
   const int qlast = min(q0 + BQ - 1, a.n - 1);
   const int lo_pos = a.is_global ? 0 : max(0, q0 - a.window + 1);
   const int t_lo = lo_pos / BKV, t_hi = qlast / BKV;
   const int n_tiles = n_meta_t + (t_hi - t_lo + 1);
 
-  // staging registers
-  uint4 rk[K_PER_T];
-  uint4 rv[V_PER_T][2];
-  auto tile_info = [&](int t, const bf16 *&Kp, const bf16 *&Vp, int &kbase, int &klim, bool &meta) {
-    if (t < n_meta_t) { meta = true; kbase = t * BKV; klim = a.m; Kp = Km; Vp = Vm; }
-    else { meta = false; kbase = (t_lo + t - n_meta_t) * BKV; klim = a.n; Kp = Kr; Vp = Vr; }
+  // DMA: per stage 8 wave-instructions of 64 x 16 bytes fill the K tile and 8
+  // the V tile; each of the min(NW, 4) loader waves issues KI of each (when
+  // 8 is not a multiple of the loader count, the extra instructions repeat
+  // earlier ones: same bytes to the same slots).  Unit u of a tile is row
+  // u/8, slot u%8, holding global chunk slot^((row/2)%8).
+  constexpr int LOADERS = NW < 4 ? NW : 4;
+  constexpr int KI = (8 + LOADERS - 1) / LOADERS;
+  constexpr int INS = 2 * KI;
+  typedef __attribute__((address_space(3))) void lds_void;
+  const bool loader = wave < LOADERS;
+  int voff[KI], part[KI];
+#pragma unroll
+  for (int j = 0; j < KI; ++j) {
+    part[j] = (wave * KI + j) & 7;
+    const int u = part[j] * 64 + lane;
+    const int row = u >> 3, c = (u & 7) ^ ((row >> 1) & 7);
+    voff[j] = row * HD * 2 + c * 16;
+  }
+  auto issue = [&](int t, int st) {
+    if (!loader) return;
+    const bool meta = t < n_meta_t;
+    const int kbase = meta ? t * BKV : (t_lo + t - n_meta_t) * BKV;
+    const int bytes = (meta ? a.m : a.n) * HD * 2;
+    // buffers end at the last valid key row: rows past it read as zero
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(meta ? Km : Kr), (short)0, bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(meta ? Vm : Vr), (short)0, bytes, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < KI; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(sK[st] + part[j] * 64), 16, voff[j],
+                                               kbase * HD * 2, 0, 0);
+#pragma unroll
+    for (int j = 0; j < KI; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(sV[st] + part[j] * 64), 16, voff[j],
+                                               kbase * HD * 2, 0, 0);
   };
-  auto gload = [&](int t) {
-    const bf16 *Kp, *Vp; int kbase, klim; bool meta;
-    tile_info(t, Kp, Vp, kbase, klim, meta);
+  // ds_read_b64_tr_b16 source offsets (bytes) inside a V tile for
+  // (dblk, ks, call) = index dblk*8 + ks*2 + call
+  const int tr_row0 = 4 * lh + ((lane & 15) >> 2);
+  const int tr_col0 = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int tr_off[16];
 #pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) {
-      const int c = tid + i * NT;
-      const int r = c >> 3, dc = c & 7;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (c < TILE_CHUNKS && kbase + r < klim)
-        v = *reinterpret_cast<const uint4 *>(Kp + (size_t)(kbase + r) * HD + dc * 8);
-      rk[i] = v;
-    }
-    // V: item = (key pair kp, d-chunk dc); 256 items
+  for (int dblk = 0; dblk < 2; ++dblk)
 #pragma unroll
-    for (int i = 0; i < V_PER_T; ++i) {
-      const int it = tid + i * NT;
-      const int kp = it >> 3, dc = it & 7;
-      uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
-      if (it < 256) {
-        const int k0 = kbase + 2 * kp;
-        if (k0 < klim) v0 = *reinterpret_cast<const uint4 *>(Vp + (size_t)k0 * HD + dc * 8);
-        if (k0 + 1 < klim) v1 = *reinterpret_cast<const uint4 *>(Vp + (size_t)(k0 + 1) * HD + dc * 8);
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int call = 0; call < 2; ++call) {
+        const int row = 16 * ks + 8 * call + tr_row0;
+        const int col = 32 * dblk + tr_col0;
+        tr_off[dblk * 8 + ks * 2 + call] = row * 128 + (((col >> 3) ^ ((row >> 1) & 7)) << 4) + (col & 7) * 2;
       }
-      rv[i][0] = v0;
-      rv[i][1] = v1;
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) {
-      const int c = tid + i * NT;
-      if (c < TILE_CHUNKS) sK[buf][swz(c >> 3, c & 7)] = rk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < V_PER_T; ++i) {
-      const int it = tid + i * NT;
-      if (it < 256) {
-        const int kp = it >> 3, dc = it & 7;
-        const unsigned short *e0 = reinterpret_cast<const unsigned short *>(&rv[i][0]);
-        const unsigned short *e1 = reinterpret_cast<const unsigned short *>(&rv[i][1]);
-        // Vt row d = 8dc+j holds keys; pair (2kp, 2kp+1) is 4 bytes in chunk kp/4
-        char *base = reinterpret_cast<char *>(sVt[buf]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int d = dc * 8 + j;
-          const unsigned int pair = (unsigned int)e0[j] | ((unsigned int)e1[j] << 16);
-          *reinterpret_cast<unsigned int *>(base + swz(d, kp >> 2) * 16 + (kp & 3) * 4) = pair;
-        }
-      }
-    }
-  };
 
   const float sl2 = kLog2e * rsqrtf((float)HD);
   float m_run = -INFINITY, l_run = 0.0f;
@@ -147,15 +149,22 @@ attn_prefill_bf16(AttnArgs a) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) { o[0][r] = 0.0f; o[1][r] = 0.0f; }
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  const int tlast = n_tiles - 1;
+#pragma unroll
+  for (int st = 0; st < ASTAGES - 1; ++st) issue(min(st, tlast), st);
   for (int t = 0; t < n_tiles; ++t) {
-    const bool more = t + 1 < n_tiles;
-    if (more) gload(t + 1);
-    const int buf = t & 1;
-    const bf16 *Kp, *Vp; int kbase, klim; bool meta;
-    tile_info(t, Kp, Vp, kbase, klim, meta);
+    // this wave's DMA for tile t has landed (later tiles may still be in flight) ...
+    __builtin_amdgcn_s_waitcnt((((ASTAGES - 2) * INS) & 15) | ((((ASTAGES - 2) * INS) >> 4) << 14) |
+                               (7 << 4) | (15 << 8));
+    __builtin_amdgcn_s_barrier();   // ... and every wave's; stage (t-1) is free
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      const int nt = t + ASTAGES - 1;
+      issue(min(nt, tlast), nt % ASTAGES);
+    }
+    const int st = t % ASTAGES;
+    const bool meta = t < n_meta_t;
+    const int kbase = meta ? t * BKV : (t_lo + t - n_meta_t) * BKV;
 
     f32x16 s[2];
 #pragma unroll
@@ -164,11 +173,10 @@ attn_prefill_bf16(AttnArgs a) {
       for (int r = 0; r < 16; ++r) s[blk][r] = 0.0f;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, sK[buf][swz(blk * 32 + lr, kk * 2 + lh)]);
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, sK[st][swz(blk * 32 + lr, kk * 2 + lh)]);
         s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[blk], 0, 0, 0);
       }
     }
-    // does this tile cross a boundary for this wave's queries?
     bool need_mask;
     if (meta) need_mask = kbase + BKV > a.m;
     else need_mask = (kbase + BKV - 1 > q0) || (kbase + BKV > a.n) ||
@@ -207,24 +215,25 @@ attn_prefill_bf16(AttnArgs a) {
     m_run = m_new;
 #pragma unroll
     for (int r = 0; r < 16; ++r) { o[0][r] *= alpha; o[1][r] *= alpha; }
-    // O^T += V^T P^T over the 64 keys, 16 per MFMA
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    const char *vbase = reinterpret_cast<const char *>(sV[st]);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       bf16x8 pb;
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[e] = (bf16)s[ks >> 1][8 * (ks & 1) + e];
-      const char *vb = reinterpret_cast<const char *>(sVt[buf]);
 #pragma unroll
       for (int dblk = 0; dblk < 2; ++dblk) {
-        const int d = dblk * 32 + lr;
-        const uint2 lo = *reinterpret_cast<const uint2 *>(vb + swz(d, 2 * ks) * 16 + lh * 8);
-        const uint2 hi = *reinterpret_cast<const uint2 *>(vb + swz(d, 2 * ks + 1) * 16 + lh * 8);
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16 *)(vbase + tr_off[dblk * 8 + ks * 2]));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16 *)(vbase + tr_off[dblk * 8 + ks * 2 + 1]));
+        typedef short v8i16 __attribute__((ext_vector_type(8)));
+        const v8i16 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, both);
         o[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[dblk], 0, 0, 0);
       }
     }
-    if (more) sstore((t + 1) & 1);
-    __syncthreads();
   }
 
   if (qpos < a.n) {
@@ -240,6 +249,7 @@ attn_prefill_bf16(AttnArgs a) {
         *reinterpret_cast<bf16x4 *>(O + dblk * 32 + 8 * j + 4 * lh) = w;
       }
   }
+#endif
 }
 
 // fp32: one wave per (query, head, sequence); lanes over head_dim (<= 64)

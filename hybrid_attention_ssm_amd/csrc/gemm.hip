@@ -61,7 +61,8 @@ gemm_bf16_mfma(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, in
   int tm, tn;
   if (!tile_of((M + Cfg::BM - 1) / Cfg::BM, (N + Cfg::BN - 1) / Cfg::BN, tm, tn)) return;
   const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
   const int lr = lane & 31, lh = lane >> 5;
 
@@ -236,7 +237,8 @@ gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int
   int tm, tn;
   if (!tile_of((M + Cfg::BM - 1) / Cfg::BM, (N + Cfg::BN - 1) / Cfg::BN, tm, tn)) return;
   const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
   const int lr = lane & 31, lh = lane >> 5;
 

@@ -124,3 +124,11 @@ def test_deterministic_rerun():
     a = run_prefill(dims, inp["weights"], inp["R"], inp["x"], 64, False)
     b = run_prefill(dims, inp["weights"], inp["R"], inp["x"], 64, False)
     assert torch.equal(a["out"], b["out"]) and torch.equal(a["h"], b["h"])
+
+
+@pytest.mark.parametrize("H,G,d,D", [(2, 2, 128, 128), (4, 2, 128, 256), (3, 1, 192, 320), (8, 1, 256, 512)])
+def test_bf16_heads_per_group(H, G, d, D):
+    """Every supported query-heads-per-KV-head count of the bf16 attention."""
+    dims = LayerDims(d_model=d, n_heads=H, n_kv_heads=G, head_dim=64, d_inner=D, d_state=16,
+                     d_conv=4, n_meta=70, dtype="bf16")
+    _check_prefill(dims, 1, 150, 48, False, seed=H * 10 + G, cache_cap=48)
