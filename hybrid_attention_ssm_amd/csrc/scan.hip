@@ -61,48 +61,94 @@ __device__ __forceinline__ void load_history(const ScanArgs &a, int b, int c, in
   }
 }
 
+// One time step of the channel recurrence.  bc points at B_t then C_t (the
+// same for every channel, so the loads are uniform).
+template <int MODE>
+__device__ __forceinline__ float scan_step(const ChanParams &p, float h[NS], float hist[KC - 1],
+                                           float x, float dt, const float bv[NS],
+                                           const float cv[NS], float &dsum) {
+  const float conv = p.bias + p.w[3] * x + p.w[2] * hist[0] + p.w[1] * hist[1] + p.w[0] * hist[2];
+  hist[2] = hist[1];
+  hist[1] = hist[0];
+  hist[0] = x;
+  const float du = dt * silu_f(conv);
+  float acc = 0.0f;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const float decay = exp2_fast(dt * p.A2[s]);
+    h[s] = fmaf(decay, h[s], du * bv[s]);
+    if (MODE == 1) acc = fmaf(cv[s], h[s], acc);
+  }
+  if (MODE == 0) dsum += dt;
+  return acc;
+}
+
 // The scan over [t0, t1) of sequence b for channel c.  MODE 0: summary
 // (end state and sum of Delta); MODE 1: output (Y, and final state/history).
+// B_t/C_t are the same for every channel: SUB steps of them are staged in LDS
+// (sbc, SUB*2N floats) and read back as broadcasts; per-lane inputs are read
+// TB steps at a time.
+constexpr int SUB = 64;
+
 template <class T, int MODE>
-__device__ __forceinline__ void scan_range(const ScanArgs &a, int b, int c, int t0, int t1,
-                                           const ChanParams &p, float h[NS], float hist[KC - 1],
-                                           float &dsum) {
+__device__ __forceinline__ void scan_range(const ScanArgs &a, int b, int c, bool active, int t0,
+                                           int t1, const ChanParams &p, float h[NS],
+                                           float hist[KC - 1], float &dsum, float *sbc) {
   const float *xs = a.xs;
   const T *z = reinterpret_cast<const T *>(a.z);
   T *y = reinterpret_cast<T *>(a.y);
   const size_t D = a.D;
-  for (int tb = t0; tb < t1; tb += TB) {
-    float xv[TB], dv[TB], zv[TB];
+  const size_t row0 = (size_t)b * a.n;
+  const int lane = threadIdx.x;
+  for (int s0 = t0; s0 < t1; s0 += SUB) {
+    const int len = min(SUB, t1 - s0);
+    __syncthreads();   // previous block's reads are done
+    const float4 *src = reinterpret_cast<const float4 *>(a.bc + (row0 + s0) * (2 * NS));
+    for (int i = lane; i < len * (2 * NS / 4); i += 64)
+      reinterpret_cast<float4 *>(sbc)[i] = src[i];
+    __syncthreads();
+    int t = 0;
+    for (; t + TB <= len; t += TB) {
+      float xv[TB], dv[TB], zv[TB];
 #pragma unroll
-    for (int i = 0; i < TB; ++i) {
-      const int t = tb + i;
-      const size_t idx = ((size_t)b * a.n + t) * D + c;
-      const bool in = t < t1;
-      xv[i] = in ? xs[idx] : 0.0f;
-      dv[i] = in ? a.dt[idx] : 0.0f;
-      if (MODE == 1) zv[i] = (in && z) ? to_f32(z[idx]) : 0.0f;
-    }
-#pragma unroll
-    for (int i = 0; i < TB; ++i) {
-      const int t = tb + i;
-      if (t >= t1) break;
-      const float cv = p.bias + p.w[3] * xv[i] + p.w[2] * hist[0] + p.w[1] * hist[1] + p.w[0] * hist[2];
-      hist[2] = hist[1];
-      hist[1] = hist[0];
-      hist[0] = xv[i];
-      const float u = silu_f(cv);
-      const float dt = dv[i];
-      const float du = dt * u;
-      const float *bc = a.bc + ((size_t)b * a.n + t) * (2 * NS);
-      float acc = 0.0f;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const float decay = exp2_fast(dt * p.A2[s]);
-        h[s] = fmaf(decay, h[s], du * bc[s]);
-        if (MODE == 1) acc = fmaf(bc[NS + s], h[s], acc);
+      for (int i = 0; i < TB; ++i) {
+        const size_t idx = (row0 + s0 + t + i) * D + c;
+        xv[i] = xs[idx];
+        dv[i] = a.dt[idx];
+        if (MODE == 1) zv[i] = y ? to_f32(z[idx]) : 0.0f;
       }
-      if (MODE == 0) dsum += dt;
-      if (MODE == 1 && y) y[((size_t)b * a.n + t) * D + c] = from_f32<T>(acc * silu_f(zv[i]));
+#pragma unroll
+      for (int i = 0; i < TB; ++i) {
+        const float4 *bc4 = reinterpret_cast<const float4 *>(sbc + (t + i) * 2 * NS);
+        float bv[NS], cv[NS];
+#pragma unroll
+        for (int q = 0; q < NS / 4; ++q) {
+          const float4 v = bc4[q];
+          bv[4 * q] = v.x; bv[4 * q + 1] = v.y; bv[4 * q + 2] = v.z; bv[4 * q + 3] = v.w;
+          if (MODE == 1) {
+            const float4 u = bc4[NS / 4 + q];
+            cv[4 * q] = u.x; cv[4 * q + 1] = u.y; cv[4 * q + 2] = u.z; cv[4 * q + 3] = u.w;
+          }
+        }
+        const float acc = scan_step<MODE>(p, h, hist, xv[i], dv[i], bv, cv, dsum);
+        if (MODE == 1 && y && active) y[(row0 + s0 + t + i) * D + c] = from_f32<T>(acc * silu_f(zv[i]));
+      }
+    }
+    for (; t < len; ++t) {
+      const size_t idx = (row0 + s0 + t) * D + c;
+      const float4 *bc4 = reinterpret_cast<const float4 *>(sbc + t * 2 * NS);
+      float bv[NS], cv[NS];
+#pragma unroll
+      for (int q = 0; q < NS / 4; ++q) {
+        const float4 v = bc4[q];
+        bv[4 * q] = v.x; bv[4 * q + 1] = v.y; bv[4 * q + 2] = v.z; bv[4 * q + 3] = v.w;
+        if (MODE == 1) {
+          const float4 u = bc4[NS / 4 + q];
+          cv[4 * q] = u.x; cv[4 * q + 1] = u.y; cv[4 * q + 2] = u.z; cv[4 * q + 3] = u.w;
+        }
+      }
+      const float acc = scan_step<MODE>(p, h, hist, xs[idx], a.dt[idx], bv, cv, dsum);
+      if (MODE == 1 && y && active) y[idx] = from_f32<T>(acc * silu_f(to_f32(z[idx])));
     }
   }
 }
@@ -113,8 +159,10 @@ __device__ __forceinline__ void scan_range(const ScanArgs &a, int b, int c, int 
 template <class T>
 __global__ void __launch_bounds__(64) scan_pass1(ScanArgs a) {
   const int ck = blockIdx.x, b = blockIdx.z;
-  const int c = blockIdx.y * 64 + threadIdx.x;
-  if (c >= a.D) return;
+  // lanes past the last channel compute a copy of it (every lane takes part
+  // in staging B/C) and store nothing
+  const bool active = blockIdx.y * 64 + (int)threadIdx.x < a.D;
+  const int c = min(blockIdx.y * 64 + (int)threadIdx.x, a.D - 1);
   const int nc = (a.n + a.chunk - 1) / a.chunk;
   ChanParams p;
   load_params(a, c, p);
@@ -125,8 +173,10 @@ __global__ void __launch_bounds__(64) scan_pass1(ScanArgs a) {
 #pragma unroll
   for (int s = 0; s < NS; ++s) h[s] = 0.0f;
   float dsum = 0.0f;
-  scan_range<T, 0>(a, b, c, t0, t1, p, h, hist, dsum);
+  __shared__ float4 sbc[SUB * 2 * NS / 4];
+  scan_range<T, 0>(a, b, c, active, t0, t1, p, h, hist, dsum, reinterpret_cast<float *>(sbc));
   // carry layout: [B][nc][NS][D] states, then [B][nc][D] delta sums
+  if (!active) return;
   float *hs = a.carry + ((size_t)b * nc + ck) * NS * a.D;
 #pragma unroll
   for (int s = 0; s < NS; ++s) hs[(size_t)s * a.D + c] = h[s];
@@ -172,8 +222,10 @@ __global__ void __launch_bounds__(256) scan_pass2(ScanArgs a) {
 template <class T>
 __global__ void __launch_bounds__(64) scan_pass3(ScanArgs a) {
   const int ck = blockIdx.x, b = blockIdx.z;
-  const int c = blockIdx.y * 64 + threadIdx.x;
-  if (c >= a.D) return;
+  // lanes past the last channel compute a copy of it (every lane takes part
+  // in staging B/C) and store nothing
+  const bool active = blockIdx.y * 64 + (int)threadIdx.x < a.D;
+  const int c = min(blockIdx.y * 64 + (int)threadIdx.x, a.D - 1);
   const int nc = (a.n + a.chunk - 1) / a.chunk;
   ChanParams p;
   load_params(a, c, p);
@@ -190,8 +242,9 @@ __global__ void __launch_bounds__(64) scan_pass3(ScanArgs a) {
     for (int s = 0; s < NS; ++s) h[s] = hs[(size_t)s * a.D + c];
   }
   float dsum = 0.0f;
-  scan_range<T, 1>(a, b, c, t0, t1, p, h, hist, dsum);
-  if (ck == nc - 1) {
+  __shared__ float4 sbc[SUB * 2 * NS / 4];
+  scan_range<T, 1>(a, b, c, active, t0, t1, p, h, hist, dsum, reinterpret_cast<float *>(sbc));
+  if (ck == nc - 1 && active) {
     if (a.h_out) {
       float *ho = a.h_out + ((size_t)b * a.D + c) * NS;
 #pragma unroll
