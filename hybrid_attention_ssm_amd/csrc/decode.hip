@@ -17,7 +17,7 @@
 namespace hh {
 
 namespace {
-constexpr int DSPLIT = 512;   // virtual keys per split
+constexpr int DSPLIT = 1024;  // virtual keys per split
 constexpr int DTHREADS = 256;
 
 template <class T> struct KV8;
@@ -151,6 +151,179 @@ __global__ void __launch_bounds__(DTHREADS) decode_attn_split(DecodeAttnArgs a) 
   }
 }
 
+// bf16, head_dim 64: MFMA version.  grid (nsplit, G, B), 256 threads.
+// Each of the 4 waves walks blocks of 32 keys of the split (block w, w+4, ...):
+//   S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (rows = 16 keys, columns = the
+//   group's query heads, up to 8 of 16 used), so every lane owns one head;
+//   block-wise online softmax in the log2 domain;
+//   O^T += V^T P^T, the V block staged in this wave's LDS slice (16-byte
+//   chunks XOR-swizzled by row) and read back transposed with
+//   ds_read_b64_tr_b16 (lane j of a 16-lane group gets element j%4 of the
+//   loads of lanes 4k + j/4).
+// The 4 waves' (max, sum, O) are merged through LDS into one partial per
+// (sequence, head, split); decode_attn_combine merges the splits.
+constexpr int DB = 32;        // keys per block
+
+template <int HPG>
+__global__ void __launch_bounds__(DTHREADS) decode_attn_mfma(DecodeAttnArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf8;
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  constexpr int HD = 64;
+  __shared__ uint4 sv[4][DB * HD / 8];                 // 4 KB per wave
+  __shared__ float sm[4][16], sl[4][16], so[4][HD][17];
+  const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, grp = lane >> 4;          // MFMA column (head), lane group
+  const int p = a.len[b] - (a.producer ? 0 : 1);
+  const int lo = a.is_global ? 0 : max(0, p - a.window + 1);
+  const int last = a.is_ring ? p : min(p, a.cap - 1);
+  const int L = max(0, last - lo + 1);
+  const int nv = a.m + L;
+  const int v0 = sp * a.split, v1 = min(nv, v0 + a.split);
+  const bf16 *Kc = reinterpret_cast<const bf16 *>(a.cache_k) + (size_t)(b * a.G + g) * a.cap * HD;
+  const bf16 *Vc = reinterpret_cast<const bf16 *>(a.cache_v) + (size_t)(b * a.G + g) * a.cap * HD;
+  const bf16 *Km = reinterpret_cast<const bf16 *>(a.mk) + (size_t)g * a.m * HD;
+  const bf16 *Vm = reinterpret_cast<const bf16 *>(a.mv) + (size_t)g * a.m * HD;
+  // row of virtual key j (meta first, then positions lo..last); callers clamp j
+  auto key_row = [&](int j, const bf16 *Mp, const bf16 *Cp) -> const bf16 * {
+    if (j < a.m) return Mp + (size_t)j * HD;
+    const int pos = lo + (j - a.m);
+    const int slot = a.is_ring ? pos % a.cap : pos;
+    return Cp + (size_t)slot * HD;
+  };
+
+  // Q^T fragments (B operand): lane holds head `col`, dims 32*hh + 8*grp .. +7
+  bf8 qf[2];
+  {
+    const bf16 *Q = reinterpret_cast<const bf16 *>(a.q) + (size_t)b * a.H * HD;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (col < HPG) v = *reinterpret_cast<const uint4 *>(Q + (size_t)(g * HPG + col) * HD + 32 * hh + 8 * grp);
+      qf[hh] = __builtin_bit_cast(bf8, v);
+    }
+  }
+  const float sl2 = kLog2e * 0.125f;   // log2(e) / sqrt(64)
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x4 o[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) o[d] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // ds_read_b64_tr_b16 source offsets in this wave's V slice: (dblk, call)
+  int tr_off[8];
+#pragma unroll
+  for (int dblk = 0; dblk < 4; ++dblk)
+#pragma unroll
+    for (int call = 0; call < 2; ++call) {
+      const int row = 16 * call + 4 * grp + (col >> 2);
+      const int c16 = 16 * dblk + 4 * (col & 3);
+      tr_off[dblk * 2 + call] = row * 128 + ((((c16 >> 3) ^ (row & 7))) << 4) + (c16 & 7) * 2;
+    }
+  char *vs = reinterpret_cast<char *>(sv[wave]);
+
+  for (int kb0 = v0 + wave * DB; kb0 < v1; kb0 += 4 * DB) {
+    const int jmax = v1 - 1;
+    // K fragments (A operand of S^T): lane holds key kb0 + 16*kb + col, dims 32*hh + 8*grp
+    bf8 kf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16 *kr = key_row(min(kb0 + 16 * kb + col, jmax), Km, Kc);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        kf[kb][hh] = __builtin_bit_cast(bf8, *reinterpret_cast<const uint4 *>(kr + 32 * hh + 8 * grp));
+    }
+    // V block -> LDS: lane moves 4 chunks: row (q*8 + lane/8), chunk lane%8
+    uint4 vv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = q * 8 + (lane >> 3);
+      vv[q] = *reinterpret_cast<const uint4 *>(key_row(min(kb0 + row, jmax), Vm, Vc) + 8 * (lane & 7));
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = q * 8 + (lane >> 3);
+      *reinterpret_cast<uint4 *>(vs + row * 128 + (((lane & 7) ^ (row & 7)) << 4)) = vv[q];
+    }
+    f32x4 st[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      st[kb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][hh], qf[hh], st[kb], 0, 0, 0);
+    }
+    // st[kb][r]: key kb0 + 16*kb + 4*grp + r, head col
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = kb0 + 16 * kb + 4 * grp + r;
+        const float x = j < v1 ? st[kb][r] * sl2 : -INFINITY;
+        st[kb][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+    const float alpha = exp2_fast(m_run - m_use);
+    float rs = 0.0f;
+    bf8 pb;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pr = exp2_fast(st[kb][r] - m_use);
+        rs += pr;
+        pb[4 * kb + r] = (bf16)pr;
+      }
+    rs += __shfl_xor(rs, 16);
+    rs += __shfl_xor(rs, 32);
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[d][r] *= alpha;
+    // P^T's K slots 8*grp + e hold keys 4*grp + e (e < 4) and 16 + 4*grp + e - 4
+#pragma unroll
+    for (int dblk = 0; dblk < 4; ++dblk) {
+      const v4i16 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16 *)(vs + tr_off[dblk * 2]));
+      const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16 *)(vs + tr_off[dblk * 2 + 1]));
+      const v8i16 both = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      o[dblk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, both), pb, o[dblk], 0, 0, 0);
+    }
+  }
+  // o[dblk][r] = O^T[d = 16*dblk + 4*grp + r][head col]; merge the 4 waves
+  if (grp == 0) { sm[wave][col] = m_run; sl[wave][col] = l_run; }
+#pragma unroll
+  for (int dblk = 0; dblk < 4; ++dblk)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) so[wave][16 * dblk + 4 * grp + r][col] = o[dblk][r];
+  __syncthreads();
+  const int stride = HD + 2;
+  for (int it = threadIdx.x; it < HPG * HD; it += DTHREADS) {
+    const int hh = it / HD, d = it % HD;
+    float M = -INFINITY;
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][hh]);
+    float Ls = 0.0f, As = 0.0f;
+    for (int w = 0; w < 4; ++w) {
+      const float sc = sm[w][hh] == -INFINITY ? 0.0f : exp2_fast(sm[w][hh] - M);
+      Ls += sl[w][hh] * sc;
+      As += so[w][d][hh] * sc;
+    }
+    float *out = a.part + (((size_t)b * a.H + g * HPG + hh) * a.nsplit + sp) * stride;
+    out[2 + d] = As;
+    if (d == 0) { out[0] = M; out[1] = Ls; }
+  }
+#endif
+}
+
 // grid (B*H); hd threads
 template <class T>
 __global__ void __launch_bounds__(64) decode_attn_combine(DecodeAttnArgs a) {
@@ -183,6 +356,18 @@ hipError_t launch_decode_attention(const DecodeAttnArgs &a0, hipStream_t s) {
   a.split = DSPLIT;
   const int hpg = a.H / a.G;
   dim3 grid(a.nsplit, a.G, a.B);
+  if (sizeof(T) == 2 && a.hd == 64) {
+    switch (hpg) {
+#define HH_DECM_CASE(W) \
+      case W: hipLaunchKernelGGL((decode_attn_mfma<W>), grid, dim3(DTHREADS), 0, s, a); break;
+      HH_DECM_CASE(1) HH_DECM_CASE(2) HH_DECM_CASE(3) HH_DECM_CASE(4)
+      HH_DECM_CASE(5) HH_DECM_CASE(6) HH_DECM_CASE(7) HH_DECM_CASE(8)
+#undef HH_DECM_CASE
+      default: return hipErrorInvalidValue;
+    }
+    hipLaunchKernelGGL(decode_attn_combine<T>, dim3(a.B * a.H), dim3(64), 0, s, a);
+    return hipGetLastError();
+  }
   switch (hpg) {
 #define HH_DEC_CASE(W) \
     case W: hipLaunchKernelGGL((decode_attn_split<T, W>), grid, dim3(DTHREADS), 0, s, a); break;

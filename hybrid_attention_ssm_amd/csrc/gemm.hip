@@ -129,12 +129,17 @@ gemm_bf16_mfma(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, in
   // operand reads of the following step and the MFMAs of this one, then the
   // staged tile goes to the idle LDS buffer.  On the last tile the loads
   // repeat that tile and land in the idle buffer, which nobody reads again.
-  const int ktiles = K / Cfg::BK;
-  gload(0);
+  // split-K: grid.y slices of kps k-tiles each (kps = gridDim.y == 1 ? all)
+  const int ktiles_all = K / Cfg::BK;
+  const int kps = (ktiles_all + gridDim.y - 1) / gridDim.y;
+  const int kt_begin = blockIdx.y * kps;
+  const int ktiles = max(0, min(ktiles_all - kt_begin, kps));
+  if (ktiles == 0) return;
+  gload(kt_begin);
   sstore(0);
   __syncthreads();
   for (int kt = 0; kt < ktiles; ++kt) {
-    gload(min(kt + 1, ktiles - 1));
+    gload(kt_begin + min(kt + 1, ktiles - 1));
     const uint4 *sA = smem + (kt & 1) * Cfg::STAGE;
     const uint4 *sB = sA + Cfg::A_CHUNKS;
     fload(sA, sB, 0, 0);
@@ -434,6 +439,36 @@ struct StoreEpi {
   }
 };
 
+// Split-K partial sums: slice blockIdx.y of the K range writes fp32 to its
+// own [M, N] plane.
+struct PartialEpi {
+  float *part;
+  int M, N;
+  typedef int Col;
+  __device__ __forceinline__ Col col_info(int col) const { return col; }
+  __device__ __forceinline__ void store8(int row, const Col &col, const float v[8]) const {
+    store8_T(part + ((size_t)blockIdx.y * M + row) * N + col, v);
+  }
+};
+
+// Sum the split-K planes and hand each 8-column group to the real epilogue.
+template <class Epi>
+__global__ void __launch_bounds__(256)
+reduce_splits(const float *__restrict__ part, int splits, int M, int N, Epi epi) {
+  const int groups = N / 8;
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long)M * groups) return;
+  const int row = (int)(idx / groups), col = (int)(idx % groups) * 8;
+  float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int sp = 0; sp < splits; ++sp) {
+    const float4 *p = reinterpret_cast<const float4 *>(part + ((size_t)sp * M + row) * N + col);
+    const float4 a = p[0], b = p[1];
+    v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+    v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
+  }
+  epi.store8(row, epi.col_info(col), v);
+}
+
 template <class Cfg, class Epi>
 static hipError_t run_bf16(const bf16 *A, int M, int K, const bf16 *B, int N, const Epi &epi,
                            hipStream_t s) {
@@ -459,12 +494,47 @@ using CfgLarge = GemmCfg<256, 256, 128, 128>;
 // barriers hide behind the other's MFMAs), 3 LDS stages (96 KB)
 using CfgLds = LdsCfg<256, 256, 128, 64, 3>;
 using CfgSmall = GemmCfg<128, 64, 64, 32>;
+constexpr int kSkinnyTargetWG = 512;   // workgroups a few-row GEMM aims for
+
+// Few rows (decode, meta prefix): the weights dominate the traffic, so the
+// K range is split until there are enough workgroups to stream them at full
+// bandwidth; fp32 partials are summed by reduce_splits, which applies the
+// epilogue.  `part` holds splits*M*N floats.
+template <class Epi>
+static hipError_t run_skinny(const bf16 *A, int M, int K, const bf16 *B, int N, const Epi &epi,
+                             float *part, hipStream_t s) {
+  using Cfg = CfgSmall;
+  const int tiles = ((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
+  const int ktiles = K / Cfg::BK;
+  int splits = std::max(1, std::min(ktiles, (kSkinnyTargetWG + tiles - 1) / tiles));
+  const int kps = (ktiles + splits - 1) / splits;
+  splits = (ktiles + kps - 1) / kps;   // no empty slice
+  if (splits == 1 || !part) return run_bf16<Cfg>(A, M, K, B, N, epi, s);
+  const int grid = (tiles + 7) / 8 * 8;
+  PartialEpi pe{part, M, N};
+  hipLaunchKernelGGL((gemm_bf16_mfma<Cfg, PartialEpi>), dim3(grid, splits), dim3(Cfg::NT), 0, s, A,
+                     B, M, N, K, pe);
+  const long groups = (long)M * (N / 8);
+  hipLaunchKernelGGL((reduce_splits<Epi>), dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s,
+                     part, splits, M, N, epi);
+  return hipGetLastError();
+}
 
 template <class Epi>
 static hipError_t run_bf16_auto(const bf16 *A, int M, int K, const bf16 *B, int N, const Epi &epi,
-                                hipStream_t s) {
+                                float *part, hipStream_t s) {
   if (M >= 1024) return run_lds<CfgLds>(A, M, K, B, N, epi, s);
-  return run_bf16<CfgSmall>(A, M, K, B, N, epi, s);
+  return run_skinny(A, M, K, B, N, epi, part, s);
+}
+
+size_t skinny_part_bytes(int M, int K, int N) {
+  if (M >= 1024) return 0;
+  const int tiles = ((M + 127) / 128) * ((N + 63) / 64);
+  const int ktiles = K / 64;
+  int splits = std::max(1, std::min(ktiles, (kSkinnyTargetWG + tiles - 1) / tiles));
+  const int kps = (ktiles + splits - 1) / splits;
+  splits = (ktiles + kps - 1) / kps;
+  return splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
 }
 
 template <class Epi>
@@ -477,22 +547,22 @@ static hipError_t run_f32(const float *A, int M, int K, const float *B, int N, c
 
 template <>
 hipError_t launch_inproj<bf16>(const bf16 *x, int M, int K, const bf16 *w, int Ncols,
-                               const InProjOut &e, hipStream_t s) {
-  return run_bf16_auto(x, M, K, w, Ncols, InProjEpi<bf16>{e}, s);
+                               const InProjOut &e, float *part, hipStream_t s) {
+  return run_bf16_auto(x, M, K, w, Ncols, InProjEpi<bf16>{e}, part, s);
 }
 template <>
 hipError_t launch_inproj<float>(const float *x, int M, int K, const float *w, int Ncols,
-                                const InProjOut &e, hipStream_t s) {
+                                const InProjOut &e, float *, hipStream_t s) {
   return run_f32(x, M, K, w, Ncols, InProjEpi<float>{e}, s);
 }
 template <>
 hipError_t launch_outproj<bf16>(const bf16 *f, int M, int K, const bf16 *w, int Ncols, bf16 *out,
-                                hipStream_t s) {
-  return run_bf16_auto(f, M, K, w, Ncols, StoreEpi<bf16>{out, Ncols}, s);
+                                float *part, hipStream_t s) {
+  return run_bf16_auto(f, M, K, w, Ncols, StoreEpi<bf16>{out, Ncols}, part, s);
 }
 template <>
 hipError_t launch_outproj<float>(const float *f, int M, int K, const float *w, int Ncols,
-                                 float *out, hipStream_t s) {
+                                 float *out, float *, hipStream_t s) {
   return run_f32(f, M, K, w, Ncols, StoreEpi<float>{out, Ncols}, s);
 }
 

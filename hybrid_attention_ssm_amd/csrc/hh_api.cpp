@@ -149,12 +149,17 @@ PrefillLayout prefill_layout(const Shape &s, int B, int n) {
   take(HH_WS_Y, T * s.D * s.es);
   take(HH_WS_F, T * (s.Wa + s.D) * s.es);
   take(HH_WS_SCAN, hh::scan_carry_bytes(B, n, s.D, s.N, &L.chunk));
+  const size_t gp = s.dtype == HH_BF16
+                        ? std::max(hh::skinny_part_bytes((int)T, s.d, s.n_in),
+                                   hh::skinny_part_bytes((int)T, s.Wa + s.D, s.d))
+                        : 0;
+  if (gp) take(HH_WS_GEMM, gp);
   L.total = o;
   return L;
 }
 
 struct DecodeLayout {
-  size_t q, xs, z, dt, bc, o, y, f, part, total;
+  size_t q, xs, z, dt, bc, o, y, f, part, gemm, total;
   int nsplit;
 };
 
@@ -171,19 +176,28 @@ DecodeLayout decode_layout(const Shape &s, int B, int max_real) {
   take(L.y, (size_t)B * s.D * s.es);
   take(L.f, (size_t)B * (s.Wa + s.D) * s.es);
   take(L.part, hh::decode_attn_part_bytes(B, s.H, s.hd, s.m, max_real, nullptr, &L.nsplit));
+  L.gemm = SIZE_MAX;
+  const size_t gp = s.dtype == HH_BF16 ? std::max(hh::skinny_part_bytes(B, s.d, s.n_in),
+                                                  hh::skinny_part_bytes(B, s.Wa + s.D, s.d))
+                                       : 0;
+  if (gp) take(L.gemm, gp);
   L.total = o;
   return L;
 }
 
 char *at(void *ws, size_t off) { return static_cast<char *>(ws) + off; }
 
+float *part_ptr(void *ws, size_t off) {
+  return off == SIZE_MAX ? nullptr : reinterpret_cast<float *>(at(ws, off));
+}
+
 template <class T>
 hh_status run_inproj(const Shape &s, const hh_weights *w, const void *x, int M,
-                     const hh::InProjOut &e, hipStream_t st) {
+                     const hh::InProjOut &e, float *part, hipStream_t st) {
   Stage sg(st, e.mode == hh::EPI_DECODE ? "decode_inproj"
               : e.mode == hh::EPI_META ? "meta_inproj" : "inproj");
   hipError_t err = hh::launch_inproj<T>(static_cast<const T *>(x), M, s.d,
-                                        static_cast<const T *>(w->w_in), s.n_in, e, st);
+                                        static_cast<const T *>(w->w_in), s.n_in, e, part, st);
   return err == hipSuccess ? HH_OK : hip_fail(err, "input projection");
 }
 
@@ -208,7 +222,7 @@ hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, i
   e.dt = reinterpret_cast<float *>(at(ws, L.off[HH_WS_DELTA]));
   e.bc = reinterpret_cast<float *>(at(ws, L.off[HH_WS_BC]));
   e.dt_bias = w->dt_bias;
-  hh_status r = run_inproj<T>(s, w, x, rows, e, st);
+  hh_status r = run_inproj<T>(s, w, x, rows, e, part_ptr(ws, L.off[HH_WS_GEMM]), st);
   if (r != HH_OK) return r;
 
   hh::AttnArgs aa{};
@@ -251,7 +265,8 @@ hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, i
   {
     Stage sg(st, "outproj");
     err = hh::launch_outproj<T>(static_cast<const T *>(na.f), rows, s.Wa + s.D,
-                                static_cast<const T *>(w->w_out), s.d, static_cast<T *>(out), st);
+                                static_cast<const T *>(w->w_out), s.d, static_cast<T *>(out),
+                                part_ptr(ws, L.off[HH_WS_GEMM]), st);
   }
   if (err != hipSuccess) return hip_fail(err, "output projection");
 
@@ -274,7 +289,7 @@ hh_status meta_prefix_t(const Shape &s, const hh_weights *w, const void *R, void
   e.dt = reinterpret_cast<float *>(at(ws, L.off[HH_WS_DELTA]));
   e.bc = reinterpret_cast<float *>(at(ws, L.off[HH_WS_BC]));
   e.dt_bias = w->dt_bias;
-  hh_status r = run_inproj<T>(s, w, R, s.m, e, st);
+  hh_status r = run_inproj<T>(s, w, R, s.m, e, part_ptr(ws, L.off[HH_WS_GEMM]), st);
   if (r != HH_OK) return r;
   hh::ScanArgs sa{};
   sa.xs = e.xs; sa.z = nullptr; sa.dt = e.dt; sa.bc = e.bc;
@@ -302,7 +317,7 @@ hh_status decode_t(const Shape &s, const hh_weights *w, const void *x, int B, co
   e.dt = reinterpret_cast<float *>(at(ws, L.dt));
   e.bc = reinterpret_cast<float *>(at(ws, L.bc));
   e.dt_bias = w->dt_bias;
-  hh_status r = run_inproj<T>(s, w, x, B, e, st);
+  hh_status r = run_inproj<T>(s, w, x, B, e, part_ptr(ws, L.gemm), st);
   if (r != HH_OK) return r;
 
   hh::DecodeAttnArgs da{};
@@ -344,7 +359,8 @@ hh_status decode_t(const Shape &s, const hh_weights *w, const void *x, int B, co
   {
     Stage sg(st, "decode_outproj");
     err = hh::launch_outproj<T>(static_cast<const T *>(na.f), B, s.Wa + s.D,
-                                static_cast<const T *>(w->w_out), s.d, static_cast<T *>(out), st);
+                                static_cast<const T *>(w->w_out), s.d, static_cast<T *>(out),
+                                part_ptr(ws, L.gemm), st);
   }
   if (err != hipSuccess) return hip_fail(err, "decode output projection");
   if (prod) {

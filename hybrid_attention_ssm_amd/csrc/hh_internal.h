@@ -214,12 +214,15 @@ __device__ __forceinline__ void inproj_store8(const InProjOut &e, int row, const
 }
 
 // ---- launchers (each returns hipGetLastError() of its launches) ------------
+// `part`: split-K scratch of skinny_part_bytes(M, K, Ncols) bytes (bf16 path
+// with few rows); may be null when that size is 0.
 template <class T>
 hipError_t launch_inproj(const T *x, int M, int K, const T *w, int Ncols,
-                         const InProjOut &epi, hipStream_t s);
+                         const InProjOut &epi, float *part, hipStream_t s);
 template <class T>
 hipError_t launch_outproj(const T *f, int M, int K, const T *w, int Ncols, T *out,
-                          hipStream_t s);
+                          float *part, hipStream_t s);
+size_t skinny_part_bytes(int M, int K, int N);
 
 struct AttnArgs {
   const void *q;           // [B*n, H*hd]

@@ -212,6 +212,7 @@ enum {
   HH_WS_Y,       /* [B*n, D] dtype gated SSM output */
   HH_WS_F,       /* [B*n, H*hd + D] dtype fused features */
   HH_WS_SCAN,    /* scan chunk carries */
+  HH_WS_GEMM,    /* split-K partial sums of the projections (few-row calls) */
   HH_WS_COUNT
 };
 size_t hh_prefill_workspace_layout(const hh_dims *dims, int32_t batch,
