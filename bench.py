@@ -35,6 +35,31 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the rocprofv3 counter
+    summaries under profiles/ (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or
+    None when there is none or the kernel's sources changed since."""
+    import glob
+    import hashlib
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "hbm_traffic_*.md"))):
+        for line in open(path):
+            if not line.startswith("traffic:"):
+                continue
+            kv = dict(tok.split("=", 1) for tok in line.split()[1:])
+            if kv.get("kernel") != kernel or kv.get("workload") != workload:
+                continue
+            h = hashlib.sha256()
+            for f in kv["sources"].split(","):
+                with open(os.path.join(ROOT, f), "rb") as fh:
+                    h.update(fh.read())
+            if h.hexdigest()[:16] != kv["sha256"]:
+                return None
+            fb, wb = float(kv["fetch_bytes"]), float(kv["write_bytes"])
+            return {"bytes": fb + wb, "fetch_bytes": fb, "write_bytes": wb,
+                    "source": os.path.relpath(path, ROOT)}
+    return None
+
+
 # ---------------------------------------------------------------------------
 # algorithmic work (what the method must do; masked-out attention pairs and
 # padding are not counted)
@@ -195,11 +220,16 @@ def bench_decode(args, hb, torch):
     # the stage loop ran at positions p_first + steps .. p_first + 2 steps - 1
     _, attn_bytes_stage = decode_bytes(dims, B, specs, p_first + args.steps + args.steps // 2,
                                        W, W, w.global_cap)
+    # the global layer's K/V bytes per launch at the stage loop's mean position
+    p_stage = p_first + args.steps + args.steps // 2
+    G, hd, m = dims.n_kv_heads, dims.head_dim, dims.n_meta
+    global_attn_bytes = B * G * (p_stage + 1) * hd * 2 * 2 + G * m * hd * 2 * 2
     st = {name: (cnt, tot) for name, (cnt, tot) in stages.items()}
     log(f"[bench] decode {ms_step:.3f} ms/step; stages " +
         ", ".join(f"{k}={v[1] / v[0] * 1e3:.1f}us x{v[0]}" for k, v in st.items()))
     return dict(workload=w.name, B=B, ms_step=ms_step, stages=st, bytes=tot_bytes,
-                attn_bytes_step=attn_bytes_stage, inp=inp, context=p_first)
+                attn_bytes_step=attn_bytes_stage, global_attn_bytes=global_attn_bytes, inp=inp,
+                context=p_first)
 
 
 # ---------------------------------------------------------------------------
@@ -258,6 +288,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--cpu-sample-seqs", type=int, default=4)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 5 device-to-device copies of MIB MiB (the known-size kernel "
+                         "that scales the HBM byte counters) and exit")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -272,6 +305,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     hb.lib()
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {n} bytes x5 (each launch reads {n} and writes {n} bytes)")
+        return
 
     pre = bench_prefill(args, hb, torch) if args.only in ("prefill", "both") else None
     dec = bench_decode(args, hb, torch) if args.only in ("decode", "both") else None
@@ -294,9 +336,13 @@ def main():
         rec["stage_us"] = {k: v * 1e3 for k, v in pre["stages"].items()}
         if t_in:
             ach = fl["inproj"] / (t_in * 1e-3)
-            rec["roofline"] = {"kernel": "inproj (gemm_bf16_mfma, split epilogue)", "bound": "mfma",
+            tr = measured_traffic("gemm_bf16_lds", pre["workload"])
+            rec["roofline"] = {"kernel": "in-proj GEMM (gemm_bf16_lds, InProjEpi)", "bound": "mfma",
                                "achieved": ach / 1e12, "peak": MFMA_BF16_PEAK / 1e12,
-                               "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK, "traffic": None,
+                               "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK,
+                               "traffic": tr["bytes"] if tr else None,
+                               "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE)",
+                               "traffic_detail": tr,
                                "flop_per_launch": fl["inproj"], "avg_launch_us": t_in * 1e3}
     if dec is not None:
         B = dec["B"]
@@ -308,13 +354,20 @@ def main():
              "hbm_frac_step": dec["bytes"] / (dec["ms_step"] * 1e-3) / HBM_PEAK,
              "algorithmic_bytes_per_step": dec["bytes"],
              "stage_us": {k: v[1] / v[0] * 1e3 for k, v in st.items()}}
-        if "decode_attention" in st:
-            cnt, tot = st["decode_attention"]
-            steps = cnt / 3.0
-            ach = dec["attn_bytes_step"] * steps / (tot * 1e-3)
-            d["roofline"] = {"kernel": "decode_attention (split-K + combine), 3 layers",
+        if "decode_attention_global" in st:
+            cnt, tot = st["decode_attention_global"]
+            ach = dec["global_attn_bytes"] / (tot / cnt * 1e-3)
+            tr = measured_traffic("decode_attn_mfma", dec["workload"])
+            d["roofline"] = {"kernel": "decode attention of the global layer (decode_attn_mfma + "
+                                       "decode_attn_combine)",
                              "bound": "hbm", "achieved": ach / 1e9, "peak": HBM_PEAK / 1e9,
-                             "unit": "GB/s", "frac": ach / HBM_PEAK, "traffic": None}
+                             "unit": "GB/s", "frac": ach / HBM_PEAK,
+                             "traffic": tr["bytes"] if tr else None,
+                             "traffic_unit": "HBM bytes per launch of decode_attn_mfma "
+                                             "(FETCH_SIZE + WRITE_SIZE)",
+                             "traffic_detail": tr,
+                             "bytes_per_launch": dec["global_attn_bytes"],
+                             "avg_launch_us": tot / cnt * 1e3}
         rec["decode"] = d
         if pre is None:
             rec.update(value=d["value"], ms_per_step=d["ms_per_step"],

@@ -330,7 +330,7 @@ hh_status decode_t(const Shape &s, const hh_weights *w, const void *x, int B, co
   da.nsplit = L.nsplit;
   hipError_t err;
   {
-    Stage sg(st, "decode_attention");
+    Stage sg(st, is_global ? "decode_attention_global" : "decode_attention_swa");
     err = hh::launch_decode_attention<T>(da, st);
   }
   if (err != hipSuccess) return hip_fail(err, "decode attention");
