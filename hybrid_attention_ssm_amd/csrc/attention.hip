@@ -154,8 +154,7 @@ attn_prefill_bf16(AttnArgs a) {
   for (int st = 0; st < ASTAGES - 1; ++st) issue(min(st, tlast), st);
   for (int t = 0; t < n_tiles; ++t) {
     // this wave's DMA for tile t has landed (later tiles may still be in flight) ...
-    __builtin_amdgcn_s_waitcnt((((ASTAGES - 2) * INS) & 15) | ((((ASTAGES - 2) * INS) >> 4) << 14) |
-                               (7 << 4) | (15 << 8));
+    wait_vmcnt<(ASTAGES - 2) * INS>();
     __builtin_amdgcn_s_barrier();   // ... and every wave's; stage (t-1) is free
     __builtin_amdgcn_sched_barrier(0);
     {

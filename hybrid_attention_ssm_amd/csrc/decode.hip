@@ -17,7 +17,7 @@
 namespace hh {
 
 namespace {
-constexpr int DSPLIT = 1024;  // virtual keys per split
+constexpr int DSPLIT = 1280;  // most virtual keys per split
 constexpr int DTHREADS = 256;
 
 template <class T> struct KV8;
@@ -324,6 +324,225 @@ __global__ void __launch_bounds__(DTHREADS) decode_attn_mfma(DecodeAttnArgs a) {
 #endif
 }
 
+// Same computation with both K and V blocks streamed into LDS by DMA
+// (buffer_load_dwordx4 ... lds: full 128-byte rows, no VGPR staging), two
+// stages per wave, so a wave's next block is in flight while it works on the
+// current one.  The two stages are separate LDS arrays and the loop alternates
+// between them explicitly: reads of one stage then provably do not alias the
+// DMA into the other, and the compiler waits only for the block being read.  Needs the meta count to be a multiple of the 32-key block so
+// that a block is all meta or all cache (one buffer descriptor per block).
+// LDS rows are 128 B with 16-byte chunk c of row r stored at chunk c ^ (r % 8).
+template <int HPG>
+__global__ void __launch_bounds__(DTHREADS) decode_attn_dma(DecodeAttnArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf8;
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  typedef __attribute__((address_space(3))) void lds_void;
+  constexpr int HD = 64;
+  constexpr int BLK = DB * HD * 2;          // one K or V block: 4 KB
+  constexpr int SLICE = 2 * 2 * BLK;        // per wave: 2 stages of (K, V)
+  constexpr int SO = 17;                    // merge-buffer row stride (floats)
+  static_assert(4 * HD * SO * 4 <= 4 * SLICE / 2, "merge buffer fits the slices");
+  __shared__ __attribute__((aligned(16))) char lds0[4 * SLICE / 2];
+  __shared__ __attribute__((aligned(16))) char lds1[4 * SLICE / 2];
+  __shared__ float sm[4][16], sl[4][16];
+  const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int p = a.len[b] - (a.producer ? 0 : 1);
+  const int lo = a.is_global ? 0 : max(0, p - a.window + 1);
+  const int last = a.is_ring ? p : min(p, a.cap - 1);
+  const int L = max(0, last - lo + 1);
+  const int nv = a.m + L;
+  const int v0 = sp * a.split, v1 = min(nv, v0 + a.split);
+  const size_t cache_off = (size_t)(b * a.G + g) * a.cap * HD;
+  const __amdgpu_buffer_rsrc_t rkc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(reinterpret_cast<const bf16 *>(a.cache_k) + cache_off), (short)0, a.cap * HD * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rvc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(reinterpret_cast<const bf16 *>(a.cache_v) + cache_off), (short)0, a.cap * HD * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rkm = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(reinterpret_cast<const bf16 *>(a.mk) + (size_t)g * a.m * HD), (short)0, a.m * HD * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rvm = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(reinterpret_cast<const bf16 *>(a.mv) + (size_t)g * a.m * HD), (short)0, a.m * HD * 2, 0x00020000);
+  // real position lo + t sits in slot rbase + t (wrapped once for a ring)
+  const int rbase = a.is_ring ? lo % a.cap : lo;
+  const int wrap = a.is_ring ? a.cap : 0x7fffffff;
+  char *slice0 = lds0 + wave * (SLICE / 2);
+  char *slice1 = lds1 + wave * (SLICE / 2);
+  // DMA of the 32-key block at virtual key kb into stage st: instruction q moves
+  // rows 8q .. 8q+7 (lane: row 8q + lane/8, chunk (lane%8) ^ row%8)
+  auto issue = [&](int kb, char *kdst) {
+    int voff[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 8 * q + (lane >> 3);
+      const int j = min(kb + r, v1 - 1);
+      int row = j;
+      if (kb >= a.m) {   // uniform: the whole block is cache
+        row = rbase + (j - a.m);
+        row = row >= wrap ? row - wrap : row;
+      }
+      voff[q] = row * 128 + (((lane & 7) ^ (r & 7)) << 4);
+    }
+    if (kb < a.m) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rkm, (lds_void *)(kdst + q * 1024), 16, voff[q], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rvm, (lds_void *)(kdst + BLK + q * 1024), 16, voff[q], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rkc, (lds_void *)(kdst + q * 1024), 16, voff[q], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rvc, (lds_void *)(kdst + BLK + q * 1024), 16, voff[q], 0, 0, 0);
+      }
+    }
+  };
+
+  bf8 qf[2];
+  {
+    const bf16 *Q = reinterpret_cast<const bf16 *>(a.q) + (size_t)b * a.H * HD;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (col < HPG) v = *reinterpret_cast<const uint4 *>(Q + (size_t)(g * HPG + col) * HD + 32 * hh + 8 * grp);
+      qf[hh] = __builtin_bit_cast(bf8, v);
+    }
+  }
+  wait_vmcnt<0>();   // Q is in registers before the DMA stream starts
+  const float sl2 = kLog2e * 0.125f;   // log2(e) / sqrt(64)
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x4 o[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) o[d] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // K fragment (A operand of S^T): row 16*k2 + col, chunk 4*hh + grp
+  int k_off[4];
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int r = 16 * k2 + col;
+      k_off[k2 * 2 + hh] = r * 128 + (((4 * hh + grp) ^ (r & 7)) << 4);
+    }
+  // V^T through ds_read_b64_tr_b16 (rows 4*grp + col/4 and 16 + ..., columns 16*dblk + 4*(col%4))
+  int tr_off[8];
+#pragma unroll
+  for (int dblk = 0; dblk < 4; ++dblk)
+#pragma unroll
+    for (int call = 0; call < 2; ++call) {
+      const int row = 16 * call + 4 * grp + (col >> 2);
+      const int c16 = 16 * dblk + 4 * (col & 3);
+      tr_off[dblk * 2 + call] = row * 128 + ((((c16 >> 3) ^ (row & 7))) << 4) + (c16 & 7) * 2;
+    }
+
+  auto process = [&](int kb, const char *ks) {
+    const char *vs = ks + BLK;
+    f32x4 stt[2];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      stt[k2] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const bf8 kf = __builtin_bit_cast(bf8, *reinterpret_cast<const uint4 *>(ks + k_off[k2 * 2 + hh]));
+        stt[k2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[hh], stt[k2], 0, 0, 0);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = kb + 16 * k2 + 4 * grp + r;
+        const float x = j < v1 ? stt[k2][r] * sl2 : -INFINITY;
+        stt[k2][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = exp2_fast(m_run - m_new);
+    float rs = 0.0f;
+    bf8 pb;
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pr = exp2_fast(stt[k2][r] - m_new);
+        rs += pr;
+        pb[4 * k2 + r] = (bf16)pr;
+      }
+    rs += __shfl_xor(rs, 16);
+    rs += __shfl_xor(rs, 32);
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[d][r] *= alpha;
+#pragma unroll
+    for (int dblk = 0; dblk < 4; ++dblk) {
+      const v4i16 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16 *)(vs + tr_off[dblk * 2]));
+      const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16 *)(vs + tr_off[dblk * 2 + 1]));
+      const v8i16 both = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      o[dblk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, both), pb, o[dblk], 0, 0, 0);
+    }
+  };
+  int kb = v0 + wave * DB;
+  if (kb < v1) {
+    issue(kb, slice0);
+    while (true) {
+      issue(kb + 4 * DB < v1 ? kb + 4 * DB : kb, slice1);
+      wait_vmcnt<8>();
+      __builtin_amdgcn_sched_barrier(0);
+      process(kb, slice0);
+      __builtin_amdgcn_sched_barrier(0);
+      kb += 4 * DB;
+      if (kb >= v1) break;
+      issue(kb + 4 * DB < v1 ? kb + 4 * DB : kb, slice0);
+      wait_vmcnt<8>();
+      __builtin_amdgcn_sched_barrier(0);
+      process(kb, slice1);
+      __builtin_amdgcn_sched_barrier(0);
+      kb += 4 * DB;
+      if (kb >= v1) break;
+    }
+    wait_vmcnt<0>();
+  }
+  // merge the 4 waves (the DMA slices become the merge buffer)
+  __syncthreads();
+  float *so = reinterpret_cast<float *>(lds0);
+  if (grp == 0) { sm[wave][col] = m_run; sl[wave][col] = l_run; }
+#pragma unroll
+  for (int dblk = 0; dblk < 4; ++dblk)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) so[(wave * HD + 16 * dblk + 4 * grp + r) * SO + col] = o[dblk][r];
+  __syncthreads();
+  const int stride = HD + 2;
+  for (int it = threadIdx.x; it < HPG * HD; it += DTHREADS) {
+    const int hh = it / HD, d = it % HD;
+    float M = -INFINITY;
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][hh]);
+    float Ls = 0.0f, As = 0.0f;
+    for (int w = 0; w < 4; ++w) {
+      const float sc = sm[w][hh] == -INFINITY ? 0.0f : exp2_fast(sm[w][hh] - M);
+      Ls += sl[w][hh] * sc;
+      As += so[(w * HD + d) * SO + hh] * sc;
+    }
+    if (a.nsplit == 1) {   // the only split: this is the output
+      reinterpret_cast<bf16 *>(a.o)[((size_t)b * a.H + g * HPG + hh) * HD + d] = (bf16)(As / Ls);
+      continue;
+    }
+    float *out = a.part + (((size_t)b * a.H + g * HPG + hh) * a.nsplit + sp) * stride;
+    out[2 + d] = As;
+    if (d == 0) { out[0] = M; out[1] = Ls; }
+  }
+#endif
+}
+
 // grid (B*H); hd threads
 template <class T>
 __global__ void __launch_bounds__(64) decode_attn_combine(DecodeAttnArgs a) {
@@ -343,19 +562,38 @@ __global__ void __launch_bounds__(64) decode_attn_combine(DecodeAttnArgs a) {
   reinterpret_cast<T *>(a.o)[(size_t)bh * a.hd + d] = from_f32<T>(acc / L);
 }
 
-size_t decode_attn_part_bytes(int B, int H, int hd, int m, int max_real, int * /*unused*/,
+// Keys per split: at most DSPLIT, and small enough that the grid has about
+// kDecodeTargetWG workgroups (a short sliding window over few heads would
+// otherwise leave most of the chip idle); a multiple of the 32-key block.
+constexpr int kDecodeTargetWG = 640;
+size_t decode_attn_part_bytes(int B, int H, int G, int hd, int m, int max_real, int *split_out,
                               int *nsplit_out) {
-  const int nsplit = std::max(1, (m + max_real + DSPLIT - 1) / DSPLIT);
+  const int nv = std::max(1, m + max_real);
+  const int want = (kDecodeTargetWG + B * G - 1) / (B * G);
+  int nsplit = std::max((nv + DSPLIT - 1) / DSPLIT, std::min(want, (nv + 127) / 128));
+  const int split = ((nv + nsplit - 1) / nsplit + 31) / 32 * 32;
+  nsplit = (nv + split - 1) / split;
+  if (split_out) *split_out = split;
   if (nsplit_out) *nsplit_out = nsplit;
   return (size_t)B * H * nsplit * (hd + 2) * sizeof(float);
 }
 
 template <class T>
-hipError_t launch_decode_attention(const DecodeAttnArgs &a0, hipStream_t s) {
-  DecodeAttnArgs a = a0;
-  a.split = DSPLIT;
+hipError_t launch_decode_attention(const DecodeAttnArgs &a, hipStream_t s) {
   const int hpg = a.H / a.G;
   dim3 grid(a.nsplit, a.G, a.B);
+  if (sizeof(T) == 2 && a.hd == 64 && a.m % DB == 0 && a.split % DB == 0) {
+    switch (hpg) {
+#define HH_DECD_CASE(W) \
+      case W: hipLaunchKernelGGL((decode_attn_dma<W>), grid, dim3(DTHREADS), 0, s, a); break;
+      HH_DECD_CASE(1) HH_DECD_CASE(2) HH_DECD_CASE(3) HH_DECD_CASE(4)
+      HH_DECD_CASE(5) HH_DECD_CASE(6) HH_DECD_CASE(7) HH_DECD_CASE(8)
+#undef HH_DECD_CASE
+      default: return hipErrorInvalidValue;
+    }
+    if (a.nsplit > 1) hipLaunchKernelGGL(decode_attn_combine<T>, dim3(a.B * a.H), dim3(64), 0, s, a);
+    return hipGetLastError();
+  }
   if (sizeof(T) == 2 && a.hd == 64) {
     switch (hpg) {
 #define HH_DECM_CASE(W) \
@@ -383,52 +621,79 @@ template hipError_t launch_decode_attention<float>(const DecodeAttnArgs &, hipSt
 template hipError_t launch_decode_attention<bf16>(const DecodeAttnArgs &, hipStream_t);
 
 // ---------------------------------------------------------------------------
-// one SSM step per (sequence, channel)
+// one SSM step: four lanes per (sequence, channel), four states each, so the
+// state, A and B/C move as contiguous 16-byte vectors across the quad.  It
+// runs after the step's attention and also advances a producer's len.
 // ---------------------------------------------------------------------------
-template <class T>
+__device__ __forceinline__ float quad_sum(float v) {
+  // quad_perm [1,0,3,2] then [2,3,0,1]
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+  return v;
+}
+
+template <class T, int K>
 __global__ void __launch_bounds__(256) decode_ssm_step(DecodeSsmArgs a) {
   constexpr int NS = 16;
-  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (long)a.B * a.D) return;
-  const int b = (int)(idx / a.D), c = (int)(idx % a.D);
-  const T *z = reinterpret_cast<const T *>(a.z);
-  float *conv = a.conv + (size_t)b * (a.k - 1) * a.D;
-  const float x = a.xs[idx];
-  // window: conv rows (oldest first) then the current xs; tap j multiplies window[j]
-  float cv = a.conv_b[c];
-  float win[4];
-  for (int j = 0; j < a.k - 1; ++j) win[j] = conv[(size_t)j * a.D + c];
-  win[a.k - 1] = x;
-  for (int j = 0; j < a.k; ++j) cv = fmaf(a.conv_w[(size_t)c * a.k + j], win[j], cv);
-  const float u = silu_f(cv);
-  const float dt = a.dt[idx];
-  const float du = dt * u;
-  const float *bc = a.bc + (size_t)b * 2 * NS;
-  float *hp = a.h + idx * NS;
-  float h[NS];
+  const long t = (long)blockIdx.x * 256 + threadIdx.x;
+  const long idx = t >> 2;                  // sequence * D + channel
+  const int q = (int)(t & 3);               // states 4q .. 4q+3
+  const bool live = idx < (long)a.B * a.D;
+  const long ci = live ? idx : 0;
+  const int b = (int)(ci / a.D), c = (int)(ci % a.D);
+  float *conv = a.conv + (size_t)b * (K - 1) * a.D + c;
+  // every load is independent: issue them all before any arithmetic
+  float win[K], wk[K];
 #pragma unroll
-  for (int s = 0; s < NS; s += 4) {
-    const float4 v = *reinterpret_cast<const float4 *>(hp + s);
-    h[s] = v.x; h[s + 1] = v.y; h[s + 2] = v.z; h[s + 3] = v.w;
+  for (int j = 0; j < K - 1; ++j) win[j] = conv[(size_t)j * a.D];   // oldest first
+  win[K - 1] = a.xs[ci];
+#pragma unroll
+  for (int j = 0; j < K; ++j) wk[j] = a.conv_w[(size_t)c * K + j];
+  const float cb = a.conv_b[c];
+  const float dt = a.dt[ci];
+  const float zv = to_f32(reinterpret_cast<const T *>(a.z)[ci]);
+  const float4 Bq = *reinterpret_cast<const float4 *>(a.bc + (size_t)b * 2 * NS + 4 * q);
+  const float4 Cq = *reinterpret_cast<const float4 *>(a.bc + (size_t)b * 2 * NS + NS + 4 * q);
+  const float4 Aq = *reinterpret_cast<const float4 *>(a.A + (size_t)c * NS + 4 * q);
+  float4 *hp = reinterpret_cast<float4 *>(a.h + ci * NS + 4 * q);
+  float4 h = *hp;
+  // tap j multiplies window row j (tap K-1 the current row)
+  float cv = cb;
+#pragma unroll
+  for (int j = 0; j < K; ++j) cv = fmaf(wk[j], win[j], cv);
+  const float du = dt * silu_f(cv);
+  const float d2 = dt * kLog2e;
+  h.x = fmaf(exp2_fast(d2 * Aq.x), h.x, du * Bq.x);
+  h.y = fmaf(exp2_fast(d2 * Aq.y), h.y, du * Bq.y);
+  h.z = fmaf(exp2_fast(d2 * Aq.z), h.z, du * Bq.z);
+  h.w = fmaf(exp2_fast(d2 * Aq.w), h.w, du * Bq.w);
+  float y = Cq.x * h.x;
+  y = fmaf(Cq.y, h.y, y);
+  y = fmaf(Cq.z, h.z, y);
+  y = fmaf(Cq.w, h.w, y);
+  y = quad_sum(y);
+  if (!live) return;
+  *hp = h;
+  if (q == 0) {
+    // a producer's new token joins the cache once this step's attention (an
+    // earlier launch on the stream) has read len
+    if (a.len_bump && c == 0 && (a.is_ring || a.len_bump[b] < a.cap)) a.len_bump[b] += 1;
+#pragma unroll
+    for (int j = 0; j < K - 1; ++j) conv[(size_t)j * a.D] = win[j + 1];
+    reinterpret_cast<T *>(a.y)[idx] = from_f32<T>(y * silu_f(zv));
   }
-  float y = 0.0f;
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const float A2 = a.A[(size_t)c * NS + s] * kLog2e;
-    h[s] = fmaf(exp2_fast(dt * A2), h[s], du * bc[s]);
-    y = fmaf(bc[NS + s], h[s], y);
-  }
-#pragma unroll
-  for (int s = 0; s < NS; s += 4)
-    *reinterpret_cast<float4 *>(hp + s) = make_float4(h[s], h[s + 1], h[s + 2], h[s + 3]);
-  for (int j = 0; j < a.k - 1; ++j) conv[(size_t)j * a.D + c] = win[j + 1];
-  reinterpret_cast<T *>(a.y)[idx] = from_f32<T>(y * silu_f(to_f32(z[idx])));
 }
 
 template <class T>
 hipError_t launch_decode_ssm(const DecodeSsmArgs &a, hipStream_t s) {
-  const long n = (long)a.B * a.D;
-  hipLaunchKernelGGL(decode_ssm_step<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  const long n = (long)a.B * a.D * 4;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  switch (a.k) {
+    case 2: hipLaunchKernelGGL((decode_ssm_step<T, 2>), grid, dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((decode_ssm_step<T, 3>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_ssm_step<T, 4>), grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 template hipError_t launch_decode_ssm<float>(const DecodeSsmArgs &, hipStream_t);
@@ -441,16 +706,8 @@ __global__ void set_len_kernel(int32_t *len, int B, int value) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < B) len[i] = value;
 }
-__global__ void bump_len_kernel(int32_t *len, int B, int cap, int is_ring) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < B && (is_ring || len[i] < cap)) len[i] += 1;
-}
 hipError_t launch_set_len(int32_t *len, int B, int value, hipStream_t s) {
   hipLaunchKernelGGL(set_len_kernel, dim3((B + 255) / 256), dim3(256), 0, s, len, B, value);
-  return hipGetLastError();
-}
-hipError_t launch_bump_len(int32_t *len, int B, int cap, int is_ring, hipStream_t s) {
-  hipLaunchKernelGGL(bump_len_kernel, dim3((B + 255) / 256), dim3(256), 0, s, len, B, cap, is_ring);
   return hipGetLastError();
 }
 

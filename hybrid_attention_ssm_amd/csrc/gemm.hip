@@ -11,29 +11,6 @@
 
 namespace hh {
 
-// ---------------------------------------------------------------------------
-// bf16 MFMA kernel
-// ---------------------------------------------------------------------------
-template <int BM_, int BN_, int WM_, int WN_>
-struct GemmCfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-  static constexpr int BK = 64;                      // bf16 elements per k-tile
-  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
-  static constexpr int NWAVES = WAVES_M * WAVES_N;
-  static constexpr int NT = NWAVES * 64;
-  static constexpr int TM = WM / 32, TN = WN / 32;   // 32x32 blocks per wave
-  static constexpr int A_CHUNKS = BM * BK / 8;       // 16-byte chunks per tile
-  static constexpr int B_CHUNKS = BN * BK / 8;
-  static constexpr int A_PER_T = (A_CHUNKS + NT - 1) / NT;
-  static constexpr int B_PER_T = (B_CHUNKS + NT - 1) / NT;
-  static constexpr int STAGE = A_CHUNKS + B_CHUNKS;
-};
-
-// LDS position of 16-byte chunk kc (0..7) of tile row `row`.  Rows are 128 B;
-// XOR-ing the chunk with (row/2)%8 spreads the 32 rows one MFMA operand read
-// touches over all banks.
-__device__ __forceinline__ int swz(int row, int kc) { return row * 8 + (kc ^ ((row >> 1) & 7)); }
-
 // Map the linear block id to an output tile.  Hardware hands consecutive
 // block ids to the 8 XCDs in turn; the remap gives each XCD a contiguous run
 // of logical tiles, and the grouped order (GROUP row-tiles per column sweep)
@@ -51,148 +28,6 @@ __device__ __forceinline__ bool tile_of(int tiles_m, int tiles_n, int &tm, int &
   tm = first_m + in_group % gm;
   tn = in_group / gm;
   return true;
-}
-
-template <class Cfg, class Epi>
-__global__ void __launch_bounds__(Cfg::NT)
-gemm_bf16_mfma(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int N, int K,
-               Epi epi) {
-  __shared__ uint4 smem[2 * Cfg::STAGE];
-  int tm, tn;
-  if (!tile_of((M + Cfg::BM - 1) / Cfg::BM, (N + Cfg::BN - 1) / Cfg::BN, tm, tn)) return;
-  const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
-  const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
-  const int lr = lane & 31, lh = lane >> 5;
-
-  // Global -> register staging with buffer loads.  Each operand gets a buffer
-  // descriptor based at the tile's first row whose size ends at the last
-  // valid row, so rows past M (or N) read as zero in hardware; the k offset is
-  // a uniform (SGPR) offset.  K is a multiple of BK on this path (checked on
-  // the host).
-  uint4 ra[Cfg::A_PER_T], rb[Cfg::B_PER_T];
-  static_assert(Cfg::A_CHUNKS % Cfg::NT == 0 && Cfg::B_CHUNKS % Cfg::NT == 0, "tile/threads");
-  constexpr int ROWS_PER_PASS = Cfg::NT / 8;
-  const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(A + (size_t)m0 * K), (short)0, (M - m0) * K * 2, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(B + (size_t)n0 * K), (short)0, (N - n0) * K * 2, 0x00020000);
-  const int voff = ((tid >> 3) * K + (tid & 7) * 8) * 2;
-  const int vstep = ROWS_PER_PASS * K * 2;
-  auto gload = [&](int kt) {
-    const int koff = kt * Cfg::BK * 2;
-#pragma unroll
-    for (int i = 0; i < Cfg::A_PER_T; ++i)
-      ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsA, voff + i * vstep, koff, 0));
-#pragma unroll
-    for (int i = 0; i < Cfg::B_PER_T; ++i)
-      rb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsB, voff + i * vstep, koff, 0));
-  };
-  auto sstore = [&](int buf) {
-    uint4 *sA = smem + buf * Cfg::STAGE;
-    uint4 *sB = sA + Cfg::A_CHUNKS;
-#pragma unroll
-    for (int i = 0; i < Cfg::A_PER_T; ++i) {
-      const int c = tid + i * Cfg::NT;
-      sA[swz(c >> 3, c & 7)] = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < Cfg::B_PER_T; ++i) {
-      const int c = tid + i * Cfg::NT;
-      sB[swz(c >> 3, c & 7)] = rb[i];
-    }
-  };
-
-  f32x16 acc[Cfg::TM][Cfg::TN];
-#pragma unroll
-  for (int i = 0; i < Cfg::TM; ++i)
-#pragma unroll
-    for (int j = 0; j < Cfg::TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  // MFMA operand fragments, double-buffered across the 16-wide k-steps so the
-  // LDS reads of step ks+1 are in flight while step ks's MFMAs issue.
-  bf16x8 af[2][Cfg::TM], bfr[2][Cfg::TN];
-  auto fload = [&](const uint4 *sA, const uint4 *sB, int ks, int slot) {
-#pragma unroll
-    for (int i = 0; i < Cfg::TM; ++i)
-      af[slot][i] = __builtin_bit_cast(bf16x8, sA[swz(wm * Cfg::WM + i * 32 + lr, ks * 2 + lh)]);
-#pragma unroll
-    for (int j = 0; j < Cfg::TN; ++j)
-      bfr[slot][j] = __builtin_bit_cast(bf16x8, sB[swz(wn * Cfg::WN + j * 32 + lr, ks * 2 + lh)]);
-  };
-
-  // One basic block per k-tile (no branches), so the scheduling barriers fix
-  // the order: next tile's global loads, then for each 16-wide k-step the
-  // operand reads of the following step and the MFMAs of this one, then the
-  // staged tile goes to the idle LDS buffer.  On the last tile the loads
-  // repeat that tile and land in the idle buffer, which nobody reads again.
-  // split-K: grid.y slices of kps k-tiles each (kps = gridDim.y == 1 ? all)
-  const int ktiles_all = K / Cfg::BK;
-  const int kps = (ktiles_all + gridDim.y - 1) / gridDim.y;
-  const int kt_begin = blockIdx.y * kps;
-  const int ktiles = max(0, min(ktiles_all - kt_begin, kps));
-  if (ktiles == 0) return;
-  gload(kt_begin);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < ktiles; ++kt) {
-    gload(kt_begin + min(kt + 1, ktiles - 1));
-    const uint4 *sA = smem + (kt & 1) * Cfg::STAGE;
-    const uint4 *sB = sA + Cfg::A_CHUNKS;
-    fload(sA, sB, 0, 0);
-#pragma unroll
-    for (int ks = 0; ks < Cfg::BK / 16; ++ks) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (ks + 1 < Cfg::BK / 16) fload(sA, sB, ks + 1, (ks + 1) & 1);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < Cfg::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < Cfg::TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j],
-                                                              acc[i][j], 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    sstore((kt + 1) & 1);
-    __syncthreads();
-  }
-
-  // Epilogue.  32x32 accumulator layout: lane holds column lane%32, register
-  // r holds row 8*(r/4) + 4*(lane/32) + r%4.  Each wave stages one 32-row
-  // strip of its tile through LDS (static register indexing keeps the
-  // accumulators in registers), then reads it back row-major so that every
-  // lane hands 8 consecutive columns to the epilogue.
-  constexpr int SROW = Cfg::WN + 8;             // padded strip row (floats)
-  constexpr int LPR = Cfg::WN / 8;              // lanes per strip row
-  constexpr int RPI = 64 / LPR;                 // strip rows per pass
-  float *strip = reinterpret_cast<float *>(smem) + wave * 32 * SROW;
-  // a lane stores the same 8 columns for every row: resolve them once
-  const int cc = (lane % LPR) * 8;
-  const int gcol = n0 + wn * Cfg::WN + cc;
-  const bool col_ok = gcol < N;
-  const typename Epi::Col ci = epi.col_info(col_ok ? gcol : 0);
-#pragma unroll
-  for (int i = 0; i < Cfg::TM; ++i) {
-#pragma unroll
-    for (int j = 0; j < Cfg::TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        strip[(8 * (r >> 2) + 4 * lh + (r & 3)) * SROW + j * 32 + lr] = acc[i][j][r];
-    __syncthreads();
-#pragma unroll 1
-    for (int it = 0; it < 32 / RPI; ++it) {
-      const int rr = it * RPI + lane / LPR;
-      const float4 a = *reinterpret_cast<const float4 *>(strip + rr * SROW + cc);
-      const float4 b = *reinterpret_cast<const float4 *>(strip + rr * SROW + cc + 4);
-      const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-      const int row = m0 + wm * Cfg::WM + i * 32 + rr;
-      if (row < M && col_ok) epi.store8(row, ci, v);
-    }
-    __syncthreads();
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -224,13 +59,6 @@ struct LdsCfg {
 // same c land on 16 distinct 16-byte bank groups
 __device__ __forceinline__ int swz4(int row, int c) { return row * 4 + (c ^ ((row >> 2) & 3)); }
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  // gfx9 s_waitcnt immediate: vmcnt[3:0] at bits 3:0, vmcnt[5:4] at 15:14;
-  // expcnt (6:4) and lgkmcnt (11:8) left at their maxima (no wait)
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 template <class Cfg, class Epi>
 __global__ void __launch_bounds__(Cfg::NT)
@@ -298,10 +126,14 @@ gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int
       bfr[slot][j] = __builtin_bit_cast(bf16x8, sB[swz4(wn * Cfg::WN + j * 32 + lr, ks * 2 + lh)]);
   };
 
-  const int ktiles = K / Cfg::BK;
-  const int klast = ktiles - 1;
+  // split-K: slice blockIdx.y of gridDim.y covers k-tiles [kt0, kt0 + ktiles)
+  const int ktiles_all = K / Cfg::BK;
+  const int kps = (ktiles_all + gridDim.y - 1) / gridDim.y;
+  const int kt0 = blockIdx.y * kps;
+  const int ktiles = max(0, min(ktiles_all - kt0, kps));
+  auto ktile = [&](int i) { return kt0 + min(i, ktiles - 1); };   // steps past the end repeat the last
 #pragma unroll
-  for (int st = 0; st < Cfg::STAGES - 1; ++st) issue(min(st, klast), st);
+  for (int st = 0; st < Cfg::STAGES - 1; ++st) issue(ktile(st), st);
   constexpr int PER_TILE = Cfg::A_INS + Cfg::B_INS;
   for (int kt = 0; kt < ktiles; ++kt) {
     wait_vmcnt<(Cfg::STAGES - 2) * PER_TILE>();   // this wave's loads of tile kt have landed
@@ -309,7 +141,7 @@ gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int
     __builtin_amdgcn_sched_barrier(0);
     // refill the stage every wave finished reading before this barrier
     const int nt = kt + Cfg::STAGES - 1;
-    issue(min(nt, klast), nt % Cfg::STAGES);
+    issue(ktile(nt), nt % Cfg::STAGES);
     const uint4 *sA = smem + (kt % Cfg::STAGES) * Cfg::STAGE;
     const uint4 *sB = sA + Cfg::A_UNITS;
     fload(sA, sB, 0, 0);
@@ -470,16 +302,6 @@ reduce_splits(const float *__restrict__ part, int splits, int M, int N, Epi epi)
 }
 
 template <class Cfg, class Epi>
-static hipError_t run_bf16(const bf16 *A, int M, int K, const bf16 *B, int N, const Epi &epi,
-                           hipStream_t s) {
-  const int tiles = ((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
-  const int grid = (tiles + 7) / 8 * 8;
-  hipLaunchKernelGGL((gemm_bf16_mfma<Cfg, Epi>), dim3(grid), dim3(Cfg::NT), 0, s, A, B, M, N,
-                     K, epi);
-  return hipGetLastError();
-}
-
-template <class Cfg, class Epi>
 static hipError_t run_lds(const bf16 *A, int M, int K, const bf16 *B, int N, const Epi &epi,
                           hipStream_t s) {
   const int tiles = ((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
@@ -489,35 +311,52 @@ static hipError_t run_lds(const bf16 *A, int M, int K, const bf16 *B, int N, con
   return hipGetLastError();
 }
 
-using CfgLarge = GemmCfg<256, 256, 128, 128>;
 // 256x256 tile, 8 waves of 128x64 (two per SIMD, so one wave's LDS waits and
 // barriers hide behind the other's MFMAs), 3 LDS stages (96 KB)
 using CfgLds = LdsCfg<256, 256, 128, 64, 3>;
-using CfgSmall = GemmCfg<128, 64, 64, 32>;
-constexpr int kSkinnyTargetWG = 512;   // workgroups a few-row GEMM aims for
+// Few rows (decode, meta prefix): the weights dominate the traffic and each
+// workgroup streams a slab of 64 weight rows.  When those slabs alone leave
+// the chip short of workgroups (the output projection: 25 slabs) the K range
+// is split too; fp32 partials are then summed by reduce_splits, which applies
+// the epilogue.  `part` holds splits*M*N floats.  (A split input projection
+// loses more to its partial planes and the scattered epilogue of the reduce
+// than it gains.)
+using CfgSkinny = LdsCfg<128, 64, 64, 32, 4>;
+constexpr int kSkinnyTargetWG = 200;   // workgroups a few-row GEMM aims for
 
-// Few rows (decode, meta prefix): the weights dominate the traffic, so the
-// K range is split until there are enough workgroups to stream them at full
-// bandwidth; fp32 partials are summed by reduce_splits, which applies the
-// epilogue.  `part` holds splits*M*N floats.
-template <class Epi>
-static hipError_t run_skinny(const bf16 *A, int M, int K, const bf16 *B, int N, const Epi &epi,
-                             float *part, hipStream_t s) {
-  using Cfg = CfgSmall;
-  const int tiles = ((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
-  const int ktiles = K / Cfg::BK;
-  int splits = std::max(1, std::min(ktiles, (kSkinnyTargetWG + tiles - 1) / tiles));
+static int skinny_splits(int M, int K, int N) {
+  using C = CfgSkinny;
+  const int tiles = ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
+  if (tiles >= 128) return 1;
+  const int ktiles = K / C::BK;
+  const int splits = std::max(1, std::min(ktiles / 8, (kSkinnyTargetWG + tiles - 1) / tiles));
   const int kps = (ktiles + splits - 1) / splits;
-  splits = (ktiles + kps - 1) / kps;   // no empty slice
-  if (splits == 1 || !part) return run_bf16<Cfg>(A, M, K, B, N, epi, s);
+  return (ktiles + kps - 1) / kps;   // no empty slice
+}
+
+template <class Cfg, class Epi>
+static hipError_t run_skinny_cfg(const bf16 *A, int M, int K, const bf16 *B, int N, const Epi &epi,
+                                 int splits, float *part, hipStream_t s) {
+  const int tiles = ((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
   const int grid = (tiles + 7) / 8 * 8;
+  if (splits == 1) {
+    hipLaunchKernelGGL((gemm_bf16_lds<Cfg, Epi>), dim3(grid), dim3(Cfg::NT), 0, s, A, B, M, N, K,
+                       epi);
+    return hipGetLastError();
+  }
   PartialEpi pe{part, M, N};
-  hipLaunchKernelGGL((gemm_bf16_mfma<Cfg, PartialEpi>), dim3(grid, splits), dim3(Cfg::NT), 0, s, A,
+  hipLaunchKernelGGL((gemm_bf16_lds<Cfg, PartialEpi>), dim3(grid, splits), dim3(Cfg::NT), 0, s, A,
                      B, M, N, K, pe);
   const long groups = (long)M * (N / 8);
   hipLaunchKernelGGL((reduce_splits<Epi>), dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s,
                      part, splits, M, N, epi);
   return hipGetLastError();
+}
+
+template <class Epi>
+static hipError_t run_skinny(const bf16 *A, int M, int K, const bf16 *B, int N, const Epi &epi,
+                             float *part, hipStream_t s) {
+  return run_skinny_cfg<CfgSkinny>(A, M, K, B, N, epi, part ? skinny_splits(M, K, N) : 1, part, s);
 }
 
 template <class Epi>
@@ -529,11 +368,7 @@ static hipError_t run_bf16_auto(const bf16 *A, int M, int K, const bf16 *B, int 
 
 size_t skinny_part_bytes(int M, int K, int N) {
   if (M >= 1024) return 0;
-  const int tiles = ((M + 127) / 128) * ((N + 63) / 64);
-  const int ktiles = K / 64;
-  int splits = std::max(1, std::min(ktiles, (kSkinnyTargetWG + tiles - 1) / tiles));
-  const int kps = (ktiles + splits - 1) / splits;
-  splits = (ktiles + kps - 1) / kps;
+  const int splits = skinny_splits(M, K, N);
   return splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
 }
 

@@ -160,7 +160,7 @@ PrefillLayout prefill_layout(const Shape &s, int B, int n) {
 
 struct DecodeLayout {
   size_t q, xs, z, dt, bc, o, y, f, part, gemm, total;
-  int nsplit;
+  int split, nsplit;
 };
 
 DecodeLayout decode_layout(const Shape &s, int B, int max_real) {
@@ -175,7 +175,7 @@ DecodeLayout decode_layout(const Shape &s, int B, int max_real) {
   take(L.o, (size_t)B * s.Wa * s.es);
   take(L.y, (size_t)B * s.D * s.es);
   take(L.f, (size_t)B * (s.Wa + s.D) * s.es);
-  take(L.part, hh::decode_attn_part_bytes(B, s.H, s.hd, s.m, max_real, nullptr, &L.nsplit));
+  take(L.part, hh::decode_attn_part_bytes(B, s.H, s.G, s.hd, s.m, max_real, &L.split, &L.nsplit));
   L.gemm = SIZE_MAX;
   const size_t gp = s.dtype == HH_BF16 ? std::max(hh::skinny_part_bytes(B, s.d, s.n_in),
                                                   hh::skinny_part_bytes(B, s.Wa + s.D, s.d))
@@ -327,6 +327,7 @@ hh_status decode_t(const Shape &s, const hh_weights *w, const void *x, int B, co
   da.part = reinterpret_cast<float *>(at(ws, L.part));
   da.B = B; da.H = s.H; da.G = s.G; da.hd = s.hd; da.m = s.m; da.cap = kv->cap;
   da.is_ring = kv->is_ring; da.window = window; da.is_global = is_global;
+  da.split = L.split;
   da.nsplit = L.nsplit;
   hipError_t err;
   {
@@ -340,6 +341,8 @@ hh_status decode_t(const Shape &s, const hh_weights *w, const void *x, int B, co
   sa.A = w->A; sa.conv_w = w->conv_w; sa.conv_b = w->conv_b;
   sa.h = state->h; sa.conv = state->conv; sa.y = at(ws, L.y);
   sa.B = B; sa.D = s.D; sa.N = s.N; sa.k = s.k;
+  sa.len_bump = prod ? kv->len : nullptr;
+  sa.cap = kv->cap; sa.is_ring = kv->is_ring;
   {
     Stage sg(st, "decode_ssm");
     err = hh::launch_decode_ssm<T>(sa, st);
@@ -363,10 +366,6 @@ hh_status decode_t(const Shape &s, const hh_weights *w, const void *x, int B, co
                                 part_ptr(ws, L.gemm), st);
   }
   if (err != hipSuccess) return hip_fail(err, "decode output projection");
-  if (prod) {
-    err = hh::launch_bump_len(kv->len, B, kv->cap, kv->is_ring, st);
-    if (err != hipSuccess) return hip_fail(err, "cache length");
-  }
   return HH_OK;
 }
 

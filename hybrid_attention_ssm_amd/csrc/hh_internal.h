@@ -29,6 +29,15 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf
 
 // ---- fast transcendental helpers (fp32) ------------------------------------
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Wait until at most N of this wave's vector-memory loads are outstanding
+// (they complete in issue order).  gfx9 s_waitcnt immediate: vmcnt[3:0] at
+// bits 3:0 and vmcnt[5:4] at 15:14; expcnt and lgkmcnt at their maxima.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 __device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
 // x * sigmoid(x) with sigmoid = 1 / (1 + 2^(-x log2 e)); saturates cleanly:
 // x -> -inf gives 2^(+inf) = inf, rcp(inf) = 0.
@@ -274,7 +283,7 @@ struct DecodeAttnArgs {
   int B, H, G, hd, m, cap, is_ring, window, is_global, split, nsplit;
 };
 template <class T> hipError_t launch_decode_attention(const DecodeAttnArgs &a, hipStream_t s);
-size_t decode_attn_part_bytes(int B, int H, int hd, int m, int max_real,
+size_t decode_attn_part_bytes(int B, int H, int G, int hd, int m, int max_real,
                               int *split_out, int *nsplit_out);
 
 struct DecodeSsmArgs {
@@ -285,11 +294,12 @@ struct DecodeSsmArgs {
   float *h;                // [B, D, N] in/out
   float *conv;             // [B, k-1, D] fp32 in/out
   void *y;                 // [B, D]
+  int32_t *len_bump;       // producer: len[b] += 1 (ring, or below cap); else null
+  int cap, is_ring;
   int B, D, N, k;
 };
 template <class T> hipError_t launch_decode_ssm(const DecodeSsmArgs &a, hipStream_t s);
 
 hipError_t launch_set_len(int32_t *len, int B, int value, hipStream_t s);
-hipError_t launch_bump_len(int32_t *len, int B, int cap, int is_ring, hipStream_t s);
 
 }  // namespace hh

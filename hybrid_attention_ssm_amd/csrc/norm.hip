@@ -2,7 +2,8 @@
 // of its text and the mean fusion of Appendix B):
 //   F = 1/2 [beta_attn * O / rms(O) || beta_ssm * Y / rms(Y)],
 //   rms(v) = sqrt(mean(v^2) + eps), statistics in fp32.
-// One wavefront per token row; the two halves are written side by side so a
+// One wavefront (or, for few rows, one workgroup) per token row; the two
+// halves are written side by side so a
 // single output projection over [H*hd + D] columns follows.
 #include "hh_internal.h"
 
@@ -19,12 +20,13 @@ template <class T> struct Vec;
 template <> struct Vec<bf16> { static constexpr int W = 8; typedef bf16x8 type; };
 template <> struct Vec<float> { static constexpr int W = 4; typedef f32x4 type; };
 
-template <class T>
+// partial sums over this lane's elements; lanes of WPR waves stride the row
+template <class T, int WPR>
 __device__ __forceinline__ float sumsq(const T *p, int n, int lane) {
   constexpr int W = Vec<T>::W;
   typedef typename Vec<T>::type V;
   float s = 0.0f;
-  for (int i = lane * W; i < n; i += 64 * W) {
+  for (int i = lane * W; i < n; i += 64 * WPR * W) {
     const V v = *reinterpret_cast<const V *>(p + i);
 #pragma unroll
     for (int e = 0; e < W; ++e) { const float f = to_f32(v[e]); s = fmaf(f, f, s); }
@@ -32,11 +34,11 @@ __device__ __forceinline__ float sumsq(const T *p, int n, int lane) {
   return wave_sum(s);
 }
 
-template <class T>
+template <class T, int WPR>
 __device__ __forceinline__ void scaled(const T *p, const float *beta, float r, T *dst, int n, int lane) {
   constexpr int W = Vec<T>::W;
   typedef typename Vec<T>::type V;
-  for (int i = lane * W; i < n; i += 64 * W) {
+  for (int i = lane * W; i < n; i += 64 * WPR * W) {
     const V v = *reinterpret_cast<const V *>(p + i);
     V o;
 #pragma unroll
@@ -46,23 +48,41 @@ __device__ __forceinline__ void scaled(const T *p, const float *beta, float r, T
 }
 }  // namespace
 
-template <class T>
+// WPR waves per token row (1 for long inputs, 4 when there are few rows);
+// 256 threads per workgroup
+template <class T, int WPR>
 __global__ void __launch_bounds__(256) norm_fuse(NormArgs a) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= a.rows) return;
-  const T *o = reinterpret_cast<const T *>(a.o) + (size_t)row * a.Wa;
-  const T *y = reinterpret_cast<const T *>(a.y) + (size_t)row * a.D;
-  T *f = reinterpret_cast<T *>(a.f) + (size_t)row * (a.Wa + a.D);
-  const float ro = 1.0f / sqrtf(sumsq(o, a.Wa, lane) / (float)a.Wa + a.eps);
-  const float ry = 1.0f / sqrtf(sumsq(y, a.D, lane) / (float)a.D + a.eps);
-  scaled(o, a.beta_attn, ro, f, a.Wa, lane);
-  scaled(y, a.beta_ssm, ry, f + a.Wa, a.D, lane);
+  __shared__ float part[4][2];
+  const int wave = threadIdx.x >> 6;
+  const int row = blockIdx.x * (4 / WPR) + wave / WPR;
+  const int lane = (wave % WPR) * 64 + (threadIdx.x & 63);
+  const bool live = row < a.rows;
+  const int r = live ? row : 0;
+  const T *o = reinterpret_cast<const T *>(a.o) + (size_t)r * a.Wa;
+  const T *y = reinterpret_cast<const T *>(a.y) + (size_t)r * a.D;
+  T *f = reinterpret_cast<T *>(a.f) + (size_t)r * (a.Wa + a.D);
+  float so = sumsq<T, WPR>(o, a.Wa, lane);
+  float sy = sumsq<T, WPR>(y, a.D, lane);
+  if (WPR > 1) {
+    if ((threadIdx.x & 63) == 0) { part[wave][0] = so; part[wave][1] = sy; }
+    __syncthreads();
+    so = 0.0f; sy = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WPR; ++w) { so += part[w][0]; sy += part[w][1]; }
+  }
+  if (!live) return;
+  const float ro = 1.0f / sqrtf(so / (float)a.Wa + a.eps);
+  const float ry = 1.0f / sqrtf(sy / (float)a.D + a.eps);
+  scaled<T, WPR>(o, a.beta_attn, ro, f, a.Wa, lane);
+  scaled<T, WPR>(y, a.beta_ssm, ry, f + a.Wa, a.D, lane);
 }
 
 template <class T>
 hipError_t launch_norm_fuse(const NormArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(norm_fuse<T>, dim3((a.rows + 3) / 4), dim3(256), 0, s, a);
+  if (a.rows < 2048)
+    hipLaunchKernelGGL((norm_fuse<T, 4>), dim3(a.rows), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((norm_fuse<T, 1>), dim3((a.rows + 3) / 4), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 template hipError_t launch_norm_fuse<float>(const NormArgs &, hipStream_t);
