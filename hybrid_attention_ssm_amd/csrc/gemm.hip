@@ -162,15 +162,18 @@ gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int
   __syncthreads();
 
   constexpr int SROW = Cfg::WN + 8;
-  constexpr int LPR = Cfg::WN / 8;
+  constexpr int LPR = Cfg::WN / 8;   // lanes per row; each stores two groups of 4 columns
   constexpr int RPI = 64 / LPR;
   static_assert(Cfg::NWAVES * 32 * SROW * 4 <= (int)sizeof(smem), "epilogue strip fits");
   float *strip = reinterpret_cast<float *>(smem) + wave * 32 * SROW;
-  // a lane stores the same 8 columns for every row: resolve them once
-  const int cc = (lane % LPR) * 8;
-  const int gcol = n0 + wn * Cfg::WN + cc;
-  const bool col_ok = gcol < N;
-  const typename Epi::Col ci = epi.col_info(col_ok ? gcol : 0);
+  // a lane stores columns c0..c0+3 and WN/2+c0..+3 of every row it visits, so
+  // each store instruction writes one contiguous run per row; the routing of
+  // both groups is resolved once
+  const int c0 = (lane % LPR) * 4, c1 = Cfg::WN / 2 + c0;
+  const int g0 = n0 + wn * Cfg::WN + c0, g1 = n0 + wn * Cfg::WN + c1;
+  const bool ok0 = g0 < N, ok1 = g1 < N;
+  const typename Epi::template Col<4> ci0 = epi.template col_info<4>(ok0 ? g0 : 0);
+  const typename Epi::template Col<4> ci1 = epi.template col_info<4>(ok1 ? g1 : 0);
 #pragma unroll
   for (int i = 0; i < Cfg::TM; ++i) {
 #pragma unroll
@@ -182,11 +185,14 @@ gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int
 #pragma unroll 1
     for (int it = 0; it < 32 / RPI; ++it) {
       const int rr = it * RPI + lane / LPR;
-      const float4 a = *reinterpret_cast<const float4 *>(strip + rr * SROW + cc);
-      const float4 b = *reinterpret_cast<const float4 *>(strip + rr * SROW + cc + 4);
-      const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      const float4 a = *reinterpret_cast<const float4 *>(strip + rr * SROW + c0);
+      const float4 b = *reinterpret_cast<const float4 *>(strip + rr * SROW + c1);
+      const float va[4] = {a.x, a.y, a.z, a.w}, vb[4] = {b.x, b.y, b.z, b.w};
       const int row = m0 + wm * Cfg::WM + i * 32 + rr;
-      if (row < M && col_ok) epi.store8(row, ci, v);
+      if (row < M) {
+        if (ok0) epi.template store<4>(row, ci0, va);
+        if (ok1) epi.template store<4>(row, ci1, vb);
+      }
     }
     __syncthreads();
   }
@@ -244,16 +250,21 @@ gemm_f32_tiled(const float *__restrict__ A, const float *__restrict__ B, int M, 
 // ---------------------------------------------------------------------------
 // epilogues and launchers
 // ---------------------------------------------------------------------------
+// Epilogue interface: col_info<W>(col) resolves, once per lane, a group of W
+// consecutive output columns (col % W == 0); store<W>(row, info, v) writes
+// the group's W values of one row.
 template <class T>
 struct InProjEpi {
   InProjOut e;
   __device__ __forceinline__ void operator()(int row, int col, float v) const {
     inproj_store<T>(e, row, col, v);
   }
-  typedef ColInfo Col;
-  __device__ __forceinline__ Col col_info(int col) const { return inproj_col(e, col); }
-  __device__ __forceinline__ void store8(int row, const Col &ci, const float v[8]) const {
-    inproj_store8<T>(e, row, ci, v);
+  template <int W> using Col = ColInfo<W>;
+  template <int W>
+  __device__ __forceinline__ Col<W> col_info(int col) const { return inproj_col<W>(e, col); }
+  template <int W>
+  __device__ __forceinline__ void store(int row, const Col<W> &ci, const float v[W]) const {
+    inproj_storeW<T, W>(e, row, ci, v);
   }
 };
 
@@ -264,10 +275,12 @@ struct StoreEpi {
   __device__ __forceinline__ void operator()(int row, int col, float v) const {
     out[(size_t)row * ld + col] = from_f32<T>(v);
   }
-  typedef int Col;
-  __device__ __forceinline__ Col col_info(int col) const { return col; }
-  __device__ __forceinline__ void store8(int row, const Col &col, const float v[8]) const {
-    store8_T(out + (size_t)row * ld + col, v);
+  template <int W> using Col = int;
+  template <int W>
+  __device__ __forceinline__ int col_info(int col) const { return col; }
+  template <int W>
+  __device__ __forceinline__ void store(int row, int col, const float v[W]) const {
+    storeW_T<T, W>(out + (size_t)row * ld + col, v);
   }
 };
 
@@ -276,10 +289,12 @@ struct StoreEpi {
 struct PartialEpi {
   float *part;
   int M, N;
-  typedef int Col;
-  __device__ __forceinline__ Col col_info(int col) const { return col; }
-  __device__ __forceinline__ void store8(int row, const Col &col, const float v[8]) const {
-    store8_T(part + ((size_t)blockIdx.y * M + row) * N + col, v);
+  template <int W> using Col = int;
+  template <int W>
+  __device__ __forceinline__ int col_info(int col) const { return col; }
+  template <int W>
+  __device__ __forceinline__ void store(int row, int col, const float v[W]) const {
+    storeW_T<float, W>(part + ((size_t)blockIdx.y * M + row) * N + col, v);
   }
 };
 
@@ -298,7 +313,7 @@ reduce_splits(const float *__restrict__ part, int splits, int M, int N, Epi epi)
     v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
     v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
   }
-  epi.store8(row, epi.col_info(col), v);
+  epi.template store<8>(row, epi.template col_info<8>(col), v);
 }
 
 template <class Cfg, class Epi>

@@ -138,18 +138,37 @@ __device__ __forceinline__ void store8_T(T *dst, const float v[8]) {
   }
 }
 
-// Column-side part of an 8-column group (col % 8 == 0), resolved once per
-// lane: which block of the map the columns fall in, the offset inside it and,
-// for the Delta block, the biases.
+// Store W (4 or 8) consecutive values (converted to T).
+template <class T, int W>
+__device__ __forceinline__ void storeW_T(T *dst, const float v[W]) {
+  if constexpr (W == 8) {
+    store8_T(dst, v);
+  } else if constexpr (sizeof(T) == 2) {
+    typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+    bf16x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (bf16)v[e];
+    *reinterpret_cast<bf16x4 *>(dst) = o;
+  } else {
+    *reinterpret_cast<float4 *>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+// Column-side part of a group of W consecutive columns (col % W == 0; no
+// block boundary inside a group), resolved once per lane: which block of the
+// map the columns fall in, the offset inside it and, for the Delta block,
+// the biases.
+template <int W>
 struct ColInfo {
   int seg;       // 0 Q, 1 K, 2 V, 3 xs, 4 z, 5 dt, 6 B|C
   int c;         // column offset inside the block
   int g, d;      // K/V: head and position inside the head
-  float bias[8];
+  float bias[W];
 };
 
-__device__ __forceinline__ ColInfo inproj_col(const InProjOut &e, int col) {
-  ColInfo ci{};
+template <int W>
+__device__ __forceinline__ ColInfo<W> inproj_col(const InProjOut &e, int col) {
+  ColInfo<W> ci{};
   const int Wa = e.Wa, KV = e.KV, D = e.D;
   if (col < Wa) { ci.seg = 0; ci.c = col; return ci; }
   col -= Wa;
@@ -167,22 +186,23 @@ __device__ __forceinline__ ColInfo inproj_col(const InProjOut &e, int col) {
   col -= D;
   if (col < D) {
     ci.seg = 5; ci.c = col;
-    const float4 b0 = *reinterpret_cast<const float4 *>(e.dt_bias + col);
-    const float4 b1 = *reinterpret_cast<const float4 *>(e.dt_bias + col + 4);
-    ci.bias[0] = b0.x; ci.bias[1] = b0.y; ci.bias[2] = b0.z; ci.bias[3] = b0.w;
-    ci.bias[4] = b1.x; ci.bias[5] = b1.y; ci.bias[6] = b1.z; ci.bias[7] = b1.w;
+#pragma unroll
+    for (int q = 0; q < W / 4; ++q) {
+      const float4 bq = *reinterpret_cast<const float4 *>(e.dt_bias + col + 4 * q);
+      ci.bias[4 * q] = bq.x; ci.bias[4 * q + 1] = bq.y; ci.bias[4 * q + 2] = bq.z; ci.bias[4 * q + 3] = bq.w;
+    }
     return ci;
   }
   ci.seg = 6; ci.c = col - D;
   return ci;
 }
 
-template <class T>
-__device__ __forceinline__ void inproj_store8(const InProjOut &e, int row, const ColInfo &ci,
-                                              const float v[8]) {
+template <class T, int W>
+__device__ __forceinline__ void inproj_storeW(const InProjOut &e, int row, const ColInfo<W> &ci,
+                                              const float v[W]) {
   const int Wa = e.Wa, D = e.D;
   switch (ci.seg) {
-    case 0: store8_T(reinterpret_cast<T *>(e.q) + (size_t)row * Wa + ci.c, v); return;
+    case 0: storeW_T<T, W>(reinterpret_cast<T *>(e.q) + (size_t)row * Wa + ci.c, v); return;
     case 1:
     case 2: {
       const bool isv = ci.seg == 2;
@@ -192,33 +212,33 @@ __device__ __forceinline__ void inproj_store8(const InProjOut &e, int row, const
         if (p < 0 || (!e.is_ring && p >= e.cap)) return;
         const int slot = e.is_ring ? p % e.cap : p;
         T *dst = reinterpret_cast<T *>(isv ? e.cache_v : e.cache_k);
-        store8_T(dst + (((size_t)row * G + ci.g) * e.cap + slot) * e.hd + ci.d, v);
+        storeW_T<T, W>(dst + (((size_t)row * G + ci.g) * e.cap + slot) * e.hd + ci.d, v);
         return;
       }
       const int n = e.n_rows_per_seq;
       const int b = row / n, p = row - b * n;
       T *full = reinterpret_cast<T *>(isv ? e.v_full : e.k_full);
-      store8_T(full + (((size_t)b * G + ci.g) * n + p) * e.hd + ci.d, v);
+      storeW_T<T, W>(full + (((size_t)b * G + ci.g) * n + p) * e.hd + ci.d, v);
       if (e.mode == EPI_PREFILL && e.cache_k) {
         const bool keep = e.is_ring ? (p >= n - e.cap) : (p < e.cap);
         if (keep) {
           const int slot = e.is_ring ? p % e.cap : p;
           T *dst = reinterpret_cast<T *>(isv ? e.cache_v : e.cache_k);
-          store8_T(dst + (((size_t)b * G + ci.g) * e.cap + slot) * e.hd + ci.d, v);
+          storeW_T<T, W>(dst + (((size_t)b * G + ci.g) * e.cap + slot) * e.hd + ci.d, v);
         }
       }
       return;
     }
-    case 3: store8_T(e.xs + (size_t)row * D + ci.c, v); return;
-    case 4: store8_T(reinterpret_cast<T *>(e.z) + (size_t)row * D + ci.c, v); return;
+    case 3: storeW_T<float, W>(e.xs + (size_t)row * D + ci.c, v); return;
+    case 4: storeW_T<T, W>(reinterpret_cast<T *>(e.z) + (size_t)row * D + ci.c, v); return;
     case 5: {
-      float sp[8];
+      float sp[W];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sp[i] = softplus_f(v[i] + ci.bias[i]);
-      store8_T(e.dt + (size_t)row * D + ci.c, sp);
+      for (int i = 0; i < W; ++i) sp[i] = softplus_f(v[i] + ci.bias[i]);
+      storeW_T<float, W>(e.dt + (size_t)row * D + ci.c, sp);
       return;
     }
-    default: store8_T(e.bc + (size_t)row * 2 * e.N + ci.c, v); return;
+    default: storeW_T<float, W>(e.bc + (size_t)row * 2 * e.N + ci.c, v); return;
   }
 }
 
