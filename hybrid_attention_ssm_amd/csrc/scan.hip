@@ -97,26 +97,46 @@ __device__ __forceinline__ void scan_range(const ScanArgs &a, int b, int c, bool
   const float *xs = a.xs;
   const T *z = reinterpret_cast<const T *>(a.z);
   T *y = reinterpret_cast<T *>(a.y);
+  // without Y the gate is not needed: read (and ignore) xs instead, so the
+  // loads stay unconditional
+  const T *zp = y ? z : reinterpret_cast<const T *>(xs);
   const size_t D = a.D;
   const size_t row0 = (size_t)b * a.n;
   const int lane = threadIdx.x;
   for (int s0 = t0; s0 < t1; s0 += SUB) {
     const int len = min(SUB, t1 - s0);
     __syncthreads();   // previous block's reads are done
+    // all loads first, then the LDS writes (indices past the block repeat
+    // its last vector, so every load is unconditional)
     const float4 *src = reinterpret_cast<const float4 *>(a.bc + (row0 + s0) * (2 * NS));
-    for (int i = lane; i < len * (2 * NS / 4); i += 64)
-      reinterpret_cast<float4 *>(sbc)[i] = src[i];
+    constexpr int PER_LANE = SUB * (2 * NS / 4) / 64;
+    const int last = len * (2 * NS / 4) - 1;
+    float4 stage[PER_LANE];
+#pragma unroll
+    for (int j = 0; j < PER_LANE; ++j) stage[j] = src[min(lane + 64 * j, last)];
+#pragma unroll
+    for (int j = 0; j < PER_LANE; ++j) reinterpret_cast<float4 *>(sbc)[min(lane + 64 * j, last)] = stage[j];
     __syncthreads();
     int t = 0;
-    for (; t + TB <= len; t += TB) {
-      float xv[TB], dv[TB], zv[TB];
+    // per-lane inputs of batch t are loaded one batch ahead (the loads of
+    // batch t+TB are in flight while batch t is computed); the prefetch past
+    // the last full batch re-reads that batch (a cache hit)
+    float xv[TB], dv[TB];
+    T zv[TB];
+    auto load_batch = [&](int tb, float (&xo)[TB], float (&dvo)[TB], T (&zo)[TB]) {
 #pragma unroll
       for (int i = 0; i < TB; ++i) {
-        const size_t idx = (row0 + s0 + t + i) * D + c;
-        xv[i] = xs[idx];
-        dv[i] = a.dt[idx];
-        if (MODE == 1) zv[i] = y ? to_f32(z[idx]) : 0.0f;
+        const size_t idx = (row0 + s0 + tb + i) * D + c;
+        xo[i] = xs[idx];
+        dvo[i] = a.dt[idx];
+        if (MODE == 1) zo[i] = zp[idx];
       }
+    };
+    if (TB <= len) load_batch(0, xv, dv, zv);
+    for (; t + TB <= len; t += TB) {
+      float xn[TB], dn[TB];
+      T zn[TB];
+      load_batch(t + 2 * TB <= len ? t + TB : t, xn, dn, zn);
 #pragma unroll
       for (int i = 0; i < TB; ++i) {
         const float4 *bc4 = reinterpret_cast<const float4 *>(sbc + (t + i) * 2 * NS);
@@ -131,8 +151,11 @@ __device__ __forceinline__ void scan_range(const ScanArgs &a, int b, int c, bool
           }
         }
         const float acc = scan_step<MODE>(p, h, hist, xv[i], dv[i], bv, cv, dsum);
-        if (MODE == 1 && y && active) y[(row0 + s0 + t + i) * D + c] = from_f32<T>(acc * silu_f(zv[i]));
+        if (MODE == 1 && y && active)
+          y[(row0 + s0 + t + i) * D + c] = from_f32<T>(acc * silu_f(to_f32(zv[i])));
       }
+#pragma unroll
+      for (int i = 0; i < TB; ++i) { xv[i] = xn[i]; dv[i] = dn[i]; zv[i] = zn[i]; }
     }
     for (; t < len; ++t) {
       const size_t idx = (row0 + s0 + t) * D + c;
