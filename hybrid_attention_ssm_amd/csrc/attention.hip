@@ -50,11 +50,15 @@ constexpr int ASTAGES = 3;
 constexpr int TILE_UNITS = BKV * HD / 8;     // 512 16-byte units per K (or V) tile
 
 template <int NW>
-__global__ void __launch_bounds__(NW * 64, 2)
+// 4 waves per SIMD (at most 128 VGPRs): three 48 KB workgroups per CU
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
 attn_prefill_bf16(AttnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __shared__ uint4 sK[ASTAGES][TILE_UNITS];
-  __shared__ uint4 sV[ASTAGES][TILE_UNITS];
+  // one LDS array per stage: reads of one stage then provably do not alias the
+  // DMA into another, so the compiler waits only for the tile being read
+  __shared__ uint4 sK0[TILE_UNITS], sK1[TILE_UNITS], sK2[TILE_UNITS];
+  __shared__ uint4 sV0[TILE_UNITS], sV1[TILE_UNITS], sV2[TILE_UNITS];
+  static_assert(ASTAGES == 3, "three stage arrays");
 
   const int nqt = (a.n + BQ - 1) / BQ;
   const int qt = nqt - 1 - (int)blockIdx.x;  // heaviest (latest) query tiles first
@@ -108,7 +112,7 @@ attn_prefill_bf16(AttnArgs a) {
     const int row = u >> 3, c = (u & 7) ^ ((row >> 1) & 7);
     voff[j] = row * HD * 2 + c * 16;
   }
-  auto issue = [&](int t, int st) {
+  auto issue = [&](int t, uint4 *dK, uint4 *dV) {
     if (!loader) return;
     const bool meta = t < n_meta_t;
     const int kbase = meta ? t * BKV : (t_lo + t - n_meta_t) * BKV;
@@ -120,11 +124,11 @@ attn_prefill_bf16(AttnArgs a) {
         __builtin_amdgcn_make_buffer_rsrc((void *)(meta ? Vm : Vr), (short)0, bytes, 0x00020000);
 #pragma unroll
     for (int j = 0; j < KI; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(sK[st] + part[j] * 64), 16, voff[j],
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(dK + part[j] * 64), 16, voff[j],
                                                kbase * HD * 2, 0, 0);
 #pragma unroll
     for (int j = 0; j < KI; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(sV[st] + part[j] * 64), 16, voff[j],
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(dV + part[j] * 64), 16, voff[j],
                                                kbase * HD * 2, 0, 0);
   };
   // ds_read_b64_tr_b16 source offsets (bytes) inside a V tile for
@@ -144,27 +148,19 @@ attn_prefill_bf16(AttnArgs a) {
       }
 
   const float sl2 = kLog2e * rsqrtf((float)HD);
+  // Online softmax with a lazily updated maximum: probabilities are taken as
+  // 2^(s*sl2 - m_run) and m_run (with the O rescale) only moves when some
+  // lane's tile maximum exceeds it by more than 2^8, so most tiles skip the
+  // rescale; the probabilities stay below 2^8 and the result is unchanged.
+  constexpr float kLazy = 8.0f;
   float m_run = -INFINITY, l_run = 0.0f;
   f32x16 o[2];
 #pragma unroll
   for (int r = 0; r < 16; ++r) { o[0][r] = 0.0f; o[1][r] = 0.0f; }
 
-  const int tlast = n_tiles - 1;
-#pragma unroll
-  for (int st = 0; st < ASTAGES - 1; ++st) issue(min(st, tlast), st);
-  for (int t = 0; t < n_tiles; ++t) {
-    // this wave's DMA for tile t has landed (later tiles may still be in flight) ...
-    wait_vmcnt<(ASTAGES - 2) * INS>();
-    __builtin_amdgcn_s_barrier();   // ... and every wave's; stage (t-1) is free
-    __builtin_amdgcn_sched_barrier(0);
-    {
-      const int nt = t + ASTAGES - 1;
-      issue(min(nt, tlast), nt % ASTAGES);
-    }
-    const int st = t % ASTAGES;
+  auto body = [&](int t, const uint4 *sK, const uint4 *sV) {
     const bool meta = t < n_meta_t;
     const int kbase = meta ? t * BKV : (t_lo + t - n_meta_t) * BKV;
-
     f32x16 s[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
@@ -172,7 +168,7 @@ attn_prefill_bf16(AttnArgs a) {
       for (int r = 0; r < 16; ++r) s[blk][r] = 0.0f;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, sK[st][swz(blk * 32 + lr, kk * 2 + lh)]);
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, sK[swz(blk * 32 + lr, kk * 2 + lh)]);
         s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[blk], 0, 0, 0);
       }
     }
@@ -180,42 +176,45 @@ attn_prefill_bf16(AttnArgs a) {
     if (meta) need_mask = kbase + BKV > a.m;
     else need_mask = (kbase + BKV - 1 > q0) || (kbase + BKV > a.n) ||
                      (!a.is_global && kbase < q0 + BQ - 1 - a.window + 1);
-    float mx = -INFINITY;
+    if (need_mask) {
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+      for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[blk][r] * sl2;
-        if (need_mask) {
+        for (int r = 0; r < 16; ++r) {
           const int key = kbase + blk * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
           bool ok;
           if (meta) ok = key < a.m;
           else ok = key < a.n && key <= qpos && (a.is_global || qpos - key < a.window);
-          x = ok ? x : -INFINITY;
+          s[blk][r] = ok ? s[blk][r] : -INFINITY;
         }
-        s[blk][r] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = wave_max32(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = exp2_fast(m_run - m_use);
+    }
+    float mx = -INFINITY;   // raw scores: sl2 > 0 keeps the order
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[blk][r]);
+    mx = wave_max32(mx) * sl2;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = exp2_fast(m_run - (m_new == -INFINITY ? 0.0f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { o[0][r] *= alpha; o[1][r] *= alpha; }
+      m_run = m_new;
+    }
+    const float neg_m = m_run == -INFINITY ? 0.0f : -m_run;
     float rs = 0.0f;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2_fast(s[blk][r] - m_use);
+        const float p = exp2_fast(fmaf(s[blk][r], sl2, neg_m));
         s[blk][r] = p;
         rs += p;
       }
-    rs = wave_sum32(rs);
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { o[0][r] *= alpha; o[1][r] *= alpha; }
+    l_run += wave_sum32(rs);
     typedef short v4i16 __attribute__((ext_vector_type(4)));
-    const char *vbase = reinterpret_cast<const char *>(sV[st]);
+    const char *vbase = reinterpret_cast<const char *>(sV);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       bf16x8 pb;
@@ -233,7 +232,27 @@ attn_prefill_bf16(AttnArgs a) {
         o[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[dblk], 0, 0, 0);
       }
     }
+  };
+
+  const int tlast = n_tiles - 1;
+  issue(0, sK0, sV0);
+  issue(min(1, tlast), sK1, sV1);
+  // tile t lives in stage t % 3; each step waits for its own tile, then (after
+  // the barrier frees the stage read one step earlier) issues tile t + 2
+#define HH_ATTN_STEP(KC, VC, KN, VN)                                    \
+  wait_vmcnt<(ASTAGES - 2) * INS>();                                   \
+  __builtin_amdgcn_s_barrier();                                        \
+  __builtin_amdgcn_sched_barrier(0);                                   \
+  issue(min(t + 2, tlast), KN, VN);                                    \
+  body(t, KC, VC);                                                     \
+  if (++t >= n_tiles) break;
+  for (int t = 0;;) {
+    HH_ATTN_STEP(sK0, sV0, sK2, sV2)
+    HH_ATTN_STEP(sK1, sV1, sK0, sV0)
+    HH_ATTN_STEP(sK2, sV2, sK1, sV1)
   }
+#undef HH_ATTN_STEP
+  wait_vmcnt<0>();   // the repeated last prefetches, before the workgroup ends
 
   if (qpos < a.n) {
     const float inv = 1.0f / l_run;
