@@ -116,14 +116,22 @@ gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+  // fragments: slot ks of k-tile kt (ks = 0, 1: the two 16-deep halves)
   bf16x8 af[2][Cfg::TM], bfr[2][Cfg::TN];
-  auto fload = [&](const uint4 *sA, const uint4 *sB, int ks, int slot) {
+  auto fload = [&](const uint4 *sA, const uint4 *sB, int ks) {
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i)
-      af[slot][i] = __builtin_bit_cast(bf16x8, sA[swz4(wm * Cfg::WM + i * 32 + lr, ks * 2 + lh)]);
+      af[ks][i] = __builtin_bit_cast(bf16x8, sA[swz4(wm * Cfg::WM + i * 32 + lr, ks * 2 + lh)]);
 #pragma unroll
     for (int j = 0; j < Cfg::TN; ++j)
-      bfr[slot][j] = __builtin_bit_cast(bf16x8, sB[swz4(wn * Cfg::WN + j * 32 + lr, ks * 2 + lh)]);
+      bfr[ks][j] = __builtin_bit_cast(bf16x8, sB[swz4(wn * Cfg::WN + j * 32 + lr, ks * 2 + lh)]);
+  };
+  auto mfmas = [&](int ks) {
+#pragma unroll
+    for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < Cfg::TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
   };
 
   // split-K: slice blockIdx.y of gridDim.y covers k-tiles [kt0, kt0 + ktiles)
@@ -132,31 +140,33 @@ gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int
   const int kt0 = blockIdx.y * kps;
   const int ktiles = max(0, min(ktiles_all - kt0, kps));
   auto ktile = [&](int i) { return kt0 + min(i, ktiles - 1); };   // steps past the end repeat the last
+  auto stage = [&](int kt) { return smem + (kt % Cfg::STAGES) * Cfg::STAGE; };
+  constexpr int PER_TILE = Cfg::A_INS + Cfg::B_INS;
+  // Software pipeline per k-tile kt (its stage holds tile kt):
+  //   read the ks=1 fragments of kt, multiply ks=0 (read one step earlier),
+  //   refill the stage of tile kt-1 with tile kt+STAGES-1 (every wave passed
+  //   the barrier after its last read of it), multiply ks=1, then wait for
+  //   tile kt+1, barrier, and read its ks=0 fragments while the MFMAs drain.
 #pragma unroll
   for (int st = 0; st < Cfg::STAGES - 1; ++st) issue(ktile(st), st);
-  constexpr int PER_TILE = Cfg::A_INS + Cfg::B_INS;
+  wait_vmcnt<(Cfg::STAGES - 2) * PER_TILE>();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  fload(stage(0), stage(0) + Cfg::A_UNITS, 0);
   for (int kt = 0; kt < ktiles; ++kt) {
-    wait_vmcnt<(Cfg::STAGES - 2) * PER_TILE>();   // this wave's loads of tile kt have landed
-    __builtin_amdgcn_s_barrier();               // ... and every other wave's
+    const uint4 *sA = stage(kt);
+    fload(sA, sA + Cfg::A_UNITS, 1);
+    mfmas(0);
     __builtin_amdgcn_sched_barrier(0);
-    // refill the stage every wave finished reading before this barrier
     const int nt = kt + Cfg::STAGES - 1;
     issue(ktile(nt), nt % Cfg::STAGES);
-    const uint4 *sA = smem + (kt % Cfg::STAGES) * Cfg::STAGE;
-    const uint4 *sB = sA + Cfg::A_UNITS;
-    fload(sA, sB, 0, 0);
+    mfmas(1);
     __builtin_amdgcn_sched_barrier(0);
-    fload(sA, sB, 1, 1);
+    wait_vmcnt<(Cfg::STAGES - 2) * PER_TILE>();   // this wave's loads of tile kt+1 have landed
+    __builtin_amdgcn_s_barrier();               // ... and every other wave's
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int i = 0; i < Cfg::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < Cfg::TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    const uint4 *sN = stage(kt + 1);
+    fload(sN, sN + Cfg::A_UNITS, 0);            // (past the last tile: a harmless re-read)
   }
   wait_vmcnt<0>();
   __syncthreads();
