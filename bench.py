@@ -251,7 +251,7 @@ def cpu_baseline(pre, dec, args):
         ref.prefill(dims.as_dict(), inp["weights"], inp["R"], inp["x"][:, :ns], pre["W"], False)
         dt = time.perf_counter() - t0
         res["prefill"] = dict(value=ns / dt, seconds=dt,
-                              sample=f"oracle prefill of the first {ns} of the 8192 tokens "
+                              sample=f"oracle prefill of {ns} of the 8192 tokens "
                                      f"(same layer, meta rows included), fp64")
     if dec is not None:
         from hybrid_attention_ssm_amd.configs import CFG3_DECODE
@@ -275,7 +275,16 @@ def cpu_baseline(pre, dec, args):
                              sample=f"oracle decode step (3 layers) for {len(S)} of the 128 "
                                     f"sequences, fp64")
     res["cores"] = threads
-    res["cpu"] = platform.processor() or platform.machine()
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    res["cpu"] = cpu
     return res
 
 
@@ -286,8 +295,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["prefill", "decode", "both"], default="both")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
-    ap.add_argument("--cpu-sample-seqs", type=int, default=4)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=8192,
+                    help="prefill tokens the CPU oracle runs (default: the whole 8k workload)")
+    ap.add_argument("--cpu-sample-seqs", type=int, default=64,
+                    help="decode sequences the CPU oracle steps (of 128)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (the known-size kernel "
                          "that scales the HBM byte counters) and exit")
@@ -357,13 +368,13 @@ def main():
         if "decode_attention_global" in st:
             cnt, tot = st["decode_attention_global"]
             ach = dec["global_attn_bytes"] / (tot / cnt * 1e-3)
-            tr = measured_traffic("decode_attn_mfma", dec["workload"])
-            d["roofline"] = {"kernel": "decode attention of the global layer (decode_attn_mfma + "
+            tr = measured_traffic("decode_attn_dma", dec["workload"])
+            d["roofline"] = {"kernel": "decode attention of the global layer (decode_attn_dma + "
                                        "decode_attn_combine)",
                              "bound": "hbm", "achieved": ach / 1e9, "peak": HBM_PEAK / 1e9,
                              "unit": "GB/s", "frac": ach / HBM_PEAK,
                              "traffic": tr["bytes"] if tr else None,
-                             "traffic_unit": "HBM bytes per launch of decode_attn_mfma "
+                             "traffic_unit": "HBM bytes per launch of decode_attn_dma "
                                              "(FETCH_SIZE + WRITE_SIZE)",
                              "traffic_detail": tr,
                              "bytes_per_launch": dec["global_attn_bytes"],
