@@ -28,8 +28,12 @@ def np_of(t: torch.Tensor) -> np.ndarray:
 
 
 def run_meta_prefix(dims: LayerDims, weights: dict, R: np.ndarray):
+    """hh_meta_prefix of the layer (with no meta tokens: no meta K/V, and the
+    SSM state and conv history start from zero)."""
     sd = hb.storage_dtype(dims)
     layer = hb.upload_weights(dims, weights)
+    if dims.n_meta == 0:
+        return layer, dict(k=None, v=None, h0=None, conv_tail=None)
     meta = hb.hh_meta_prefix(layer, hb.to_device(R, sd))
     torch.cuda.synchronize()
     return layer, meta
