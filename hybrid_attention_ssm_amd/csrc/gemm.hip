@@ -40,25 +40,28 @@ __device__ __forceinline__ bool tile_of(int tiles_m, int tiles_n, int &tm, int &
 // reads STAGES-1 tiles of MFMA time to land.  Waits and barriers are explicit
 // (s_waitcnt vmcnt + s_barrier) so nothing drains the load pipeline.
 // ---------------------------------------------------------------------------
-template <int BM_, int BN_, int WM_, int WN_, int STAGES_>
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_, int BK_ = 32>
 struct LdsCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
-  static constexpr int BK = 32;                      // bf16 per k-tile row (64 B)
+  static constexpr int BK = BK_;                     // bf16 per k-tile row (32 or 64)
+  static constexpr int KCH = BK / 8;                 // 16-byte chunks per row
+  static constexpr int KS = BK / 16;                 // MFMA k-steps per k-tile
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
   static constexpr int NWAVES = WAVES_M * WAVES_N;
   static constexpr int NT = NWAVES * 64;
   static constexpr int TM = WM / 32, TN = WN / 32;
-  static constexpr int A_UNITS = BM * 4, B_UNITS = BN * 4;   // 16-byte units
+  static constexpr int A_UNITS = BM * KCH, B_UNITS = BN * KCH;   // 16-byte units
   static constexpr int STAGE = A_UNITS + B_UNITS;
   static constexpr int A_INS = A_UNITS / 64 / NWAVES;        // load instrs per wave
   static constexpr int B_INS = B_UNITS / 64 / NWAVES;
+  static_assert(BK == 32 || BK == 64, "k-tile");
   static_assert(A_INS * 64 * NWAVES == A_UNITS && B_INS * 64 * NWAVES == B_UNITS, "tile");
+  // chunk c of row `row` sits at slot c ^ f(row): the 16 (32) rows one
+  // fragment read touches with the same c land on distinct 16-byte bank groups
+  __device__ static __forceinline__ int swz(int row, int c) {
+    return BK == 32 ? row * 4 + (c ^ ((row >> 2) & 3)) : row * 8 + (c ^ ((row >> 1) & 7));
+  }
 };
-
-// slot of 16-byte chunk c (0..3) of 64-byte row `row`: 16 rows read with the
-// same c land on 16 distinct 16-byte bank groups
-__device__ __forceinline__ int swz4(int row, int c) { return row * 4 + (c ^ ((row >> 2) & 3)); }
-
 
 template <class Cfg, class Epi>
 __global__ void __launch_bounds__(Cfg::NT)
@@ -82,15 +85,15 @@ gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int
       (void *)(B + (size_t)n0 * K), (short)0, (N - n0) * K * 2, 0x00020000);
   int voffA[Cfg::A_INS], voffB[Cfg::B_INS];
 #pragma unroll
-  for (int j = 0; j < Cfg::A_INS; ++j) {
+  for (int j = 0; j < Cfg::A_INS; ++j) {   // LDS unit u holds chunk of swz(row, kc) == u
     const int u = (wave * Cfg::A_INS + j) * 64 + lane;
-    const int row = u >> 2, kc = (u & 3) ^ ((row >> 2) & 3);
+    const int row = u / Cfg::KCH, kc = Cfg::swz(row, u % Cfg::KCH) - row * Cfg::KCH;
     voffA[j] = (row * K + kc * 8) * 2;
   }
 #pragma unroll
   for (int j = 0; j < Cfg::B_INS; ++j) {
     const int u = (wave * Cfg::B_INS + j) * 64 + lane;
-    const int row = u >> 2, kc = (u & 3) ^ ((row >> 2) & 3);
+    const int row = u / Cfg::KCH, kc = Cfg::swz(row, u % Cfg::KCH) - row * Cfg::KCH;
     voffB[j] = (row * K + kc * 8) * 2;
   }
   typedef __attribute__((address_space(3))) void lds_void;
@@ -116,22 +119,23 @@ gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // fragments: slot ks of k-tile kt (ks = 0, 1: the two 16-deep halves)
+  // fragments of k-step ks (16 deep) sit in buffer ks % 2
   bf16x8 af[2][Cfg::TM], bfr[2][Cfg::TN];
-  auto fload = [&](const uint4 *sA, const uint4 *sB, int ks) {
+  auto fload = [&](const uint4 *sA, int ks) {
+    const uint4 *sB = sA + Cfg::A_UNITS;
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i)
-      af[ks][i] = __builtin_bit_cast(bf16x8, sA[swz4(wm * Cfg::WM + i * 32 + lr, ks * 2 + lh)]);
+      af[ks & 1][i] = __builtin_bit_cast(bf16x8, sA[Cfg::swz(wm * Cfg::WM + i * 32 + lr, ks * 2 + lh)]);
 #pragma unroll
     for (int j = 0; j < Cfg::TN; ++j)
-      bfr[ks][j] = __builtin_bit_cast(bf16x8, sB[swz4(wn * Cfg::WN + j * 32 + lr, ks * 2 + lh)]);
+      bfr[ks & 1][j] = __builtin_bit_cast(bf16x8, sB[Cfg::swz(wn * Cfg::WN + j * 32 + lr, ks * 2 + lh)]);
   };
   auto mfmas = [&](int ks) {
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i)
 #pragma unroll
       for (int j = 0; j < Cfg::TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j], acc[i][j], 0, 0, 0);
   };
 
   // split-K: slice blockIdx.y of gridDim.y covers k-tiles [kt0, kt0 + ktiles)
@@ -142,31 +146,34 @@ gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int
   auto ktile = [&](int i) { return kt0 + min(i, ktiles - 1); };   // steps past the end repeat the last
   auto stage = [&](int kt) { return smem + (kt % Cfg::STAGES) * Cfg::STAGE; };
   constexpr int PER_TILE = Cfg::A_INS + Cfg::B_INS;
-  // Software pipeline per k-tile kt (its stage holds tile kt):
-  //   read the ks=1 fragments of kt, multiply ks=0 (read one step earlier),
-  //   refill the stage of tile kt-1 with tile kt+STAGES-1 (every wave passed
-  //   the barrier after its last read of it), multiply ks=1, then wait for
-  //   tile kt+1, barrier, and read its ks=0 fragments while the MFMAs drain.
+  // Software pipeline per k-tile kt (its stage holds tile kt): each k-step's
+  // fragments are read while the previous k-step's MFMAs run; after the
+  // first k-step the stage of tile kt-1 is refilled with tile kt+STAGES-1
+  // (every wave passed the barrier after its last read of it); after the
+  // last k-step wait for tile kt+1, barrier, and read its first fragments
+  // while the MFMAs drain.
 #pragma unroll
   for (int st = 0; st < Cfg::STAGES - 1; ++st) issue(ktile(st), st);
   wait_vmcnt<(Cfg::STAGES - 2) * PER_TILE>();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  fload(stage(0), stage(0) + Cfg::A_UNITS, 0);
+  fload(stage(0), 0);
   for (int kt = 0; kt < ktiles; ++kt) {
     const uint4 *sA = stage(kt);
-    fload(sA, sA + Cfg::A_UNITS, 1);
-    mfmas(0);
-    __builtin_amdgcn_sched_barrier(0);
-    const int nt = kt + Cfg::STAGES - 1;
-    issue(ktile(nt), nt % Cfg::STAGES);
-    mfmas(1);
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < Cfg::KS; ++ks) {
+      if (ks + 1 < Cfg::KS) fload(sA, ks + 1);
+      mfmas(ks);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks == 0) {
+        const int nt = kt + Cfg::STAGES - 1;
+        issue(ktile(nt), nt % Cfg::STAGES);
+      }
+    }
     wait_vmcnt<(Cfg::STAGES - 2) * PER_TILE>();   // this wave's loads of tile kt+1 have landed
     __builtin_amdgcn_s_barrier();               // ... and every other wave's
     __builtin_amdgcn_sched_barrier(0);
-    const uint4 *sN = stage(kt + 1);
-    fload(sN, sN + Cfg::A_UNITS, 0);            // (past the last tile: a harmless re-read)
+    fload(stage(kt + 1), 0);                     // (past the last tile: a harmless re-read)
   }
   wait_vmcnt<0>();
   __syncthreads();
@@ -345,8 +352,10 @@ using CfgLds = LdsCfg<256, 256, 128, 64, 3>;
 // is split too; fp32 partials are then summed by reduce_splits, which applies
 // the epilogue.  `part` holds splits*M*N floats.  (A split input projection
 // loses more to its partial planes and the scattered epilogue of the reduce
-// than it gains.)
-using CfgSkinny = LdsCfg<128, 64, 64, 32, 4>;
+// than it gains.)  Each workgroup re-reads all M rows of the activations from
+// L2, which bounds it; 64-deep k-tiles halve its barriers and double the bytes
+// per DMA batch, and 8 waves of 32x32 keep more loads in flight.
+using CfgSkinny = LdsCfg<128, 64, 32, 32, 4, 64>;
 constexpr int kSkinnyTargetWG = 200;   // workgroups a few-row GEMM aims for
 
 static int skinny_splits(int M, int K, int N) {
