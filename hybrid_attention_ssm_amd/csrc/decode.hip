@@ -401,6 +401,8 @@ __global__ void __launch_bounds__(DTHREADS) decode_attn_dma(DecodeAttnArgs a) {
     }
   };
 
+  int kb = v0 + wave * DB;
+  if (kb < v1) issue(kb, slice0);   // the first block travels with Q
   bf8 qf[2];
   {
     const bf16 *Q = reinterpret_cast<const bf16 *>(a.q) + (size_t)b * a.H * HD;
@@ -411,7 +413,7 @@ __global__ void __launch_bounds__(DTHREADS) decode_attn_dma(DecodeAttnArgs a) {
       qf[hh] = __builtin_bit_cast(bf8, v);
     }
   }
-  wait_vmcnt<0>();   // Q is in registers before the DMA stream starts
+  wait_vmcnt<0>();   // Q (and the first block) have landed before the loop
   const float sl2 = kLog2e * 0.125f;   // log2(e) / sqrt(64)
   float m_run = -INFINITY, l_run = 0.0f;
   f32x4 o[4];
@@ -491,9 +493,7 @@ __global__ void __launch_bounds__(DTHREADS) decode_attn_dma(DecodeAttnArgs a) {
       o[dblk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, both), pb, o[dblk], 0, 0, 0);
     }
   };
-  int kb = v0 + wave * DB;
   if (kb < v1) {
-    issue(kb, slice0);
     while (true) {
       issue(kb + 4 * DB < v1 ? kb + 4 * DB : kb, slice1);
       wait_vmcnt<8>();
@@ -579,9 +579,13 @@ size_t decode_attn_part_bytes(int B, int H, int G, int hd, int m, int max_real, 
 }
 
 template <class T>
-hipError_t launch_decode_attention(const DecodeAttnArgs &a, hipStream_t s) {
+hipError_t launch_decode_attention(const DecodeAttnArgs &a, hipStream_t s, bool defer_combine,
+                                   bool *o_ready) {
   const int hpg = a.H / a.G;
   dim3 grid(a.nsplit, a.G, a.B);
+  // the DMA kernel writes O itself when there is a single split; the others
+  // always leave per-split partials
+  bool direct = false;
   if (sizeof(T) == 2 && a.hd == 64 && a.m % DB == 0 && a.split % DB == 0) {
     switch (hpg) {
 #define HH_DECD_CASE(W) \
@@ -591,10 +595,8 @@ hipError_t launch_decode_attention(const DecodeAttnArgs &a, hipStream_t s) {
 #undef HH_DECD_CASE
       default: return hipErrorInvalidValue;
     }
-    if (a.nsplit > 1) hipLaunchKernelGGL(decode_attn_combine<T>, dim3(a.B * a.H), dim3(64), 0, s, a);
-    return hipGetLastError();
-  }
-  if (sizeof(T) == 2 && a.hd == 64) {
+    direct = a.nsplit == 1;
+  } else if (sizeof(T) == 2 && a.hd == 64) {
     switch (hpg) {
 #define HH_DECM_CASE(W) \
       case W: hipLaunchKernelGGL((decode_attn_mfma<W>), grid, dim3(DTHREADS), 0, s, a); break;
@@ -603,22 +605,23 @@ hipError_t launch_decode_attention(const DecodeAttnArgs &a, hipStream_t s) {
 #undef HH_DECM_CASE
       default: return hipErrorInvalidValue;
     }
-    hipLaunchKernelGGL(decode_attn_combine<T>, dim3(a.B * a.H), dim3(64), 0, s, a);
-    return hipGetLastError();
-  }
-  switch (hpg) {
+  } else {
+    switch (hpg) {
 #define HH_DEC_CASE(W) \
-    case W: hipLaunchKernelGGL((decode_attn_split<T, W>), grid, dim3(DTHREADS), 0, s, a); break;
-    HH_DEC_CASE(1) HH_DEC_CASE(2) HH_DEC_CASE(3) HH_DEC_CASE(4)
-    HH_DEC_CASE(5) HH_DEC_CASE(6) HH_DEC_CASE(7) HH_DEC_CASE(8)
+      case W: hipLaunchKernelGGL((decode_attn_split<T, W>), grid, dim3(DTHREADS), 0, s, a); break;
+      HH_DEC_CASE(1) HH_DEC_CASE(2) HH_DEC_CASE(3) HH_DEC_CASE(4)
+      HH_DEC_CASE(5) HH_DEC_CASE(6) HH_DEC_CASE(7) HH_DEC_CASE(8)
 #undef HH_DEC_CASE
-    default: return hipErrorInvalidValue;
+      default: return hipErrorInvalidValue;
+    }
   }
-  hipLaunchKernelGGL(decode_attn_combine<T>, dim3(a.B * a.H), dim3(64), 0, s, a);
+  if (!direct && !defer_combine)
+    hipLaunchKernelGGL(decode_attn_combine<T>, dim3(a.B * a.H), dim3(64), 0, s, a);
+  if (o_ready) *o_ready = direct || !defer_combine;
   return hipGetLastError();
 }
-template hipError_t launch_decode_attention<float>(const DecodeAttnArgs &, hipStream_t);
-template hipError_t launch_decode_attention<bf16>(const DecodeAttnArgs &, hipStream_t);
+template hipError_t launch_decode_attention<float>(const DecodeAttnArgs &, hipStream_t, bool, bool *);
+template hipError_t launch_decode_attention<bf16>(const DecodeAttnArgs &, hipStream_t, bool, bool *);
 
 // ---------------------------------------------------------------------------
 // one SSM step: four lanes per (sequence, channel), four states each, so the

@@ -330,9 +330,10 @@ hh_status decode_t(const Shape &s, const hh_weights *w, const void *x, int B, co
   da.split = L.split;
   da.nsplit = L.nsplit;
   hipError_t err;
+  bool o_ready = false;
   {
     Stage sg(st, is_global ? "decode_attention_global" : "decode_attention_swa");
-    err = hh::launch_decode_attention<T>(da, st);
+    err = hh::launch_decode_attention<T>(da, st, /*defer_combine=*/true, &o_ready);
   }
   if (err != hipSuccess) return hip_fail(err, "decode attention");
 
@@ -353,6 +354,9 @@ hh_status decode_t(const Shape &s, const hh_weights *w, const void *x, int B, co
   na.o = da.o; na.y = sa.y; na.beta_attn = w->beta_attn; na.beta_ssm = w->beta_ssm;
   na.f = at(ws, L.f);
   na.rows = B; na.Wa = s.Wa; na.D = s.D; na.eps = s.eps;
+  if (!o_ready) {   // merge the attention's split partials here
+    na.part = da.part; na.H = s.H; na.hd = s.hd; na.nsplit = da.nsplit;
+  }
   {
     Stage sg(st, "decode_norm");
     err = hh::launch_norm_fuse<T>(na, st);

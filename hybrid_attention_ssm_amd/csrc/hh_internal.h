@@ -289,6 +289,10 @@ struct NormArgs {
   void *f;                 // [rows, Wa + D]
   int rows, Wa, D;
   float eps;
+  // decode: when part is set the attention half is merged from the split
+  // partials of the decode attention (o unused); Wa = H * hd
+  const float *part;
+  int H, hd, nsplit;
 };
 template <class T> hipError_t launch_norm_fuse(const NormArgs &a, hipStream_t s);
 
@@ -302,7 +306,14 @@ struct DecodeAttnArgs {
   float *part;             // split partials
   int B, H, G, hd, m, cap, is_ring, window, is_global, split, nsplit;
 };
-template <class T> hipError_t launch_decode_attention(const DecodeAttnArgs &a, hipStream_t s);
+// Per-split partials sit at part[((b*H + h)*nsplit + s)*(hd + 2)]: the running
+// maximum m of the base-2 scaled scores, l = sum 2^(score - m), then
+// a[hd] = sum 2^(score - m) v.  With defer_combine the merge of several splits
+// is left to the caller (the decode norm does it); *o_ready says whether o
+// holds the finished output.
+template <class T>
+hipError_t launch_decode_attention(const DecodeAttnArgs &a, hipStream_t s, bool defer_combine,
+                                   bool *o_ready);
 size_t decode_attn_part_bytes(int B, int H, int G, int hd, int m, int max_real,
                               int *split_out, int *nsplit_out);
 

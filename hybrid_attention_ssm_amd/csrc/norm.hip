@@ -144,10 +144,111 @@ __global__ void __launch_bounds__(256) norm_fuse_reg(NormArgs a) {
   }
 }
 
+// Decode: the attention half arrives as the split partials of the decode
+// attention (per head and split: m, l, a[hd], see launch_decode_attention).
+// Scaling split s by 2^(m_s - max m) and summing gives O = sum a / sum l, the
+// same softmax-weighted mean of V over all keys; O is rounded to T exactly as
+// a stored O would be, then normalised like above.  One workgroup per row;
+// thread t merges the W-wide column groups t, t + 256, ... (C at most).
+template <class T, int C>
+__global__ void __launch_bounds__(256) norm_fuse_parts(NormArgs a) {
+  constexpr int W = Vec<T>::W;
+  typedef typename Vec<T>::type V;
+  __shared__ float part[4][2];
+  const int row = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
+  const int no = a.Wa / W, ny = a.D / W, per_head = a.hd / W, stride = a.hd + 2;
+  const float *pr = a.part + (size_t)row * a.H * a.nsplit * stride;
+  const T *y = reinterpret_cast<const T *>(a.y) + (size_t)row * a.D;
+  T *f = reinterpret_cast<T *>(a.f) + (size_t)row * (a.Wa + a.D);
+  V vy[C];
+#pragma unroll
+  for (int j = 0; j < C; ++j)   // indices past the row repeat its last chunk
+    vy[j] = *reinterpret_cast<const V *>(y + (size_t)min(tid + j * 256, ny - 1) * W);
+  float vo[C][W];
+  float so = 0.0f, sy = 0.0f;
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    const int u = tid + j * 256;
+#pragma unroll
+    for (int e = 0; e < W; ++e) vo[j][e] = 0.0f;
+    if (u < no) {
+      const float *ph = pr + (size_t)(u / per_head) * a.nsplit * stride;
+      const int c = (u % per_head) * W;
+      float M = -INFINITY, L = 0.0f, acc[W];
+#pragma unroll
+      for (int e = 0; e < W; ++e) acc[e] = 0.0f;
+#pragma unroll 4
+      for (int sp = 0; sp < a.nsplit; ++sp) {
+        const float *q = ph + (size_t)sp * stride;
+        const float ms = q[0], ls = q[1];
+        float av[W];
+#pragma unroll
+        for (int e = 0; e < W; e += 2) {   // a[] is 8-byte aligned
+          const float2 t = *reinterpret_cast<const float2 *>(q + 2 + c + e);
+          av[e] = t.x; av[e + 1] = t.y;
+        }
+        const float mn = fmaxf(M, ms);
+        const float sc_old = M == -INFINITY ? 0.0f : exp2_fast(M - mn);
+        const float sc_new = ms == -INFINITY ? 0.0f : exp2_fast(ms - mn);
+        L = L * sc_old + ls * sc_new;
+#pragma unroll
+        for (int e = 0; e < W; ++e) acc[e] = acc[e] * sc_old + av[e] * sc_new;
+        M = mn;
+      }
+      const float inv = 1.0f / L;
+#pragma unroll
+      for (int e = 0; e < W; ++e) {
+        vo[j][e] = to_f32(from_f32<T>(acc[e] * inv));
+        so = fmaf(vo[j][e], vo[j][e], so);
+      }
+    }
+    if (u < ny) {
+#pragma unroll
+      for (int e = 0; e < W; ++e) { const float fy = to_f32(vy[j][e]); sy = fmaf(fy, fy, sy); }
+    }
+  }
+  so = wave_sum(so);
+  sy = wave_sum(sy);
+  if ((tid & 63) == 0) { part[wave][0] = so; part[wave][1] = sy; }
+  __syncthreads();
+  so = part[0][0] + part[1][0] + part[2][0] + part[3][0];
+  sy = part[0][1] + part[1][1] + part[2][1] + part[3][1];
+  const float ro = 0.5f / sqrtf(so / (float)a.Wa + a.eps);
+  const float ry = 0.5f / sqrtf(sy / (float)a.D + a.eps);
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    const int u = tid + j * 256;
+    if (u < no) {
+      V out;
+#pragma unroll
+      for (int e = 0; e < W; ++e) out[e] = from_f32<T>(a.beta_attn[u * W + e] * vo[j][e] * ro);
+      *reinterpret_cast<V *>(f + (size_t)u * W) = out;
+    }
+    if (u < ny) {
+      V out;
+#pragma unroll
+      for (int e = 0; e < W; ++e) out[e] = from_f32<T>(a.beta_ssm[u * W + e] * to_f32(vy[j][e]) * ry);
+      *reinterpret_cast<V *>(f + a.Wa + (size_t)u * W) = out;
+    }
+  }
+}
+
 template <class T>
 hipError_t launch_norm_fuse(const NormArgs &a, hipStream_t s) {
   constexpr int W = Vec<T>::W;
   constexpr int MAXC = 8;
+  if (a.part) {
+    if (a.Wa % W || a.D % W || a.hd % W || a.Wa != a.H * a.hd) return hipErrorInvalidValue;
+    const int need = (std::max(a.Wa, a.D) / W + 255) / 256;
+    switch (need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 0) {
+      case 1: hipLaunchKernelGGL((norm_fuse_parts<T, 1>), dim3(a.rows), dim3(256), 0, s, a); break;
+      case 2: hipLaunchKernelGGL((norm_fuse_parts<T, 2>), dim3(a.rows), dim3(256), 0, s, a); break;
+      case 4: hipLaunchKernelGGL((norm_fuse_parts<T, 4>), dim3(a.rows), dim3(256), 0, s, a); break;
+      case 8: hipLaunchKernelGGL((norm_fuse_parts<T, 8>), dim3(a.rows), dim3(256), 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   const int widest = std::max(a.Wa, a.D) / W;
   if (a.Wa % W == 0 && a.D % W == 0) {
     if (a.rows < 2048 && widest <= MAXC * 256) {
