@@ -14,7 +14,11 @@ namespace hh {
 // Map the linear block id to an output tile.  Hardware hands consecutive
 // block ids to the 8 XCDs in turn; the remap gives each XCD a contiguous run
 // of logical tiles, and the grouped order (GROUP row-tiles per column sweep)
-// keeps the A rows and B columns of that run in the XCD's own L2.
+// keeps the A rows and B columns of that run in the XCD's own L2.  Logical
+// column tiles alternate between the left and right halves of the output, so
+// each XCD's run mixes both: column blocks whose epilogue costs more (the
+// in-projection's softplus columns sit at its right end) are spread over all
+// XCDs instead of piling onto half of them.
 __device__ __forceinline__ bool tile_of(int tiles_m, int tiles_n, int &tm, int &tn) {
   constexpr int GROUP = 8;
   int bid = blockIdx.x;
@@ -26,7 +30,8 @@ __device__ __forceinline__ bool tile_of(int tiles_m, int tiles_n, int &tm, int &
   const int gm = min(tiles_m - first_m, GROUP);
   const int in_group = bid % group_size;
   tm = first_m + in_group % gm;
-  tn = in_group / gm;
+  const int lt = in_group / gm;
+  tn = (lt & 1) ? (tiles_n + 1) / 2 + (lt >> 1) : (lt >> 1);
   return true;
 }
 

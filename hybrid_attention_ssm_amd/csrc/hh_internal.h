@@ -45,13 +45,18 @@ __device__ __forceinline__ float silu_f(float x) {
   return x * rcp_fast(1.0f + exp2_fast(-x * kLog2e));
 }
 // log(1 + e^v) without overflow: max(v, 0) + log1p(t), t = e^-|v| in (0, 1].
-// log1p(t) = log(u) * t / (u - 1) with u = fl(1 + t) cancels the rounding of
-// 1 + t (Kahan's correction), so small t keeps full relative accuracy.
+// With u = fl(1 + t) (so u - 1 is exact), log1p(t) = log(u) + log(1 + r) where
+// r = (t - (u - 1)) / u is the relative rounding error of 1 + t, |r| <= 2^-24;
+// log(1 + r) = r to within r^2 / 2.  1/u (u in [1, 2]) is taken from the chord
+// 1.5 - u/2, within 6 %, which only scales the already tiny r.  Two
+// transcendentals (2^x, log2) and no division; small t keeps full relative
+// accuracy (u = 1 gives exactly t).
 __device__ __forceinline__ float softplus_f(float v) {
-  const float t = __expf(-fabsf(v));
+  constexpr float kLn2 = 0.6931471805599453f;
+  const float t = exp2_fast(-fabsf(v) * kLog2e);
   const float u = 1.0f + t;
-  const float l1p = (u == 1.0f) ? t : __logf(u) * __fdividef(t, u - 1.0f);
-  return fmaxf(v, 0.0f) + l1p;
+  const float r = (t - (u - 1.0f)) * fmaf(-0.5f, u, 1.5f);
+  return fmaxf(v, 0.0f) + fmaf(__builtin_amdgcn_logf(u), kLn2, r);
 }
 
 // ---- the in-projection column map ------------------------------------------
