@@ -369,8 +369,8 @@ def main():
             cnt, tot = st["decode_attention_global"]
             ach = dec["global_attn_bytes"] / (tot / cnt * 1e-3)
             tr = measured_traffic("decode_attn_dma", dec["workload"])
-            d["roofline"] = {"kernel": "decode attention of the global layer (decode_attn_dma + "
-                                       "decode_attn_combine)",
+            d["roofline"] = {"kernel": "decode attention of the global layer (decode_attn_dma; "
+                                       "its split partials are merged by the decode norm kernel)",
                              "bound": "hbm", "achieved": ach / 1e9, "peak": HBM_PEAK / 1e9,
                              "unit": "GB/s", "frac": ach / HBM_PEAK,
                              "traffic": tr["bytes"] if tr else None,
