@@ -702,16 +702,4 @@ hipError_t launch_decode_ssm(const DecodeSsmArgs &a, hipStream_t s) {
 template hipError_t launch_decode_ssm<float>(const DecodeSsmArgs &, hipStream_t);
 template hipError_t launch_decode_ssm<bf16>(const DecodeSsmArgs &, hipStream_t);
 
-// ---------------------------------------------------------------------------
-// cache length bookkeeping
-// ---------------------------------------------------------------------------
-__global__ void set_len_kernel(int32_t *len, int B, int value) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < B) len[i] = value;
-}
-hipError_t launch_set_len(int32_t *len, int B, int value, hipStream_t s) {
-  hipLaunchKernelGGL(set_len_kernel, dim3((B + 255) / 256), dim3(256), 0, s, len, B, value);
-  return hipGetLastError();
-}
-
 }  // namespace hh

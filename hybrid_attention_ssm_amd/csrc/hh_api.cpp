@@ -256,6 +256,9 @@ hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, i
   na.o = aa.o; na.y = sa.y; na.beta_attn = w->beta_attn; na.beta_ssm = w->beta_ssm;
   na.f = at(ws, L.off[HH_WS_F]);
   na.rows = rows; na.Wa = s.Wa; na.D = s.D; na.eps = s.eps;
+  if (prod && kv && kv->len) {   // the cache now holds the prompt's n positions
+    na.set_len = kv->len; na.set_len_n = B; na.set_len_value = n;
+  }
   {
     Stage sg(st, "norm");
     err = hh::launch_norm_fuse<T>(na, st);
@@ -270,10 +273,6 @@ hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, i
   }
   if (err != hipSuccess) return hip_fail(err, "output projection");
 
-  if (prod && kv && kv->len) {
-    err = hh::launch_set_len(kv->len, B, n, st);
-    if (err != hipSuccess) return hip_fail(err, "cache length");
-  }
   return HH_OK;
 }
 

@@ -298,6 +298,10 @@ struct NormArgs {
   // partials of the decode attention (o unused); Wa = H * hd
   const float *part;
   int H, hd, nsplit;
+  // prefill of a producer with a cache: set_len[0..set_len_n) = set_len_value
+  // (the cache now holds the prompt's positions); null: nothing
+  int32_t *set_len;
+  int set_len_n, set_len_value;
 };
 template <class T> hipError_t launch_norm_fuse(const NormArgs &a, hipStream_t s);
 
@@ -336,6 +340,5 @@ struct DecodeSsmArgs {
 };
 template <class T> hipError_t launch_decode_ssm(const DecodeSsmArgs &a, hipStream_t s);
 
-hipError_t launch_set_len(int32_t *len, int B, int value, hipStream_t s);
 
 }  // namespace hh

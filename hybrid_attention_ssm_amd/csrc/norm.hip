@@ -16,6 +16,12 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// block 0 records the prompt length of a producer's cache (see NormArgs)
+__device__ __forceinline__ void record_len(const NormArgs &a) {
+  if (a.set_len && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < a.set_len_n; i += blockDim.x) a.set_len[i] = a.set_len_value;
+}
+
 template <class T> struct Vec;
 template <> struct Vec<bf16> { static constexpr int W = 8; typedef bf16x8 type; };
 template <> struct Vec<float> { static constexpr int W = 4; typedef f32x4 type; };
@@ -52,6 +58,7 @@ __device__ __forceinline__ void scaled(const T *p, const float *beta, float r, T
 // 256 threads per workgroup
 template <class T, int WPR>
 __global__ void __launch_bounds__(256) norm_fuse(NormArgs a) {
+  record_len(a);
   __shared__ float part[4][2];
   const int wave = threadIdx.x >> 6;
   const int row = blockIdx.x * (4 / WPR) + wave / WPR;
@@ -82,6 +89,7 @@ __global__ void __launch_bounds__(256) norm_fuse(NormArgs a) {
 // Lanes of WPR waves take chunks lane, lane + 64*WPR, ... (MAXC at most).
 template <class T, int WPR, int MAXC>
 __global__ void __launch_bounds__(256) norm_fuse_reg(NormArgs a) {
+  record_len(a);
   constexpr int W = Vec<T>::W;
   typedef typename Vec<T>::type V;
   __shared__ float part[4][2];
@@ -152,6 +160,7 @@ __global__ void __launch_bounds__(256) norm_fuse_reg(NormArgs a) {
 // thread t merges the W-wide column groups t, t + 256, ... (C at most).
 template <class T, int C>
 __global__ void __launch_bounds__(256) norm_fuse_parts(NormArgs a) {
+  record_len(a);
   constexpr int W = Vec<T>::W;
   typedef typename Vec<T>::type V;
   __shared__ float part[4][2];
