@@ -345,6 +345,17 @@ def main():
         rec["mfma_frac_layer"] = fl["total"] / (pre["ms_step"] * 1e-3) / MFMA_BF16_PEAK
         rec["algorithmic_gflop_per_step"] = fl["total"] / 1e9
         rec["stage_us"] = {k: v * 1e3 for k, v in pre["stages"].items()}
+        t_scan = pre["stages"].get("scan")
+        if t_scan:
+            # the scan step alone: xs, Delta (fp32), z (bf16) and B|C (fp32) read, Y (bf16) written,
+            # and one exp per (token, channel, state) of the recurrence
+            dd = pre["dims"]
+            T = pre["B"] * pre["n"]
+            sb = T * dd.d_inner * (4 + 4 + 2 + 2) + T * 2 * dd.d_state * 4
+            ex = T * dd.d_inner * dd.d_state
+            rec["scan"] = {"us": t_scan * 1e3, "algorithmic_bytes": sb,
+                           "GB_per_s": sb / (t_scan * 1e-3) / 1e9, "frac_hbm": sb / (t_scan * 1e-3) / HBM_PEAK,
+                           "recurrence_exps": ex, "exps_per_s": ex / (t_scan * 1e-3)}
         if t_in:
             ach = fl["inproj"] / (t_in * 1e-3)
             tr = measured_traffic("gemm_bf16_lds", pre["workload"])
