@@ -7,6 +7,10 @@ window 1024) and its 128 meta tokens (§2.3 and the authors' OpenReview reply on
 the number of meta tokens).  Head dim 64 and d_inner 3200 are the two free
 widths of that table fixed by the workload definitions below.
 
+The block around the layer (pre-norms, residuals and the MLP) uses the same
+table's MLP hidden width, 5504 at 1.5B, and its 32 blocks with 3 full-attention
+layers (first, middle, last).
+
 This module holds data only: no arithmetic of the method lives here.
 """
 from dataclasses import dataclass, field, replace
@@ -104,3 +108,48 @@ def shrink(w: PrefillWorkload, **kw) -> PrefillWorkload:
     dims_kw = {k: kw.pop(k) for k in list(kw) if hasattr(w.dims, k)}
     dims = replace(w.dims, **dims_kw) if dims_kw else w.dims
     return replace(w, dims=dims, **kw)
+
+
+MLP_HIDDEN_1P5B = 5504     # Table 11, 1.5B column
+MLP_HIDDEN_TINY = 96
+
+
+@dataclass(frozen=True)
+class StackWorkload:
+    """A decode step through a stack of blocks.
+
+    Full-attention layers own a linear cache of global_cap slots; sliding-window
+    layers pair up in order (the first of a pair produces K/V into a ring of
+    `window` slots, the second reads it); an unpaired window layer produces
+    for itself.
+    """
+    name: str
+    seed: int
+    dims: LayerDims
+    d_ff: int
+    batch: int
+    context: int
+    window: int
+    global_cap: int
+    n_layers: int
+    global_layers: Tuple[int, ...]
+
+    def layer_plan(self):
+        """[(is_global, kv_producer, cache name)] per layer."""
+        plan, pending = [], None
+        for i in range(self.n_layers):
+            if i in self.global_layers:
+                plan.append((True, True, f"g{i}"))
+                pending = None
+            elif pending is None:
+                plan.append((False, True, f"r{i}"))
+                pending = f"r{i}"
+            else:
+                plan.append((False, False, pending))
+                pending = None
+        return plan
+
+
+STACK_DECODE = StackWorkload("stack32_decode_b128_ctx8192", 5, HYMBA_1P5B, MLP_HIDDEN_1P5B,
+                             batch=128, context=8191, window=1024, global_cap=8192,
+                             n_layers=32, global_layers=(0, 15, 31))

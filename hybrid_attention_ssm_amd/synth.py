@@ -14,9 +14,14 @@ draws in this fixed order):
   6. conv_w [D, k]             ~ N(0, 1/k);  conv_b = 0
   7. W_out  [d, H*hd + D]      ~ N(0, 1/(H*hd + D))
   8. beta_attn = beta_ssm = 1
+A block (pre-norm, layer, residual, pre-norm, MLP, residual) draws its layer
+(3-8), then:
+  9. g1, g2 [d]                ~ 1 + 0.1 N(0, 1)    (RMSNorm gains, fp32)
+ 10. W_gu   [2 d_ff, d]        ~ N(0, 1/d)          (rows 2i gate i, 2i+1 up i)
+ 11. W_down [d, d_ff]          ~ N(0, 1/d_ff)
 For bf16 workloads x, R, W_in, conv_w and W_out are rounded to bf16 once
-(round to nearest even); every consumer sees the rounded values.  A, b_dt and
-the betas stay fp32.  A consumer layer (no K/V projection) drops the K and V
+(round to nearest even); every consumer sees the rounded values, and so are
+W_gu and W_down.  A, b_dt, the betas and the norm gains stay fp32.  A consumer layer (no K/V projection) drops the K and V
 rows of the same draw, so it shares every other weight with its producer.
 """
 from __future__ import annotations
@@ -62,6 +67,26 @@ def layer_weights(rng, dims: LayerDims, kv_producer: bool = True) -> dict:
     return dict(w_in=w_in, dt_bias=dt_bias, A=A, conv_w=conv_w, conv_b=conv_b,
                 beta_attn=np.ones(Wa, np.float32), beta_ssm=np.ones(D, np.float32),
                 w_out=w_out, kv_producer=bool(kv_producer))
+
+
+def block_weights(rng, dims: LayerDims, d_ff: int, kv_producer: bool = True) -> dict:
+    """Draw one block's parameters: its layer, then steps 9-11 of the recipe."""
+    d = dims.d_model
+    mixer = layer_weights(rng, dims, kv_producer)
+    g1 = (1.0 + 0.1 * _normal(rng, (d,))).astype(np.float32)
+    g2 = (1.0 + 0.1 * _normal(rng, (d,))).astype(np.float32)
+    w_gu = _store(dims, _normal(rng, (2 * d_ff, d), (1.0 / d) ** 0.5))
+    w_down = _store(dims, _normal(rng, (d, d_ff), (1.0 / d_ff) ** 0.5))
+    return dict(mixer=mixer, norm1=g1, norm2=g2, w_gate_up=w_gu, w_down=w_down, d_ff=int(d_ff))
+
+
+def block_inputs(w: PrefillWorkload, d_ff: int, kv_producer: bool = True, seed=None) -> dict:
+    """x, meta tokens R and one block's weights for a prefill workload."""
+    dims = w.dims
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    x = _store(dims, _normal(rng, (w.batch, w.seqlen, dims.d_model)))
+    R = _store(dims, _normal(rng, (dims.n_meta, dims.d_model)))
+    return dict(x=x, R=R, weights=block_weights(rng, dims, d_ff, kv_producer))
 
 
 def prefill_inputs(w: PrefillWorkload, kv_producer: bool = True, seed=None) -> dict:

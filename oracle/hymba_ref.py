@@ -38,6 +38,15 @@ Readings where the pages are silent or ambiguous (each is a stated choice):
   * query head h reads KV head floor(h / (H/G))
   * a KV-sharing consumer layer has no K/V projection rows and attends over
     its producer's K/V                   [authors' reply, cache optimisation]
+
+The block around the layer (the pages name its MLP width, 5504 at 1.5B in the
+architecture table, and draw it in their architecture figure, but do not
+write it out; these are the plain pre-norm readings):
+  * x1 = x + layer(g1 * norm(x)),  out = x1 + MLP(g2 * norm(x1)), with norm the
+    RMS normalisation above and g1, g2 learned per-channel gains; the meta
+    rows enter the layer as g1 * norm(R)
+  * MLP(v) = W_down (SiLU(W_gate v) * (W_up v)); W_gate and W_up are stored
+    as one matrix whose rows alternate gate, up (row 2i gate i, 2i+1 up i)
 """
 from __future__ import annotations
 
@@ -353,3 +362,56 @@ def decode_step(dims, weights, x_t, meta_k, meta_v, window, is_global, cache, h,
     if w["kv_producer"]:
         length[seqs] += 1
     return dict(out=out, cache_k=ck, cache_v=cv, len=length, h=h_new, conv=conv_new)
+
+
+# ---------------------------------------------------------------------------
+# the block around the layer: pre-norms, residuals, SiLU-gated MLP
+# [architecture table (MLP hidden width) and figure; readings in the header]
+# ---------------------------------------------------------------------------
+def rms_norm(v, g, eps):
+    """g * v / sqrt(mean(v^2) + eps), row-wise."""
+    return _f64(g) * rms_normalize(_f64(v), eps)
+
+
+def mlp(v, w_gate_up, w_down):
+    """W_down (SiLU(W_gate v) * W_up v); rows of w_gate_up alternate gate, up."""
+    gu = _f64(v) @ _f64(w_gate_up).T
+    return (silu(gu[..., 0::2]) * gu[..., 1::2]) @ _f64(w_down).T
+
+
+def block_meta_prefix(dims, bw, R):
+    """meta_prefix of the block's layer, whose meta rows are g1 * norm(R)."""
+    eps = dict(dims)["eps"]
+    return meta_prefix(dims, bw["mixer"], rms_norm(R, bw["norm1"], eps))
+
+
+def block_prefill(dims, bw, R, x, window, is_global, shared_kv=None, cache=None):
+    """One block over the prompt x [B, n, d] with meta rows R [m, d].
+
+    Returns prefill()'s dict for the layer (K/V, state, caches) with `out`
+    replaced by the block output and `x1` the residual stream after the layer.
+    """
+    eps = dict(dims)["eps"]
+    x = _f64(x)
+    layer = prefill(dims, bw["mixer"], rms_norm(R, bw["norm1"], eps), rms_norm(x, bw["norm1"], eps),
+                    window, is_global, shared_kv=shared_kv, cache=cache)
+    x1 = x + layer["out"]
+    res = dict(layer)
+    res["x1"] = x1
+    res["out"] = x1 + mlp(rms_norm(x1, bw["norm2"], eps), bw["w_gate_up"], bw["w_down"])
+    return res
+
+
+def block_decode_step(dims, bw, x_t, meta_k, meta_v, window, is_global, cache, h, conv,
+                      seqs=None):
+    """One new token per sequence through one block (see decode_step)."""
+    eps = dict(dims)["eps"]
+    x_t = _f64(x_t)
+    seqs = np.arange(x_t.shape[0]) if seqs is None else np.asarray(seqs, dtype=np.int64)
+    layer = decode_step(dims, bw["mixer"], rms_norm(x_t, bw["norm1"], eps), meta_k, meta_v,
+                        window, is_global, cache, h, conv, seqs=seqs)
+    x1 = x_t[seqs] + layer["out"]
+    res = dict(layer)
+    res["out"] = x1 + mlp(rms_norm(x1, bw["norm2"], eps), bw["w_gate_up"], bw["w_down"])
+    return res
+

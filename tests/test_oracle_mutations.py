@@ -92,6 +92,40 @@ MUTANTS = {
 ref._fuse_orig = ref.fuse
 
 
+# the block around the layer: caught by the block's library-composition pin
+from tests.test_oracle_pins import _block, block_by_library
+
+
+def _block_err():
+    from hybrid_attention_ssm_amd.configs import TINY
+    x, R, bw = _block(TINY, 13, seed=34)
+    got = ref.block_prefill(TINY.as_dict(), bw, R, x, 6, False)
+    want = block_by_library(TINY, bw, R, x[0], 6, False)
+    return float(np.abs(got["out"][0] - want["out"]).max())
+
+
+_orig_mlp = ref.mlp
+_orig_rms_norm = ref.rms_norm
+BLOCK_MUTANTS = {
+    "gate<->up": ("mlp", lambda v, w_gu, w_down: _orig_mlp(v, w_gu[np.arange(w_gu.shape[0]) ^ 1], w_down)),
+    "MLP without SiLU": ("mlp", lambda v, w_gu, w_down: ((np.asarray(v) @ w_gu.T)[..., 0::2]
+                                                         * (np.asarray(v) @ w_gu.T)[..., 1::2]) @ w_down.T),
+    "norm gain dropped": ("rms_norm", lambda v, g, eps: _orig_rms_norm(v, np.ones_like(g), eps)),
+    "norm gain applied twice": ("rms_norm", lambda v, g, eps: np.asarray(g) * _orig_rms_norm(v, g, eps)),
+}
+
+
+def test_unmutated_block_agrees():
+    assert _block_err() < 1e-9
+
+
+@pytest.mark.parametrize("name", sorted(BLOCK_MUTANTS))
+def test_block_pin_catches_mutant(name, monkeypatch):
+    attr, fn = BLOCK_MUTANTS[name]
+    monkeypatch.setattr(ref, attr, fn)
+    assert _block_err() > 1e-4, f"mutant '{name}' not caught"
+
+
 def test_unmutated_oracle_agrees():
     assert _max_err() < 1e-9
 

@@ -363,3 +363,90 @@ def test_consumer_decode_sees_token_appended_by_producer():
     np.testing.assert_allclose(rc["out"], rp["out"], rtol=1e-13)
     np.testing.assert_array_equal(rc["cache_k"], rp["cache_k"])
     assert list(rc["len"]) == [8, 8]
+
+
+# ---------------------------------------------------------------------------
+# the block around the layer (pre-norms, residuals, SiLU-gated MLP)
+# ---------------------------------------------------------------------------
+def _block(dims: LayerDims, n, seed, d_ff=20, kv_producer=True, batch=1):
+    from hybrid_attention_ssm_amd.synth import block_weights
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((batch, n, dims.d_model)).astype(np.float32)
+    R = rng.standard_normal((dims.n_meta, dims.d_model)).astype(np.float32)
+    return x, R, block_weights(rng, dims, d_ff, kv_producer)
+
+
+def block_by_library(dims: LayerDims, bw, R, xb, window, is_global):
+    """x1 = x + layer(rms_norm(x; g1)); out = x1 + down(silu(gate) * up) of
+    rms_norm(x1; g2), with torch's rms_norm, linear and silu; the gate/up rows
+    are taken from the even/odd rows of the stored matrix."""
+    t = lambda a: torch.as_tensor(np.asarray(a, dtype=np.float64))
+    d = dims.d_model
+    n1 = lambda v: TF.rms_norm(t(v), (d,), weight=t(bw["norm1"]), eps=dims.eps).numpy()
+    layer = layer_by_library(dims, bw["mixer"], n1(R), n1(xb), window, is_global)
+    x1 = t(xb) + t(layer["out"])
+    n2 = TF.rms_norm(x1, (d,), weight=t(bw["norm2"]), eps=dims.eps)
+    w = t(bw["w_gate_up"])
+    hidden = TF.silu(TF.linear(n2, w[0::2])) * TF.linear(n2, w[1::2])
+    return dict(out=(x1 + TF.linear(hidden, t(bw["w_down"]))).numpy(), x1=x1.numpy(), h=layer["h"])
+
+
+@pytest.mark.parametrize("dims,n,window,is_global", [(TINY, 21, 8, False), (GQA, 17, 5, True)])
+def test_block_matches_library_composition(dims, n, window, is_global):
+    x, R, bw = _block(dims, n, seed=31)
+    got = ref.block_prefill(dims.as_dict(), bw, R, x, window, is_global)
+    want = block_by_library(dims, bw, R, x[0], window, is_global)
+    np.testing.assert_allclose(got["out"][0], want["out"], rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(got["x1"][0], want["x1"], rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(got["h"][0], want["h"], rtol=1e-10, atol=1e-12)
+
+
+def test_rms_norm_closed_form():
+    # rms([3, 4]) = sqrt(12.5)
+    got = ref.rms_norm(np.array([3.0, 4.0]), np.array([2.0, 1.0]), 0.0)
+    r = math.sqrt(12.5)
+    np.testing.assert_allclose(got, [6.0 / r, 4.0 / r], rtol=1e-15)
+
+
+def test_mlp_gate_is_the_even_row():
+    """SiLU(v) -> v for large v and -> 0 for very negative v: with the gate on
+    coordinate 0 and the up projection on coordinate 1, the output is the
+    down column times v0 * v1 or nearly zero, never the other way round."""
+    w_gu = np.array([[1.0, 0.0], [0.0, 1.0]])     # row 0 gate = e0, row 1 up = e1
+    w_down = np.array([[2.0], [-3.0]])
+    big = ref.mlp(np.array([40.0, 0.5]), w_gu, w_down)
+    np.testing.assert_allclose(big, [2.0 * 40.0 * 0.5, -3.0 * 40.0 * 0.5], rtol=1e-15)
+    tiny = ref.mlp(np.array([-40.0, 0.5]), w_gu, w_down)
+    assert np.abs(tiny).max() < 1e-15 * 40 + 1e-15
+    swapped = ref.mlp(np.array([0.5, 40.0]), w_gu, w_down)    # gate sees 0.5, up sees 40
+    assert abs(swapped[0] - 2.0 * 0.5 / (1.0 + math.exp(-0.5)) * 40.0) < 1e-12
+
+
+def test_block_is_identity_when_both_branches_are_zero():
+    dims = GQA
+    x, R, bw = _block(dims, 9, seed=32)
+    bw = dict(bw, mixer=dict(bw["mixer"], w_out=np.zeros_like(bw["mixer"]["w_out"])),
+              w_down=np.zeros_like(bw["w_down"]))
+    got = ref.block_prefill(dims.as_dict(), bw, R, x, 4, False)
+    np.testing.assert_array_equal(got["out"], x.astype(np.float64))
+
+
+def test_block_prefill_then_decode_equals_longer_prefill():
+    dims = GQA
+    n0, steps, cap = 6, 5, 6
+    x, R, bw = _block(dims, n0 + steps, seed=33, batch=2)
+    B = x.shape[0]
+    zeros = np.zeros((B, dims.n_kv_heads, cap, dims.head_dim))
+    cache0 = dict(k=zeros, v=zeros, is_ring=True)
+    full = ref.block_prefill(dims.as_dict(), bw, R, x, cap, False, cache=cache0)
+    pre = ref.block_prefill(dims.as_dict(), bw, R, x[:, :n0], cap, False, cache=cache0)
+    mp = ref.block_meta_prefix(dims.as_dict(), bw, R)
+    cache = dict(k=pre["cache_k"], v=pre["cache_v"], len=np.full(B, n0), is_ring=True)
+    h, conv = pre["h"], pre["conv_tail"]
+    for s in range(steps):
+        r = ref.block_decode_step(dims.as_dict(), bw, x[:, n0 + s], mp["k"], mp["v"], cap,
+                                  False, cache, h, conv)
+        np.testing.assert_allclose(r["out"], full["out"][:, n0 + s], rtol=1e-10, atol=1e-11)
+        cache = dict(k=r["cache_k"], v=r["cache_v"], len=r["len"], is_ring=True)
+        h, conv = r["h"], r["conv"]
+    np.testing.assert_allclose(h, full["h"], rtol=1e-10, atol=1e-12)
