@@ -51,6 +51,11 @@ class HHSsmState(ctypes.Structure):
     _fields_ = [("h", _vp), ("conv", _vp)]
 
 
+class HHBlockWeights(ctypes.Structure):
+    _fields_ = [("mixer", HHWeights), ("norm1", _vp), ("norm2", _vp), ("w_gate_up", _vp),
+                ("w_down", _vp), ("d_ff", _i32)]
+
+
 class HHStageTime(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 32), ("launches", _i32), ("total_ms", ctypes.c_double)]
 
@@ -92,6 +97,23 @@ def lib() -> ctypes.CDLL:
         L.hh_decode_step.restype = ctypes.c_int
         L.hh_decode_step.argtypes = [P(HHDims), P(HHWeights), _vp, _i32, P(HHMeta), _i32, _i32,
                                      P(HHKV), P(HHSsmState), _vp, _vp, ctypes.c_size_t, _vp]
+        L.hh_block_meta_prefix_workspace_size.restype = ctypes.c_size_t
+        L.hh_block_meta_prefix_workspace_size.argtypes = [P(HHDims), _i32]
+        L.hh_block_prefill_workspace_size.restype = ctypes.c_size_t
+        L.hh_block_prefill_workspace_size.argtypes = [P(HHDims), _i32, _i32, _i32, _i32]
+        L.hh_block_decode_workspace_size.restype = ctypes.c_size_t
+        L.hh_block_decode_workspace_size.argtypes = [P(HHDims), _i32, _i32, _i32, _i32]
+        L.hh_block_meta_prefix.restype = ctypes.c_int
+        L.hh_block_meta_prefix.argtypes = [P(HHDims), P(HHBlockWeights), _vp, _vp, _vp, _vp, _vp,
+                                           _vp, ctypes.c_size_t, _vp]
+        L.hh_block_prefill.restype = ctypes.c_int
+        L.hh_block_prefill.argtypes = [P(HHDims), P(HHBlockWeights), _vp, _i32, _i32, P(HHMeta),
+                                       _i32, _i32, _vp, P(HHKV), P(HHSsmState), _vp,
+                                       ctypes.c_size_t, _vp]
+        L.hh_block_decode_step.restype = ctypes.c_int
+        L.hh_block_decode_step.argtypes = [P(HHDims), P(HHBlockWeights), _vp, _i32, P(HHMeta),
+                                           _i32, _i32, P(HHKV), P(HHSsmState), _vp, _vp,
+                                           ctypes.c_size_t, _vp]
         L.hh_timing_enable.restype = ctypes.c_int
         L.hh_timing_enable.argtypes = [_i32]
         L.hh_timing_read.restype = _i32
@@ -168,6 +190,35 @@ def upload_weights(dims: LayerDims, w: dict, device="cuda") -> DeviceLayer:
                    _ptr(t["conv_b"]), _ptr(t["beta_attn"]), _ptr(t["beta_ssm"]),
                    _ptr(t["w_out"]), 1 if w.get("kv_producer", True) else 0)
     return DeviceLayer(dims, t, st)
+
+
+@dataclass
+class DeviceBlock:
+    dims: LayerDims
+    mixer: DeviceLayer
+    tensors: dict
+    struct: HHBlockWeights
+
+    @property
+    def kv_producer(self) -> bool:
+        return self.mixer.kv_producer
+
+    @property
+    def d_ff(self) -> int:
+        return int(self.struct.d_ff)
+
+
+def upload_block_weights(dims: LayerDims, bw: dict, device="cuda") -> DeviceBlock:
+    """Copy one block's parameters (numpy, from synth.block_weights) to the GPU."""
+    sd = storage_dtype(dims)
+    mixer = upload_weights(dims, bw["mixer"], device)
+    t = {"norm1": torch.as_tensor(bw["norm1"]).to(device=device, dtype=torch.float32).contiguous(),
+         "norm2": torch.as_tensor(bw["norm2"]).to(device=device, dtype=torch.float32).contiguous(),
+         "w_gate_up": torch.as_tensor(bw["w_gate_up"]).to(device=device, dtype=sd).contiguous(),
+         "w_down": torch.as_tensor(bw["w_down"]).to(device=device, dtype=sd).contiguous()}
+    st = HHBlockWeights(mixer.struct, _ptr(t["norm1"]), _ptr(t["norm2"]), _ptr(t["w_gate_up"]),
+                        _ptr(t["w_down"]), int(bw["d_ff"]))
+    return DeviceBlock(dims, mixer, t, st)
 
 
 class Workspace:
@@ -297,3 +348,73 @@ def hh_timing_read(max_stages: int = 32) -> dict:
     if n < 0:
         raise HHError("hh_timing_read", 4, "HIP error while reading stage events")
     return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(n)}
+
+
+# --------------------------------------------------------------------------
+# the block around the layer
+# --------------------------------------------------------------------------
+def hh_block_meta_prefix(block: DeviceBlock, meta_tokens: torch.Tensor, ws=None, stream=None) -> dict:
+    """hh_block_meta_prefix: the layer's meta part for the block input R."""
+    dims = block.dims
+    dev = meta_tokens.device
+    sd = storage_dtype(dims)
+    G, m, hd, D, N, k = (dims.n_kv_heads, dims.n_meta, dims.head_dim, dims.d_inner,
+                         dims.d_state, dims.d_conv)
+    out = {"h0": torch.empty(D, N, dtype=torch.float32, device=dev),
+           "conv_tail": torch.empty(k - 1, D, dtype=torch.float32, device=dev)}
+    if block.kv_producer:
+        out["k"] = torch.empty(G, m, hd, dtype=sd, device=dev)
+        out["v"] = torch.empty(G, m, hd, dtype=sd, device=dev)
+    d = hh_dims(dims)
+    need = lib().hh_block_meta_prefix_workspace_size(ctypes.byref(d), int(block.kv_producer))
+    if ws is None:
+        ws = _default_ws.get(need, dev)
+    _check("hh_block_meta_prefix", lib().hh_block_meta_prefix(
+        ctypes.byref(d), ctypes.byref(block.struct), _ptr(meta_tokens), _ptr(out.get("k")),
+        _ptr(out.get("v")), _ptr(out["h0"]), _ptr(out["conv_tail"]), _ptr(ws), ws.numel(),
+        _stream(stream)))
+    return out
+
+
+def hh_block_prefill_workspace_size(block: DeviceBlock, batch: int, seqlen: int) -> int:
+    d = hh_dims(block.dims)
+    return lib().hh_block_prefill_workspace_size(ctypes.byref(d), block.d_ff, batch, seqlen,
+                                                 int(block.kv_producer))
+
+
+def hh_block_decode_workspace_size(block: DeviceBlock, batch: int, cap: int) -> int:
+    d = hh_dims(block.dims)
+    return lib().hh_block_decode_workspace_size(ctypes.byref(d), block.d_ff, batch, cap,
+                                                int(block.kv_producer))
+
+
+def hh_block_prefill(block: DeviceBlock, x: torch.Tensor, meta: HHMeta, window: int,
+                     is_global: bool, out: torch.Tensor, kv: Optional[HHKV] = None,
+                     state_h: Optional[torch.Tensor] = None,
+                     state_conv: Optional[torch.Tensor] = None, ws=None, stream=None) -> None:
+    """hh_block_prefill on device tensors; x [B, n, d] -> out [B, n, d]."""
+    B, n, _ = x.shape
+    if ws is None:
+        ws = _default_ws.get(hh_block_prefill_workspace_size(block, B, n), x.device)
+    d = hh_dims(block.dims)
+    st = HHSsmState(_ptr(state_h), _ptr(state_conv))
+    _check("hh_block_prefill", lib().hh_block_prefill(
+        ctypes.byref(d), ctypes.byref(block.struct), _ptr(x), B, n, ctypes.byref(meta),
+        int(window), int(bool(is_global)), _ptr(out), ctypes.byref(kv) if kv is not None else None,
+        ctypes.byref(st), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def hh_block_decode_step(block: DeviceBlock, x_t: torch.Tensor, meta: HHMeta, window: int,
+                         is_global: bool, kv: HHKV, state_h: torch.Tensor,
+                         state_conv: torch.Tensor, out: torch.Tensor, ws=None, stream=None) -> None:
+    """hh_block_decode_step on device tensors; x_t [B, d] -> out [B, d]."""
+    B = x_t.shape[0]
+    if ws is None:
+        ws = _default_ws.get(hh_block_decode_workspace_size(block, B, kv.cap), x_t.device)
+    d = hh_dims(block.dims)
+    st = HHSsmState(_ptr(state_h), _ptr(state_conv))
+    _check("hh_block_decode_step", lib().hh_block_decode_step(
+        ctypes.byref(d), ctypes.byref(block.struct), _ptr(x_t), B, ctypes.byref(meta),
+        int(window), int(bool(is_global)), ctypes.byref(kv), ctypes.byref(st), _ptr(out),
+        _ptr(ws), ws.numel(), _stream(stream)))
+

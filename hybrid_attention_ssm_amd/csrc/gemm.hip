@@ -260,13 +260,15 @@ gemm_f32_tiled(const float *__restrict__ A, const float *__restrict__ B, int M, 
     }
     __syncthreads();
   }
+  // each thread's 4 columns form one epilogue group (N % 4 == 0)
+  const int col = n0 + tx * 4;
+  if (col >= N) return;
+  const typename Epi::template Col<4> ci = epi.template col_info<4>(col);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = m0 + ty * 4 + i, col = n0 + tx * 4 + j;
-      if (row < M && col < N) epi(row, col, acc[i][j]);
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + ty * 4 + i;
+    if (row < M) epi.template store<4>(row, ci, acc[i]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -278,9 +280,6 @@ gemm_f32_tiled(const float *__restrict__ A, const float *__restrict__ B, int M, 
 template <class T>
 struct InProjEpi {
   InProjOut e;
-  __device__ __forceinline__ void operator()(int row, int col, float v) const {
-    inproj_store<T>(e, row, col, v);
-  }
   template <int W> using Col = ColInfo<W>;
   template <int W>
   __device__ __forceinline__ Col<W> col_info(int col) const { return inproj_col<W>(e, col); }
@@ -294,15 +293,49 @@ template <class T>
 struct StoreEpi {
   T *out;
   int ld;
-  __device__ __forceinline__ void operator()(int row, int col, float v) const {
-    out[(size_t)row * ld + col] = from_f32<T>(v);
-  }
   template <int W> using Col = int;
   template <int W>
   __device__ __forceinline__ int col_info(int col) const { return col; }
   template <int W>
   __device__ __forceinline__ void store(int row, int col, const float v[W]) const {
     storeW_T<T, W>(out + (size_t)row * ld + col, v);
+  }
+};
+
+// out = sum + resid, both [M, ld] (the block's residual add)
+template <class T>
+struct ResidEpi {
+  T *out;
+  const T *resid;
+  int ld;
+  template <int W> using Col = int;
+  template <int W>
+  __device__ __forceinline__ int col_info(int col) const { return col; }
+  template <int W>
+  __device__ __forceinline__ void store(int row, int col, const float v[W]) const {
+    float r[W];
+    loadW_T<T, W>(resid + (size_t)row * ld + col, r);
+#pragma unroll
+    for (int i = 0; i < W; ++i) r[i] += v[i];
+    storeW_T<T, W>(out + (size_t)row * ld + col, r);
+  }
+};
+
+// Columns arrive as (gate, up) pairs (the block MLP's interleaved rows):
+// h[row, col/2 + i] = SiLU(gate_i) * up_i, W/2 outputs per group.
+template <class T>
+struct GluEpi {
+  T *h;
+  int ld;   // d_ff
+  template <int W> using Col = int;
+  template <int W>
+  __device__ __forceinline__ int col_info(int col) const { return col; }
+  template <int W>
+  __device__ __forceinline__ void store(int row, int col, const float v[W]) const {
+    float o[W / 2];
+#pragma unroll
+    for (int i = 0; i < W / 2; ++i) o[i] = silu_f(v[2 * i]) * v[2 * i + 1];
+    storeW_T<T, W / 2>(h + (size_t)row * ld + col / 2, o);
   }
 };
 
@@ -414,6 +447,7 @@ size_t skinny_part_bytes(int M, int K, int N) {
 template <class Epi>
 static hipError_t run_f32(const float *A, int M, int K, const float *B, int N, const Epi &epi,
                           hipStream_t s) {
+  if (N % 4) return hipErrorInvalidValue;   // epilogue groups of 4 columns
   dim3 grid((N + 63) / 64, (M + 63) / 64);
   hipLaunchKernelGGL((gemm_f32_tiled<Epi>), grid, dim3(256), 0, s, A, B, M, N, K, epi);
   return hipGetLastError();
@@ -431,13 +465,27 @@ hipError_t launch_inproj<float>(const float *x, int M, int K, const float *w, in
 }
 template <>
 hipError_t launch_outproj<bf16>(const bf16 *f, int M, int K, const bf16 *w, int Ncols, bf16 *out,
-                                float *part, hipStream_t s) {
+                                const bf16 *resid, float *part, hipStream_t s) {
+  if (resid) return run_bf16_auto(f, M, K, w, Ncols, ResidEpi<bf16>{out, resid, Ncols}, part, s);
   return run_bf16_auto(f, M, K, w, Ncols, StoreEpi<bf16>{out, Ncols}, part, s);
 }
 template <>
 hipError_t launch_outproj<float>(const float *f, int M, int K, const float *w, int Ncols,
-                                 float *out, float *, hipStream_t s) {
+                                 float *out, const float *resid, float *, hipStream_t s) {
+  if (resid) return run_f32(f, M, K, w, Ncols, ResidEpi<float>{out, resid, Ncols}, s);
   return run_f32(f, M, K, w, Ncols, StoreEpi<float>{out, Ncols}, s);
+}
+template <>
+hipError_t launch_mlp_gate_up<bf16>(const bf16 *x, int M, int K, const bf16 *w, int Ncols,
+                                    bf16 *h, float *part, hipStream_t s) {
+  if (Ncols % 8) return hipErrorInvalidValue;
+  return run_bf16_auto(x, M, K, w, Ncols, GluEpi<bf16>{h, Ncols / 2}, part, s);
+}
+template <>
+hipError_t launch_mlp_gate_up<float>(const float *x, int M, int K, const float *w, int Ncols,
+                                     float *h, float *, hipStream_t s) {
+  if (Ncols % 8) return hipErrorInvalidValue;
+  return run_f32(x, M, K, w, Ncols, GluEpi<float>{h, Ncols / 2}, s);
 }
 
 }  // namespace hh

@@ -204,7 +204,8 @@ hh_status run_inproj(const Shape &s, const hh_weights *w, const void *x, int M,
 template <class T>
 hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, int n,
                     const hh_meta *meta, int window, int is_global, void *out, hh_kv *kv,
-                    hh_ssm_state *state, void *ws, const PrefillLayout &L, hipStream_t st) {
+                    hh_ssm_state *state, void *ws, const PrefillLayout &L, hipStream_t st,
+                    const void *resid = nullptr) {
   const int rows = B * n;
   const bool prod = w->kv_producer != 0;
   void *kfull = prod ? ((kv && kv->full_k) ? kv->full_k : at(ws, L.off[HH_WS_K])) : kv->full_k;
@@ -269,7 +270,7 @@ hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, i
     Stage sg(st, "outproj");
     err = hh::launch_outproj<T>(static_cast<const T *>(na.f), rows, s.Wa + s.D,
                                 static_cast<const T *>(w->w_out), s.d, static_cast<T *>(out),
-                                part_ptr(ws, L.off[HH_WS_GEMM]), st);
+                                static_cast<const T *>(resid), part_ptr(ws, L.off[HH_WS_GEMM]), st);
   }
   if (err != hipSuccess) return hip_fail(err, "output projection");
 
@@ -304,7 +305,7 @@ hh_status meta_prefix_t(const Shape &s, const hh_weights *w, const void *R, void
 template <class T>
 hh_status decode_t(const Shape &s, const hh_weights *w, const void *x, int B, const hh_meta *meta,
                    int window, int is_global, hh_kv *kv, hh_ssm_state *state, void *out, void *ws,
-                   const DecodeLayout &L, hipStream_t st) {
+                   const DecodeLayout &L, hipStream_t st, const void *resid = nullptr) {
   const bool prod = w->kv_producer != 0;
   hh::InProjOut e{};
   e.mode = hh::EPI_DECODE;
@@ -366,7 +367,7 @@ hh_status decode_t(const Shape &s, const hh_weights *w, const void *x, int B, co
     Stage sg(st, "decode_outproj");
     err = hh::launch_outproj<T>(static_cast<const T *>(na.f), B, s.Wa + s.D,
                                 static_cast<const T *>(w->w_out), s.d, static_cast<T *>(out),
-                                part_ptr(ws, L.gemm), st);
+                                static_cast<const T *>(resid), part_ptr(ws, L.gemm), st);
   }
   if (err != hipSuccess) return hip_fail(err, "decode output projection");
   return HH_OK;
@@ -375,6 +376,170 @@ hh_status decode_t(const Shape &s, const hh_weights *w, const void *x, int B, co
 int max_real_keys(const hh_kv *kv, int window, int is_global) {
   if (is_global || !kv->is_ring) return kv->cap;
   return std::min(window, kv->cap);
+}
+
+
+// ---- argument checks shared by the layer and block entry points -----------
+hh_status check_prefill_call(const hh_dims *dims, const hh_weights *w, const void *x, int batch,
+                             int seqlen, const hh_meta *meta, int window, int is_global,
+                             const void *out, const hh_kv *kv, Shape &s) {
+  hh_status r = check_dims(dims, w ? w->kv_producer : 1, s);
+  if (r != HH_OK) return r;
+  if ((r = check_weights(w, s)) != HH_OK) return r;
+  if (batch <= 0 || seqlen <= 0) return fail(HH_ERR_INVALID_ARG, "batch and seqlen must be positive");
+  if ((long long)batch * seqlen > (1LL << 30))
+    return fail(HH_ERR_UNSUPPORTED, "batch*seqlen above 2^30 tokens");
+  if (!is_global && window < 1) return fail(HH_ERR_INVALID_ARG, "window must be >= 1");
+  if (!aligned16(x) || !aligned16(out)) return fail(HH_ERR_INVALID_ARG, "x/out NULL or not 16-byte aligned");
+  if (!meta) return fail(HH_ERR_INVALID_ARG, "meta is NULL");
+  if (s.m > 0 && (!aligned16(meta->k) || !aligned16(meta->v)))
+    return fail(HH_ERR_INVALID_ARG, "meta k/v NULL or not 16-byte aligned");
+  if (!w->kv_producer) {
+    if (!kv || !aligned16(kv->full_k) || !aligned16(kv->full_v))
+      return fail(HH_ERR_INVALID_ARG, "a consumer layer needs its producer's full_k/full_v");
+  }
+  if (w->kv_producer && kv) {
+    if ((kv->full_k && !aligned16(kv->full_k)) || (kv->full_v && !aligned16(kv->full_v)) ||
+        (!kv->full_k) != (!kv->full_v))
+      return fail(HH_ERR_INVALID_ARG, "full_k/full_v must both be NULL or both 16-byte aligned");
+    if ((!kv->cache_k) != (!kv->cache_v))
+      return fail(HH_ERR_INVALID_ARG, "cache_k/cache_v must both be set or both NULL");
+    if (kv->cache_k) {
+      if (kv->cap < 1) return fail(HH_ERR_INVALID_ARG, "cache cap must be >= 1");
+      if (kv->is_ring && is_global) return fail(HH_ERR_INVALID_ARG, "a global layer needs a linear cache");
+      if (kv->is_ring && window > kv->cap)
+        return fail(HH_ERR_INVALID_ARG, "ring cache cap %d below window %d", kv->cap, window);
+    }
+  }
+  return HH_OK;
+}
+
+hh_status check_decode_call(const hh_dims *dims, const hh_weights *w, const void *x_t, int batch,
+                            const hh_meta *meta, int window, int is_global, const hh_kv *kv,
+                            const hh_ssm_state *state, const void *out, Shape &s) {
+  hh_status r = check_dims(dims, w ? w->kv_producer : 1, s);
+  if (r != HH_OK) return r;
+  if ((r = check_weights(w, s)) != HH_OK) return r;
+  if (batch <= 0) return fail(HH_ERR_INVALID_ARG, "batch must be positive");
+  if (!is_global && window < 1) return fail(HH_ERR_INVALID_ARG, "window must be >= 1");
+  if (!aligned16(x_t) || !aligned16(out)) return fail(HH_ERR_INVALID_ARG, "x_t/out NULL or not 16-byte aligned");
+  if (!meta) return fail(HH_ERR_INVALID_ARG, "meta is NULL");
+  if (s.m > 0 && (!aligned16(meta->k) || !aligned16(meta->v)))
+    return fail(HH_ERR_INVALID_ARG, "meta k/v NULL or not 16-byte aligned");
+  if (!kv || !aligned16(kv->cache_k) || !aligned16(kv->cache_v) || !kv->len)
+    return fail(HH_ERR_INVALID_ARG, "decode needs cache_k, cache_v and len");
+  if (kv->cap < 1) return fail(HH_ERR_INVALID_ARG, "cache cap must be >= 1");
+  if (kv->is_ring && is_global) return fail(HH_ERR_INVALID_ARG, "a global layer needs a linear cache");
+  if (kv->is_ring && window > kv->cap)
+    return fail(HH_ERR_INVALID_ARG, "ring cache cap %d below window %d", kv->cap, window);
+  if (!state || !aligned16(state->h) || !state->conv)
+    return fail(HH_ERR_INVALID_ARG, "decode needs the SSM state h and conv");
+  return HH_OK;
+}
+
+
+// ---- the block around the layer -------------------------------------------
+struct BlockLayout {
+  size_t n1, x1, n2, h, part, total;
+};
+
+// The block's buffers follow the layer's workspace (base bytes).
+BlockLayout block_layout(const Shape &s, size_t base, size_t T, int d_ff) {
+  BlockLayout L;
+  size_t o = up256(base);
+  auto take = [&](size_t &dst, size_t bytes) { dst = o; o = up256(o + bytes); };
+  take(L.n1, T * s.d * s.es);
+  take(L.x1, T * s.d * s.es);
+  take(L.n2, T * s.d * s.es);
+  take(L.h, T * d_ff * s.es);
+  const size_t gp = s.dtype == HH_BF16 ? std::max(hh::skinny_part_bytes((int)T, s.d, 2 * d_ff),
+                                                  hh::skinny_part_bytes((int)T, d_ff, s.d))
+                                       : 0;
+  L.part = SIZE_MAX;
+  if (gp) take(L.part, gp);
+  L.total = o;
+  return L;
+}
+
+hh_status check_block_weights(const hh_block_weights *w) {
+  if (!w) return fail(HH_ERR_INVALID_ARG, "block weights are NULL");
+  if (!w->norm1 || !w->norm2) return fail(HH_ERR_INVALID_ARG, "norm1/norm2 NULL");
+  if (!aligned16(w->w_gate_up) || !aligned16(w->w_down))
+    return fail(HH_ERR_INVALID_ARG, "w_gate_up/w_down NULL or not 16-byte aligned");
+  if (w->d_ff <= 0 || w->d_ff % 4)
+    return fail(HH_ERR_UNSUPPORTED, "d_ff %d is not a positive multiple of 4", w->d_ff);
+  return HH_OK;
+}
+
+// the bf16 GEMMs walk K in 64-wide k-tiles: the down projection's K is d_ff
+hh_status check_block_shape(const hh_block_weights *w, const Shape &s) {
+  if (s.dtype == HH_BF16 && w->d_ff % 64)
+    return fail(HH_ERR_UNSUPPORTED, "bf16 path needs d_ff (%d) to be a multiple of 64", w->d_ff);
+  return HH_OK;
+}
+
+// out = x1 + MLP(g2 * rms(x1)), x1 already in the block workspace
+template <class T>
+hh_status block_mlp_t(const Shape &s, const hh_block_weights *w, int rows, void *ws,
+                      const BlockLayout &BL, void *out, hipStream_t st) {
+  const T *x1 = reinterpret_cast<const T *>(at(ws, BL.x1));
+  T *n2 = reinterpret_cast<T *>(at(ws, BL.n2));
+  T *h = reinterpret_cast<T *>(at(ws, BL.h));
+  float *part = part_ptr(ws, BL.part);
+  hipError_t err;
+  {
+    Stage sg(st, "block_norm2");
+    err = hh::launch_rmsnorm<T>(x1, w->norm2, n2, rows, s.d, s.eps, st);
+  }
+  if (err != hipSuccess) return hip_fail(err, "block pre-norm 2");
+  {
+    Stage sg(st, "mlp_gate_up");
+    err = hh::launch_mlp_gate_up<T>(n2, rows, s.d, static_cast<const T *>(w->w_gate_up),
+                                    2 * w->d_ff, h, part, st);
+  }
+  if (err != hipSuccess) return hip_fail(err, "MLP gate/up projection");
+  {
+    Stage sg(st, "mlp_down");
+    err = hh::launch_outproj<T>(h, rows, w->d_ff, static_cast<const T *>(w->w_down), s.d,
+                                static_cast<T *>(out), x1, part, st);
+  }
+  return err == hipSuccess ? HH_OK : hip_fail(err, "MLP down projection");
+}
+
+template <class T>
+hh_status block_norm1_t(const Shape &s, const hh_block_weights *w, const void *x, int rows, void *dst,
+                        hipStream_t st) {
+  Stage sg(st, "block_norm1");
+  hipError_t err = hh::launch_rmsnorm<T>(static_cast<const T *>(x), w->norm1, static_cast<T *>(dst), rows,
+                                         s.d, s.eps, st);
+  return err == hipSuccess ? HH_OK : hip_fail(err, "block pre-norm 1");
+}
+
+template <class T>
+hh_status block_prefill_t(const Shape &s, const hh_block_weights *w, const void *x, int B, int n,
+                          const hh_meta *meta, int window, int is_global, void *out, hh_kv *kv,
+                          hh_ssm_state *state, void *ws, const PrefillLayout &L,
+                          const BlockLayout &BL, hipStream_t st) {
+  const int rows = B * n;
+  hh_status r = block_norm1_t<T>(s, w, x, rows, at(ws, BL.n1), st);
+  if (r != HH_OK) return r;
+  r = prefill_t<T>(s, &w->mixer, at(ws, BL.n1), B, n, meta, window, is_global, at(ws, BL.x1), kv,
+                   state, ws, L, st, x);
+  if (r != HH_OK) return r;
+  return block_mlp_t<T>(s, w, rows, ws, BL, out, st);
+}
+
+template <class T>
+hh_status block_decode_t(const Shape &s, const hh_block_weights *w, const void *x, int B,
+                         const hh_meta *meta, int window, int is_global, hh_kv *kv,
+                         hh_ssm_state *state, void *out, void *ws, const DecodeLayout &L,
+                         const BlockLayout &BL, hipStream_t st) {
+  hh_status r = block_norm1_t<T>(s, w, x, B, at(ws, BL.n1), st);
+  if (r != HH_OK) return r;
+  r = decode_t<T>(s, &w->mixer, at(ws, BL.n1), B, meta, window, is_global, kv, state,
+                  at(ws, BL.x1), ws, L, st, x);
+  if (r != HH_OK) return r;
+  return block_mlp_t<T>(s, w, B, ws, BL, out, st);
 }
 
 }  // namespace
@@ -466,34 +631,8 @@ hh_status hh_prefill(const hh_dims *dims, const hh_weights *w, const void *x, in
                      void *out, hh_kv *kv, hh_ssm_state *state, void *ws, size_t ws_bytes,
                      void *stream) {
   Shape s;
-  hh_status r = check_dims(dims, w ? w->kv_producer : 1, s);
+  hh_status r = check_prefill_call(dims, w, x, batch, seqlen, meta, window, is_global, out, kv, s);
   if (r != HH_OK) return r;
-  if ((r = check_weights(w, s)) != HH_OK) return r;
-  if (batch <= 0 || seqlen <= 0) return fail(HH_ERR_INVALID_ARG, "batch and seqlen must be positive");
-  if ((long long)batch * seqlen > (1LL << 30))
-    return fail(HH_ERR_UNSUPPORTED, "batch*seqlen above 2^30 tokens");
-  if (!is_global && window < 1) return fail(HH_ERR_INVALID_ARG, "window must be >= 1");
-  if (!aligned16(x) || !aligned16(out)) return fail(HH_ERR_INVALID_ARG, "x/out NULL or not 16-byte aligned");
-  if (!meta) return fail(HH_ERR_INVALID_ARG, "meta is NULL");
-  if (s.m > 0 && (!aligned16(meta->k) || !aligned16(meta->v)))
-    return fail(HH_ERR_INVALID_ARG, "meta k/v NULL or not 16-byte aligned");
-  if (!w->kv_producer) {
-    if (!kv || !aligned16(kv->full_k) || !aligned16(kv->full_v))
-      return fail(HH_ERR_INVALID_ARG, "a consumer layer needs its producer's full_k/full_v");
-  }
-  if (w->kv_producer && kv) {
-    if ((kv->full_k && !aligned16(kv->full_k)) || (kv->full_v && !aligned16(kv->full_v)) ||
-        (!kv->full_k) != (!kv->full_v))
-      return fail(HH_ERR_INVALID_ARG, "full_k/full_v must both be NULL or both 16-byte aligned");
-    if ((!kv->cache_k) != (!kv->cache_v))
-      return fail(HH_ERR_INVALID_ARG, "cache_k/cache_v must both be set or both NULL");
-    if (kv->cache_k) {
-      if (kv->cap < 1) return fail(HH_ERR_INVALID_ARG, "cache cap must be >= 1");
-      if (kv->is_ring && is_global) return fail(HH_ERR_INVALID_ARG, "a global layer needs a linear cache");
-      if (kv->is_ring && window > kv->cap)
-        return fail(HH_ERR_INVALID_ARG, "ring cache cap %d below window %d", kv->cap, window);
-    }
-  }
   PrefillLayout L = prefill_layout(s, batch, seqlen);
   if (!ws || ws_bytes < L.total)
     return fail(HH_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, L.total);
@@ -507,23 +646,8 @@ hh_status hh_decode_step(const hh_dims *dims, const hh_weights *w, const void *x
                          const hh_meta *meta, int32_t window, int32_t is_global, hh_kv *kv,
                          hh_ssm_state *state, void *out, void *ws, size_t ws_bytes, void *stream) {
   Shape s;
-  hh_status r = check_dims(dims, w ? w->kv_producer : 1, s);
+  hh_status r = check_decode_call(dims, w, x_t, batch, meta, window, is_global, kv, state, out, s);
   if (r != HH_OK) return r;
-  if ((r = check_weights(w, s)) != HH_OK) return r;
-  if (batch <= 0) return fail(HH_ERR_INVALID_ARG, "batch must be positive");
-  if (!is_global && window < 1) return fail(HH_ERR_INVALID_ARG, "window must be >= 1");
-  if (!aligned16(x_t) || !aligned16(out)) return fail(HH_ERR_INVALID_ARG, "x_t/out NULL or not 16-byte aligned");
-  if (!meta) return fail(HH_ERR_INVALID_ARG, "meta is NULL");
-  if (s.m > 0 && (!aligned16(meta->k) || !aligned16(meta->v)))
-    return fail(HH_ERR_INVALID_ARG, "meta k/v NULL or not 16-byte aligned");
-  if (!kv || !aligned16(kv->cache_k) || !aligned16(kv->cache_v) || !kv->len)
-    return fail(HH_ERR_INVALID_ARG, "decode needs cache_k, cache_v and len");
-  if (kv->cap < 1) return fail(HH_ERR_INVALID_ARG, "cache cap must be >= 1");
-  if (kv->is_ring && is_global) return fail(HH_ERR_INVALID_ARG, "a global layer needs a linear cache");
-  if (kv->is_ring && window > kv->cap)
-    return fail(HH_ERR_INVALID_ARG, "ring cache cap %d below window %d", kv->cap, window);
-  if (!state || !aligned16(state->h) || !state->conv)
-    return fail(HH_ERR_INVALID_ARG, "decode needs the SSM state h and conv");
   DecodeLayout L = decode_layout(s, batch, max_real_keys(kv, window, is_global));
   if (!ws || ws_bytes < L.total)
     return fail(HH_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, L.total);
@@ -531,6 +655,102 @@ hh_status hh_decode_step(const hh_dims *dims, const hh_weights *w, const void *x
   return s.dtype == HH_BF16
              ? decode_t<hh::bf16>(s, w, x_t, batch, meta, window, is_global, kv, state, out, ws, L, st)
              : decode_t<float>(s, w, x_t, batch, meta, window, is_global, kv, state, out, ws, L, st);
+}
+
+size_t hh_block_meta_prefix_workspace_size(const hh_dims *dims, int32_t kv_producer) {
+  Shape s;
+  if (!dims || dims->n_meta <= 0 || check_dims(dims, kv_producer, s) != HH_OK) return 0;
+  return up256(prefill_layout(s, 1, s.m).total) + (size_t)s.m * s.d * s.es;
+}
+
+hh_status hh_block_meta_prefix(const hh_dims *dims, const hh_block_weights *w,
+                               const void *meta_tokens, void *meta_k, void *meta_v, float *h0,
+                               float *conv_tail, void *ws, size_t ws_bytes, void *stream) {
+  hh_status r = check_block_weights(w);
+  if (r != HH_OK) return r;
+  Shape s;
+  if ((r = check_dims(dims, w->mixer.kv_producer, s)) != HH_OK) return r;
+  if ((r = check_weights(&w->mixer, s)) != HH_OK) return r;
+  if ((r = check_block_shape(w, s)) != HH_OK) return r;
+  if (s.m <= 0) return fail(HH_ERR_INVALID_ARG, "n_meta must be positive for hh_block_meta_prefix");
+  if (!aligned16(meta_tokens)) return fail(HH_ERR_INVALID_ARG, "meta_tokens NULL or not 16-byte aligned");
+  if (s.KV && (!meta_k || !meta_v)) return fail(HH_ERR_INVALID_ARG, "meta_k/meta_v NULL for a producer layer");
+  if (!h0 || !conv_tail) return fail(HH_ERR_INVALID_ARG, "h0/conv_tail NULL");
+  PrefillLayout L = prefill_layout(s, 1, s.m);
+  const size_t off = up256(L.total), need = off + (size_t)s.m * s.d * s.es;
+  if (!ws || ws_bytes < need) return fail(HH_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void *rn = at(ws, off);
+  if (s.dtype == HH_BF16) {
+    if ((r = block_norm1_t<hh::bf16>(s, w, meta_tokens, s.m, rn, st)) != HH_OK) return r;
+    return meta_prefix_t<hh::bf16>(s, &w->mixer, rn, meta_k, meta_v, h0, conv_tail, ws, L, st);
+  }
+  if ((r = block_norm1_t<float>(s, w, meta_tokens, s.m, rn, st)) != HH_OK) return r;
+  return meta_prefix_t<float>(s, &w->mixer, rn, meta_k, meta_v, h0, conv_tail, ws, L, st);
+}
+
+size_t hh_block_prefill_workspace_size(const hh_dims *dims, int32_t d_ff, int32_t batch,
+                                       int32_t seqlen, int32_t kv_producer) {
+  Shape s;
+  if (check_dims(dims, kv_producer, s) != HH_OK || batch <= 0 || seqlen <= 0 || d_ff <= 0 ||
+      d_ff % (s.dtype == HH_BF16 ? 64 : 4))
+    return 0;
+  return block_layout(s, prefill_layout(s, batch, seqlen).total, (size_t)batch * seqlen, d_ff).total;
+}
+
+hh_status hh_block_prefill(const hh_dims *dims, const hh_block_weights *w, const void *x,
+                           int32_t batch, int32_t seqlen, const hh_meta *meta, int32_t window,
+                           int32_t is_global, void *out, hh_kv *kv, hh_ssm_state *state, void *ws,
+                           size_t ws_bytes, void *stream) {
+  hh_status r = check_block_weights(w);
+  if (r != HH_OK) return r;
+  Shape s;
+  r = check_prefill_call(dims, &w->mixer, x, batch, seqlen, meta, window, is_global, out, kv, s);
+  if (r != HH_OK) return r;
+  if ((r = check_block_shape(w, s)) != HH_OK) return r;
+  if (x == out) return fail(HH_ERR_INVALID_ARG, "out must not alias x");
+  PrefillLayout L = prefill_layout(s, batch, seqlen);
+  BlockLayout BL = block_layout(s, L.total, (size_t)batch * seqlen, w->d_ff);
+  if (!ws || ws_bytes < BL.total)
+    return fail(HH_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, BL.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return s.dtype == HH_BF16
+             ? block_prefill_t<hh::bf16>(s, w, x, batch, seqlen, meta, window, is_global, out, kv, state,
+                                         ws, L, BL, st)
+             : block_prefill_t<float>(s, w, x, batch, seqlen, meta, window, is_global, out, kv, state, ws,
+                                      L, BL, st);
+}
+
+size_t hh_block_decode_workspace_size(const hh_dims *dims, int32_t d_ff, int32_t batch, int32_t cap,
+                                      int32_t kv_producer) {
+  Shape s;
+  if (check_dims(dims, kv_producer, s) != HH_OK || batch <= 0 || cap <= 0 || d_ff <= 0 ||
+      d_ff % (s.dtype == HH_BF16 ? 64 : 4))
+    return 0;
+  return block_layout(s, decode_layout(s, batch, cap).total, (size_t)batch, d_ff).total;
+}
+
+hh_status hh_block_decode_step(const hh_dims *dims, const hh_block_weights *w, const void *x_t,
+                               int32_t batch, const hh_meta *meta, int32_t window, int32_t is_global,
+                               hh_kv *kv, hh_ssm_state *state, void *out, void *ws, size_t ws_bytes,
+                               void *stream) {
+  hh_status r = check_block_weights(w);
+  if (r != HH_OK) return r;
+  Shape s;
+  r = check_decode_call(dims, &w->mixer, x_t, batch, meta, window, is_global, kv, state, out, s);
+  if (r != HH_OK) return r;
+  if ((r = check_block_shape(w, s)) != HH_OK) return r;
+  if (x_t == out) return fail(HH_ERR_INVALID_ARG, "out must not alias x_t");
+  DecodeLayout L = decode_layout(s, batch, max_real_keys(kv, window, is_global));
+  BlockLayout BL = block_layout(s, L.total, (size_t)batch, w->d_ff);
+  if (!ws || ws_bytes < BL.total)
+    return fail(HH_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, BL.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return s.dtype == HH_BF16
+             ? block_decode_t<hh::bf16>(s, w, x_t, batch, meta, window, is_global, kv, state, out, ws, L,
+                                        BL, st)
+             : block_decode_t<float>(s, w, x_t, batch, meta, window, is_global, kv, state, out, ws, L, BL,
+                                     st);
 }
 
 }  // extern "C"

@@ -79,54 +79,6 @@ struct InProjOut {
   const float *dt_bias;       // [D]
 };
 
-template <class T>
-__device__ __forceinline__ void inproj_store(const InProjOut &e, int row, int col, float v) {
-  const int Wa = e.Wa, KV = e.KV, D = e.D;
-  if (col < Wa) {
-    reinterpret_cast<T *>(e.q)[(size_t)row * Wa + col] = from_f32<T>(v);
-    return;
-  }
-  col -= Wa;
-  if (col < 2 * KV) {
-    const bool isv = col >= KV;
-    const int c = isv ? col - KV : col;
-    const int g = c / e.hd, d = c - g * e.hd;
-    const int G = KV / e.hd;
-    const T tv = from_f32<T>(v);
-    if (e.mode == EPI_DECODE) {
-      const int p = e.len[row];
-      const int slot = e.is_ring ? p % e.cap : p;
-      if (p < 0 || (!e.is_ring && p >= e.cap)) return;
-      T *dst = reinterpret_cast<T *>(isv ? e.cache_v : e.cache_k);
-      dst[(((size_t)row * G + g) * e.cap + slot) * e.hd + d] = tv;
-      return;
-    }
-    const int n = e.n_rows_per_seq;
-    const int b = row / n, p = row - b * n;
-    T *full = reinterpret_cast<T *>(isv ? e.v_full : e.k_full);
-    full[(((size_t)b * G + g) * n + p) * e.hd + d] = tv;
-    if (e.mode == EPI_PREFILL && e.cache_k) {
-      bool keep;
-      int slot;
-      if (e.is_ring) { keep = p >= n - e.cap; slot = p % e.cap; }
-      else { keep = p < e.cap; slot = p; }
-      if (keep) {
-        T *dst = reinterpret_cast<T *>(isv ? e.cache_v : e.cache_k);
-        dst[(((size_t)b * G + g) * e.cap + slot) * e.hd + d] = tv;
-      }
-    }
-    return;
-  }
-  col -= 2 * KV;
-  if (col < D) { e.xs[(size_t)row * D + col] = v; return; }
-  col -= D;
-  if (col < D) { reinterpret_cast<T *>(e.z)[(size_t)row * D + col] = from_f32<T>(v); return; }
-  col -= D;
-  if (col < D) { e.dt[(size_t)row * D + col] = softplus_f(v + e.dt_bias[col]); return; }
-  col -= D;
-  e.bc[(size_t)row * 2 * e.N + col] = v;
-}
-
 // Store 8 consecutive columns col..col+7 of one row (col % 8 == 0).  Every
 // column-block boundary of the map is a multiple of 8, so the 8 values always
 // belong to one block and are written with vector stores.
@@ -143,11 +95,22 @@ __device__ __forceinline__ void store8_T(T *dst, const float v[8]) {
   }
 }
 
-// Store W (4 or 8) consecutive values (converted to T).
+// Store W (2, 4 or 8) consecutive values (converted to T).
 template <class T, int W>
 __device__ __forceinline__ void storeW_T(T *dst, const float v[W]) {
+  static_assert(W == 2 || W == 4 || W == 8, "group width");
   if constexpr (W == 8) {
     store8_T(dst, v);
+  } else if constexpr (W == 2) {
+    if constexpr (sizeof(T) == 2) {
+      typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+      bf16x2 o;
+      o[0] = (bf16)v[0];
+      o[1] = (bf16)v[1];
+      *reinterpret_cast<bf16x2 *>(dst) = o;
+    } else {
+      *reinterpret_cast<float2 *>(dst) = make_float2(v[0], v[1]);
+    }
   } else if constexpr (sizeof(T) == 2) {
     typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
     bf16x4 o;
@@ -156,6 +119,24 @@ __device__ __forceinline__ void storeW_T(T *dst, const float v[W]) {
     *reinterpret_cast<bf16x4 *>(dst) = o;
   } else {
     *reinterpret_cast<float4 *>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+// Load W (4 or 8) consecutive values as fp32.
+template <class T, int W>
+__device__ __forceinline__ void loadW_T(const T *src, float v[W]) {
+  static_assert(W == 4 || W == 8, "group width");
+  if constexpr (sizeof(T) == 2) {
+    typedef __attribute__((__vector_size__(W * sizeof(__bf16)))) __bf16 bfW;
+    const bfW x = *reinterpret_cast<const bfW *>(src);
+#pragma unroll
+    for (int i = 0; i < W; ++i) v[i] = (float)x[i];
+  } else {
+#pragma unroll
+    for (int q = 0; q < W / 4; ++q) {
+      const float4 x = reinterpret_cast<const float4 *>(src)[q];
+      v[4 * q] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
+    }
   }
 }
 
@@ -253,9 +234,15 @@ __device__ __forceinline__ void inproj_storeW(const InProjOut &e, int row, const
 template <class T>
 hipError_t launch_inproj(const T *x, int M, int K, const T *w, int Ncols,
                          const InProjOut &epi, float *part, hipStream_t s);
+// out = f w^T (+ resid when it is not null: the block's residual add)
 template <class T>
 hipError_t launch_outproj(const T *f, int M, int K, const T *w, int Ncols, T *out,
-                          float *part, hipStream_t s);
+                          const T *resid, float *part, hipStream_t s);
+// The block MLP's first projection: w holds gate and up rows alternately
+// (Ncols = 2 d_ff); h[M, d_ff] = SiLU(gate) * up
+template <class T>
+hipError_t launch_mlp_gate_up(const T *x, int M, int K, const T *w, int Ncols, T *h,
+                              float *part, hipStream_t s);
 size_t skinny_part_bytes(int M, int K, int N);
 
 struct AttnArgs {
@@ -304,6 +291,11 @@ struct NormArgs {
   int set_len_n, set_len_value;
 };
 template <class T> hipError_t launch_norm_fuse(const NormArgs &a, hipStream_t s);
+// out[r] = g * x[r] / sqrt(mean(x[r]^2) + eps) for each of `rows` rows of d
+// values (the block's pre-norms); d a multiple of 8 (bf16) or 4 (fp32)
+template <class T>
+hipError_t launch_rmsnorm(const T *x, const float *g, T *out, int rows, int d, float eps,
+                          hipStream_t s);
 
 struct DecodeAttnArgs {
   const void *q;           // [B, H*hd]

@@ -278,4 +278,74 @@ hipError_t launch_norm_fuse(const NormArgs &a, hipStream_t s) {
 template hipError_t launch_norm_fuse<float>(const NormArgs &, hipStream_t);
 template hipError_t launch_norm_fuse<bf16>(const NormArgs &, hipStream_t);
 
+// The block's pre-norm: out = g * x / sqrt(mean(x^2) + eps), fp32 statistics.
+// WPR waves per row (4 when there are few rows, so a decode batch still
+// spreads over the chip); each lane holds up to MAXC W-wide chunks of its
+// row in registers, so the row is read once.
+template <class T, int WPR, int MAXC>
+__global__ void __launch_bounds__(256) rmsnorm_rows(const T *__restrict__ x, const float *__restrict__ g,
+                                                    T *__restrict__ out, int rows, int d, float eps) {
+  constexpr int W = Vec<T>::W;
+  typedef typename Vec<T>::type V;
+  __shared__ float part[4];
+  const int wave = threadIdx.x >> 6;
+  const int row = blockIdx.x * (4 / WPR) + wave / WPR;
+  const int lane = (wave % WPR) * 64 + (threadIdx.x & 63);
+  const bool live = row < rows;
+  const T *xr = x + (size_t)(live ? row : 0) * d;
+  const int nc = d / W;
+  V v[MAXC];
+#pragma unroll
+  for (int j = 0; j < MAXC; ++j)   // indices past the row repeat its last chunk
+    v[j] = *reinterpret_cast<const V *>(xr + (size_t)min(lane + j * 64 * WPR, nc - 1) * W);
+  float ss = 0.0f;
+#pragma unroll
+  for (int j = 0; j < MAXC; ++j) {
+    float p = 0.0f;
+#pragma unroll
+    for (int e = 0; e < W; ++e) { const float f = to_f32(v[j][e]); p = fmaf(f, f, p); }
+    if (lane + j * 64 * WPR < nc) ss += p;
+  }
+  ss = wave_sum(ss);
+  if (WPR > 1) {
+    if ((threadIdx.x & 63) == 0) part[wave] = ss;
+    __syncthreads();
+    ss = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WPR; ++w) ss += part[w];
+  }
+  if (!live) return;
+  const float rs = 1.0f / sqrtf(ss / (float)d + eps);
+  T *o = out + (size_t)row * d;
+#pragma unroll
+  for (int j = 0; j < MAXC; ++j) {
+    const int c = lane + j * 64 * WPR;
+    if (c < nc) {
+      V r;
+#pragma unroll
+      for (int e = 0; e < W; ++e) r[e] = from_f32<T>(g[c * W + e] * to_f32(v[j][e]) * rs);
+      *reinterpret_cast<V *>(o + (size_t)c * W) = r;
+    }
+  }
+}
+
+template <class T>
+hipError_t launch_rmsnorm(const T *x, const float *g, T *out, int rows, int d, float eps,
+                          hipStream_t s) {
+  constexpr int W = Vec<T>::W;
+  constexpr int MAXC = 8;
+  if (d % W || rows <= 0) return hipErrorInvalidValue;
+  const int nc = d / W;
+  if (rows < 2048 || nc > MAXC * 64) {
+    if (nc > MAXC * 256) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((rmsnorm_rows<T, 4, MAXC>), dim3(rows), dim3(256), 0, s, x, g, out, rows, d, eps);
+  } else {
+    hipLaunchKernelGGL((rmsnorm_rows<T, 1, MAXC>), dim3((rows + 3) / 4), dim3(256), 0, s, x, g, out,
+                       rows, d, eps);
+  }
+  return hipGetLastError();
+}
+template hipError_t launch_rmsnorm<float>(const float *, const float *, float *, int, int, float, hipStream_t);
+template hipError_t launch_rmsnorm<bf16>(const bf16 *, const float *, bf16 *, int, int, float, hipStream_t);
+
 }  // namespace hh

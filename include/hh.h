@@ -197,6 +197,59 @@ hh_status hh_decode_step(const hh_dims *dims, const hh_weights *w,
                          hh_ssm_state *state, void *out, void *ws,
                          size_t ws_bytes, void *stream);
 
+/* ---- the block around the layer ---------------------------------------
+ * One block (Hymba paper, Fig. 4 and the architecture table's MLP width):
+ *   x1  = x + layer(g1 * rms(x))            (the layer above, meta rows g1 * rms(R))
+ *   out = x1 + W_down (SiLU(W_gate v) * (W_up v)),  v = g2 * rms(x1)
+ * with rms(v) = v / sqrt(mean(v^2) + rms_eps) per row, fp32 statistics.
+ *   mixer      the layer's weights (hh_weights)
+ *   norm1, norm2 [d_model] fp32 gains
+ *   w_gate_up  [2 d_ff, d_model] dtype; rows alternate gate, up (row 2i is the
+ *              gate of hidden unit i, row 2i+1 its up projection)
+ *   w_down     [d_model, d_ff] dtype
+ *   d_ff       MLP hidden width: a multiple of 4 (fp32) or 64 (bf16); 5504 at 1.5B */
+typedef struct {
+  hh_weights mixer;
+  const float *norm1, *norm2;
+  const void *w_gate_up;
+  const void *w_down;
+  int32_t d_ff;
+} hh_block_weights;
+
+/* Bytes of device workspace hh_block_meta_prefix needs (0 on invalid dims). */
+size_t hh_block_meta_prefix_workspace_size(const hh_dims *dims, int32_t kv_producer);
+
+/* hh_meta_prefix of the block's layer, whose meta rows are g1 * rms(R):
+ * meta_tokens [m, d_model] dtype are the block's meta inputs R. */
+hh_status hh_block_meta_prefix(const hh_dims *dims, const hh_block_weights *w,
+                               const void *meta_tokens, void *meta_k, void *meta_v,
+                               float *h0, float *conv_tail, void *ws, size_t ws_bytes,
+                               void *stream);
+
+/* Bytes of device workspace hh_block_prefill needs (0 on invalid arguments). */
+size_t hh_block_prefill_workspace_size(const hh_dims *dims, int32_t d_ff, int32_t batch,
+                                       int32_t seqlen, int32_t kv_producer);
+
+/* hh_prefill of one block: arguments as for hh_prefill, x and out the block's
+ * input and output [B, seqlen, d_model] dtype (out must not alias x); kv and
+ * state are the layer's.  The residual stream is kept in dtype. */
+hh_status hh_block_prefill(const hh_dims *dims, const hh_block_weights *w, const void *x,
+                           int32_t batch, int32_t seqlen, const hh_meta *meta,
+                           int32_t window, int32_t is_global, void *out, hh_kv *kv,
+                           hh_ssm_state *state, void *ws, size_t ws_bytes, void *stream);
+
+/* Bytes of device workspace hh_block_decode_step needs (0 on invalid arguments). */
+size_t hh_block_decode_workspace_size(const hh_dims *dims, int32_t d_ff, int32_t batch,
+                                      int32_t cap, int32_t kv_producer);
+
+/* hh_decode_step of one block: arguments as for hh_decode_step, x_t and out
+ * [B, d_model] dtype (out must not alias x_t). */
+hh_status hh_block_decode_step(const hh_dims *dims, const hh_block_weights *w,
+                               const void *x_t, int32_t batch, const hh_meta *meta,
+                               int32_t window, int32_t is_global, hh_kv *kv,
+                               hh_ssm_state *state, void *out, void *ws,
+                               size_t ws_bytes, void *stream);
+
 /* Workspace regions of hh_prefill, for inspecting intermediate results after
  * a call (test and debugging aid).  Fills offs[HH_WS_COUNT] with byte offsets
  * (SIZE_MAX for a region that is not used) and returns the total size. */

@@ -47,6 +47,12 @@ write it out; these are the plain pre-norm readings):
     rows enter the layer as g1 * norm(R)
   * MLP(v) = W_down (SiLU(W_gate v) * (W_up v)); W_gate and W_up are stored
     as one matrix whose rows alternate gate, up (row 2i gate i, 2i+1 up i)
+The block functions take an optional `store` map (default: none).  A path
+that keeps its activations in a 16-bit type rounds the values it hands from
+one kernel to the next (the layer and MLP inputs, the residual after the
+layer, the MLP hidden units) and feeds the rounded values to bf16 matrix
+units; passing that rounding as `store` gives the exact result of the same
+computation on those stored values.  The arithmetic itself is unchanged.
 """
 from __future__ import annotations
 
@@ -373,19 +379,23 @@ def rms_norm(v, g, eps):
     return _f64(g) * rms_normalize(_f64(v), eps)
 
 
-def mlp(v, w_gate_up, w_down):
+def _ident(v):
+    return v
+
+
+def mlp(v, w_gate_up, w_down, store=_ident):
     """W_down (SiLU(W_gate v) * W_up v); rows of w_gate_up alternate gate, up."""
     gu = _f64(v) @ _f64(w_gate_up).T
-    return (silu(gu[..., 0::2]) * gu[..., 1::2]) @ _f64(w_down).T
+    return _f64(store(silu(gu[..., 0::2]) * gu[..., 1::2])) @ _f64(w_down).T
 
 
-def block_meta_prefix(dims, bw, R):
+def block_meta_prefix(dims, bw, R, store=_ident):
     """meta_prefix of the block's layer, whose meta rows are g1 * norm(R)."""
     eps = dict(dims)["eps"]
-    return meta_prefix(dims, bw["mixer"], rms_norm(R, bw["norm1"], eps))
+    return meta_prefix(dims, bw["mixer"], store(rms_norm(R, bw["norm1"], eps)))
 
 
-def block_prefill(dims, bw, R, x, window, is_global, shared_kv=None, cache=None):
+def block_prefill(dims, bw, R, x, window, is_global, shared_kv=None, cache=None, store=_ident):
     """One block over the prompt x [B, n, d] with meta rows R [m, d].
 
     Returns prefill()'s dict for the layer (K/V, state, caches) with `out`
@@ -393,25 +403,26 @@ def block_prefill(dims, bw, R, x, window, is_global, shared_kv=None, cache=None)
     """
     eps = dict(dims)["eps"]
     x = _f64(x)
-    layer = prefill(dims, bw["mixer"], rms_norm(R, bw["norm1"], eps), rms_norm(x, bw["norm1"], eps),
-                    window, is_global, shared_kv=shared_kv, cache=cache)
-    x1 = x + layer["out"]
+    layer = prefill(dims, bw["mixer"], store(rms_norm(R, bw["norm1"], eps)),
+                    store(rms_norm(x, bw["norm1"], eps)), window, is_global,
+                    shared_kv=shared_kv, cache=cache)
+    x1 = _f64(store(x + layer["out"]))
     res = dict(layer)
     res["x1"] = x1
-    res["out"] = x1 + mlp(rms_norm(x1, bw["norm2"], eps), bw["w_gate_up"], bw["w_down"])
+    res["out"] = x1 + mlp(store(rms_norm(x1, bw["norm2"], eps)), bw["w_gate_up"], bw["w_down"], store)
     return res
 
 
 def block_decode_step(dims, bw, x_t, meta_k, meta_v, window, is_global, cache, h, conv,
-                      seqs=None):
+                      seqs=None, store=_ident):
     """One new token per sequence through one block (see decode_step)."""
     eps = dict(dims)["eps"]
     x_t = _f64(x_t)
     seqs = np.arange(x_t.shape[0]) if seqs is None else np.asarray(seqs, dtype=np.int64)
-    layer = decode_step(dims, bw["mixer"], rms_norm(x_t, bw["norm1"], eps), meta_k, meta_v,
+    layer = decode_step(dims, bw["mixer"], store(rms_norm(x_t, bw["norm1"], eps)), meta_k, meta_v,
                         window, is_global, cache, h, conv, seqs=seqs)
-    x1 = x_t[seqs] + layer["out"]
+    x1 = _f64(store(x_t[seqs] + layer["out"]))
     res = dict(layer)
-    res["out"] = x1 + mlp(rms_norm(x1, bw["norm2"], eps), bw["w_gate_up"], bw["w_down"])
+    res["out"] = x1 + mlp(store(rms_norm(x1, bw["norm2"], eps)), bw["w_gate_up"], bw["w_down"], store)
     return res
 

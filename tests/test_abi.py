@@ -117,3 +117,38 @@ def test_meta_prefix_validation():
     r = hb.lib().hh_meta_prefix(ctypes.byref(d), ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE,
                                 FAKE, 1 << 40, None)
     assert r == 1
+
+
+def _block_weights(d_ff=96, norm=FAKE, kv_producer=1):
+    return hb.HHBlockWeights(_weights(kv_producer), norm, norm, FAKE, FAKE, d_ff)
+
+
+def _call_block_prefill(dims, bw, B=1, n=64, ws_bytes=1 << 40, x=FAKE, out=FAKE + 4096):
+    d = hb.hh_dims(dims)
+    meta = hb.HHMeta(FAKE, FAKE, FAKE, FAKE)
+    st = hb.HHSsmState(None, None)
+    return hb.lib().hh_block_prefill(ctypes.byref(d), ctypes.byref(bw), x, B, n, ctypes.byref(meta),
+                                     16, 0, out, None, ctypes.byref(st), FAKE, ws_bytes, None)
+
+
+def test_block_workspace_sizes():
+    d = hb.hh_dims(TINY)
+    L = hb.lib()
+    layer = hb.hh_prefill_workspace_size(TINY, 1, 64)
+    blk = L.hh_block_prefill_workspace_size(ctypes.byref(d), 96, 1, 64, 1)
+    assert blk > layer
+    assert L.hh_block_prefill_workspace_size(ctypes.byref(d), 98, 1, 64, 1) == 0   # d_ff % 4
+    dec = L.hh_block_decode_workspace_size(ctypes.byref(d), 96, 4, 16, 1)
+    assert dec > hb.hh_decode_workspace_size(TINY, 4, 16)
+    assert L.hh_block_meta_prefix_workspace_size(ctypes.byref(d), 1) > hb.hh_meta_prefix_workspace_size(TINY)
+
+
+def test_block_validation():
+    assert _call_block_prefill(TINY, _block_weights(d_ff=6)) == 2
+    assert "d_ff" in hb.hh_last_error()
+    assert _call_block_prefill(TINY, _block_weights(norm=None)) == 1
+    assert _call_block_prefill(TINY, _block_weights(), out=FAKE) == 1          # out aliases x
+    assert "alias" in hb.hh_last_error()
+    d = hb.hh_dims(TINY)
+    need = hb.lib().hh_block_prefill_workspace_size(ctypes.byref(d), 96, 1, 64, 1)
+    assert _call_block_prefill(TINY, _block_weights(), ws_bytes=need - 1) == 3

@@ -1,0 +1,162 @@
+"""GPU parity of the block around the layer (pre-norms, residuals, SiLU-gated
+MLP) through the C ABI against the CPU oracle's block functions.
+
+Besides the output itself, the branch contribution out - x is compared with
+the oracle's, relative to its own RMS, so the residual stream cannot hide an
+error in the layer or the MLP.  That comparison allows, per element, for the
+two roundings of the residual stream to the storage type (x1 and out, each
+within half an ulp: 2^-9 of the value in bf16, 2^-24 in fp32).
+
+The bf16 path also feeds its matrix units bf16 operands: the layer's input
+(the pre-norm output) and the MLP's input and hidden units are rounded to
+bf16 between kernels.  The SSM state is sensitive to that input rounding at
+the bar's scale (its largest element error reaches ~9% of its RMS), so the
+layer's state, conv history and K/V are compared with the oracle evaluated on
+the same stored values (its `store` map, bf16 rounding from the input
+recipe).  The block output is compared with the exact oracle: rounding the
+oracle's residual stream at the same points would, where the two sides differ
+by a fraction of an ulp, round them apart rather than together.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from hybrid_attention_ssm_amd import binding as hb
+from hybrid_attention_ssm_amd.configs import (HYMBA_1P5B, MLP_HIDDEN_1P5B, MLP_HIDDEN_TINY, TINY,
+                                              LayerDims, PrefillWorkload)
+from hybrid_attention_ssm_amd.synth import block_inputs, round_bf16
+from oracle import hymba_ref as ref
+from tests.harness import TOL, np_of, rel_err
+
+pytestmark = pytest.mark.gpu
+
+SMALL_BF16 = LayerDims(d_model=256, n_heads=8, n_kv_heads=2, head_dim=64, d_inner=512,
+                       d_state=16, d_conv=4, n_meta=128, dtype="bf16")
+
+
+def _run_block_prefill(dims, inp, window, is_global, cache_cap=None):
+    sd = hb.storage_dtype(dims)
+    dev = "cuda"
+    x = inp["x"]
+    B, n, d = x.shape
+    G, hd, D, N, k = dims.n_kv_heads, dims.head_dim, dims.d_inner, dims.d_state, dims.d_conv
+    blk = hb.upload_block_weights(dims, inp["weights"])
+    meta = hb.hh_block_meta_prefix(blk, hb.to_device(inp["R"], sd))
+    xt = hb.to_device(x, sd)
+    out = torch.empty(B, n, d, dtype=sd, device=dev)
+    h = torch.empty(B, D, N, dtype=torch.float32, device=dev)
+    conv = torch.empty(B, k - 1, D, dtype=torch.float32, device=dev)
+    full_k = torch.empty(B, G, n, hd, dtype=sd, device=dev)
+    full_v = torch.empty_like(full_k)
+    ck = cv = length = None
+    if cache_cap:
+        ck = torch.zeros(B, G, cache_cap, hd, dtype=sd, device=dev)
+        cv = torch.zeros_like(ck)
+        length = torch.zeros(B, dtype=torch.int32, device=dev)
+    kv = hb.make_kv(full_k, full_v, ck, cv, length, cache_cap or 0, not is_global)
+    ms = hb.make_meta(meta["k"], meta["v"], meta["h0"], meta["conv_tail"])
+    hb.hh_block_prefill(blk, xt, ms, window, is_global, out, kv=kv, state_h=h, state_conv=conv)
+    torch.cuda.synchronize()
+    return dict(block=blk, meta=meta, out=out, h=h, conv=conv, full_k=full_k, cache_k=ck,
+                cache_v=cv, len=length, x=xt)
+
+
+def _store(dims):
+    return round_bf16 if dims.dtype == "bf16" else (lambda v: v)
+
+
+def _assert_block(got_out, want_out, x, tol, label, dtype):
+    e = rel_err(got_out, want_out)
+    half_ulp = 2.0 ** -9 if dtype == "bf16" else 2.0 ** -24
+    branch = want_out - x
+    excess = np.abs(got_out - want_out) - 2.0 * half_ulp * np.abs(want_out)
+    e_branch = float(np.maximum(excess, 0.0).max()) / float(np.sqrt(np.mean(branch * branch)))
+    print(f"  {label}: err out={e:.2e} branches={e_branch:.2e} (beyond storage rounding)", flush=True)
+    assert e <= tol and e_branch <= tol
+
+
+@pytest.mark.parametrize("dims,d_ff,B,n,window,is_global", [
+    (TINY, MLP_HIDDEN_TINY, 2, 40, 16, False),
+    (TINY, MLP_HIDDEN_TINY, 1, 33, 16, True),
+    (SMALL_BF16, 256, 2, 150, 64, False),
+    (SMALL_BF16, 256, 1, 97, 64, True),
+])
+def test_block_prefill_matches_oracle(dims, d_ff, B, n, window, is_global):
+    print(f"case block {dims.dtype} d_ff={d_ff} B={B} n={n} W={window} global={is_global}", flush=True)
+    inp = block_inputs(PrefillWorkload("blk", 50, dims, B, n, window, is_global), d_ff)
+    want = ref.block_prefill(dims.as_dict(), inp["weights"], inp["R"], inp["x"], window, is_global)
+    stored = ref.block_prefill(dims.as_dict(), inp["weights"], inp["R"], inp["x"], window, is_global,
+                               store=_store(dims))
+    got = _run_block_prefill(dims, inp, window, is_global)
+    tol = TOL[dims.dtype]
+    _assert_block(np_of(got["out"]), want["out"], inp["x"].astype(np.float64), tol, "prefill", dims.dtype)
+    e_h = rel_err(np_of(got["h"]), stored["h"])
+    print(f"  state err (stored-operand oracle) {e_h:.2e}, exact oracle {rel_err(np_of(got['h']), want['h']):.2e}",
+          flush=True)
+    assert e_h <= tol
+    assert rel_err(np_of(got["conv"]), stored["conv_tail"]) <= tol
+    assert rel_err(np_of(got["full_k"]), stored["k_full"]) <= tol
+
+
+@pytest.mark.parametrize("dims,d_ff,n0,steps,window,is_global,cap", [
+    (TINY, MLP_HIDDEN_TINY, 10, 6, 8, False, 8),
+    (SMALL_BF16, 256, 60, 5, 64, False, 64),
+    (SMALL_BF16, 256, 40, 4, 64, True, 64),
+])
+def test_block_decode_matches_longer_prefill(dims, d_ff, n0, steps, window, is_global, cap):
+    """block prefill(n0) + k block decode steps == oracle block prefill(n0 + k)."""
+    print(f"case block decode {dims.dtype} n0={n0} steps={steps} W={window} global={is_global} "
+          f"cap={cap}", flush=True)
+    B = 2
+    inp = block_inputs(PrefillWorkload("bd", n0 + steps, dims, B, n0 + steps, window, is_global), d_ff)
+    x = inp["x"]
+    want = ref.block_prefill(dims.as_dict(), inp["weights"], inp["R"], x, window, is_global)
+    stored = ref.block_prefill(dims.as_dict(), inp["weights"], inp["R"], x, window, is_global,
+                               store=_store(dims))
+    sub = dict(inp, x=x[:, :n0])
+    got = _run_block_prefill(dims, sub, window, is_global, cache_cap=cap)
+    sd = hb.storage_dtype(dims)
+    blk = got["block"]
+    kv = hb.make_kv(None, None, got["cache_k"], got["cache_v"], got["len"], cap, not is_global)
+    meta = hb.make_meta(got["meta"]["k"], got["meta"]["v"], None, None)
+    tol = TOL[dims.dtype]
+    for s in range(steps):
+        xt = hb.to_device(x[:, n0 + s], sd)
+        out = torch.empty(B, dims.d_model, dtype=sd, device="cuda")
+        hb.hh_block_decode_step(blk, xt, meta, window, is_global, kv, got["h"], got["conv"], out)
+        torch.cuda.synchronize()
+        _assert_block(np_of(out), want["out"][:, n0 + s], x[:, n0 + s].astype(np.float64), tol,
+                      f"step {s}", dims.dtype)
+    assert rel_err(np_of(got["h"]), stored["h"]) <= tol
+    assert (got["len"].cpu().numpy() == n0 + steps).all()
+
+
+def test_block_full_width_prefill_and_decode():
+    """Hymba-1.5B widths (d 1600, d_ff 5504): 1024 prompt tokens take the
+    256x256 GEMM path with the gated-MLP and residual epilogues; the decode
+    step after them takes the few-row path (split-K down projection)."""
+    dims, d_ff = HYMBA_1P5B, MLP_HIDDEN_1P5B
+    n, window, steps = 1024, 1024, 2
+    print(f"case block full width n={n} d_ff={d_ff}", flush=True)
+    inp = block_inputs(PrefillWorkload("bfw", n + steps, dims, 1, n + steps, window, False), d_ff, seed=7)
+    x = inp["x"]
+    want = ref.block_prefill(dims.as_dict(), inp["weights"], inp["R"], x, window, False,
+                             cache=dict(k=np.zeros((1, dims.n_kv_heads, window, dims.head_dim)),
+                                        v=np.zeros((1, dims.n_kv_heads, window, dims.head_dim)),
+                                        is_ring=True))
+    got = _run_block_prefill(dims, dict(inp, x=x[:, :n]), window, False, cache_cap=window)
+    tol = TOL[dims.dtype]
+    _assert_block(np_of(got["out"]), want["out"][:, :n], x[:, :n].astype(np.float64), tol, "prefill",
+                  dims.dtype)
+    sd = hb.storage_dtype(dims)
+    kv = hb.make_kv(None, None, got["cache_k"], got["cache_v"], got["len"], window, True)
+    meta = hb.make_meta(got["meta"]["k"], got["meta"]["v"], None, None)
+    for s in range(steps):
+        xt = hb.to_device(x[:, n + s], sd)
+        out = torch.empty(1, dims.d_model, dtype=sd, device="cuda")
+        hb.hh_block_decode_step(got["block"], xt, meta, window, False, kv, got["h"], got["conv"], out)
+        torch.cuda.synchronize()
+        _assert_block(np_of(out), want["out"][:, n + s], x[:, n + s].astype(np.float64), tol, f"step {s}",
+                      dims.dtype)

@@ -107,9 +107,10 @@ def _block_err():
 _orig_mlp = ref.mlp
 _orig_rms_norm = ref.rms_norm
 BLOCK_MUTANTS = {
-    "gate<->up": ("mlp", lambda v, w_gu, w_down: _orig_mlp(v, w_gu[np.arange(w_gu.shape[0]) ^ 1], w_down)),
-    "MLP without SiLU": ("mlp", lambda v, w_gu, w_down: ((np.asarray(v) @ w_gu.T)[..., 0::2]
-                                                         * (np.asarray(v) @ w_gu.T)[..., 1::2]) @ w_down.T),
+    "gate<->up": ("mlp", lambda v, w_gu, w_down, store=None:
+                  _orig_mlp(v, w_gu[np.arange(w_gu.shape[0]) ^ 1], w_down)),
+    "MLP without SiLU": ("mlp", lambda v, w_gu, w_down, store=None:
+                         ((np.asarray(v) @ w_gu.T)[..., 0::2] * (np.asarray(v) @ w_gu.T)[..., 1::2]) @ w_down.T),
     "norm gain dropped": ("rms_norm", lambda v, g, eps: _orig_rms_norm(v, np.ones_like(g), eps)),
     "norm gain applied twice": ("rms_norm", lambda v, g, eps: np.asarray(g) * _orig_rms_norm(v, g, eps)),
 }
