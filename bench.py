@@ -232,6 +232,96 @@ def bench_decode(args, hb, torch):
                 context=p_first)
 
 
+def bench_stack(args, hb, torch):
+    """One decode step through the 32 blocks of the 1.5B stack (layer, pre-norms,
+    residuals, MLP), batch 128 at context 8191+.  Weights, caches, meta K/V
+    and states are normal draws made on the device (seeded torch generator):
+    this line measures speed only; the block's parity is tested elsewhere."""
+    from hybrid_attention_ssm_amd.configs import STACK_DECODE
+    w = STACK_DECODE
+    dims, B, W = w.dims, w.batch, w.window
+    sd = hb.storage_dtype(dims)
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    d, D, N, k = dims.d_model, dims.d_inner, dims.d_state, dims.d_conv
+    G, hd, m, d_ff = dims.n_kv_heads, dims.head_dim, dims.n_meta, w.d_ff
+    f32 = torch.float32
+
+    def normal(shape, std=1.0, dtype=sd):
+        t = torch.randn(shape, generator=gen, device=dev, dtype=f32)
+        if std != 1.0:
+            t.mul_(std)
+        return t.to(dtype).contiguous()
+
+    steps = max(4, args.steps // 2)
+    slack = args.warmup + steps + 2
+    plan = w.layer_plan()
+    log(f"[bench] stack setup {w.name} ({len(plan)} blocks)")
+    caches = {}
+    for is_g, prod, name in plan:
+        if name in caches:
+            continue
+        cap = w.global_cap + slack if is_g else W
+        kk, vv = normal((B, G, cap, hd)), normal((B, G, cap, hd))
+        ln = torch.full((B,), w.context, dtype=torch.int32, device=dev)
+        mk, mv = normal((G, m, hd)), normal((G, m, hd))
+        caches[name] = dict(t=(kk, vv, ln, mk, mv), kv=hb.make_kv(None, None, kk, vv, ln, cap, not is_g),
+                            meta=hb.make_meta(mk, mv, None, None), cap=cap)
+    blocks = []
+    for is_g, prod, name in plan:
+        t = {"w_in": normal((dims.n_in(prod), d), (1.0 / d) ** 0.5),
+             "dt_bias": torch.full((D,), -4.0, dtype=f32, device=dev),
+             "A": -torch.rand((D, N), generator=gen, device=dev, dtype=f32).mul_(15.0).add_(1.0),
+             "conv_w": normal((D, k), (1.0 / k) ** 0.5, f32), "conv_b": torch.zeros(D, dtype=f32, device=dev),
+             "beta_attn": torch.ones(dims.attn_width, dtype=f32, device=dev),
+             "beta_ssm": torch.ones(D, dtype=f32, device=dev),
+             "w_out": normal((d, dims.fused_width), (1.0 / dims.fused_width) ** 0.5),
+             "norm1": torch.ones(d, dtype=f32, device=dev), "norm2": torch.ones(d, dtype=f32, device=dev),
+             "w_gate_up": normal((2 * d_ff, d), (1.0 / d) ** 0.5), "w_down": normal((d, d_ff), (1.0 / d_ff) ** 0.5),
+             "h": normal((B, D, N), 1.0, f32), "conv": normal((B, k - 1, D), 1.0, f32)}
+        P = hb._ptr
+        ws_ = hb.HHWeights(P(t["w_in"]), P(t["dt_bias"]), P(t["A"]), P(t["conv_w"]), P(t["conv_b"]),
+                           P(t["beta_attn"]), P(t["beta_ssm"]), P(t["w_out"]), 1 if prod else 0)
+        bs = hb.HHBlockWeights(ws_, P(t["norm1"]), P(t["norm2"]), P(t["w_gate_up"]), P(t["w_down"]), d_ff)
+        blk = hb.DeviceBlock(dims, hb.DeviceLayer(dims, t, ws_), t, bs)
+        blocks.append(dict(block=blk, is_global=is_g, cache=caches[name]))
+    wsz = max(hb.hh_block_decode_workspace_size(b["block"], B, b["cache"]["cap"]) for b in blocks)
+    ws = torch.empty(wsz, dtype=torch.uint8, device=dev)
+    xa, xb = normal((B, d)), torch.empty(B, d, dtype=sd, device=dev)
+
+    def step():
+        cur, nxt = xa, xb
+        for b in blocks:
+            c = b["cache"]
+            hb.hh_block_decode_step(b["block"], cur, c["meta"], W, b["is_global"], c["kv"],
+                                    b["block"].tensors["h"], b["block"].tensors["conv"], nxt, ws=ws)
+            cur, nxt = nxt, cur
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(steps):
+        step()
+    s1.record()
+    torch.cuda.synchronize()
+    ms_step = s0.elapsed_time(s1) / steps
+    p_mid = w.context + 2 + steps // 2
+    layers = [(g_, p_) for g_, p_, _ in plan]
+    mixer_bytes, _ = decode_bytes(dims, B, layers, p_mid, W, W, w.global_cap)
+    mlp_bytes = len(plan) * (3 * d * d_ff * 2 + 2 * d * 4 + B * d * 2 * 2)
+    tot = mixer_bytes + mlp_bytes
+    log(f"[bench] stack {ms_step:.3f} ms/step ({B / (ms_step * 1e-3):.0f} tok/s)")
+    return {"workload": f"{w.name}: {len(plan)} Hymba-1.5B-shaped blocks (full attention in blocks "
+                        f"{', '.join(map(str, w.global_layers))}; sliding-window blocks in KV-sharing pairs; "
+                        f"MLP {d_ff}), batch {B}, context {w.context}+",
+            "value": B / (ms_step * 1e-3), "unit": "tok/s", "ms_per_step": ms_step, "steps": steps,
+            "algorithmic_bytes_per_step": tot, "hbm_frac_step": tot / (ms_step * 1e-3) / HBM_PEAK,
+            "data": "synthetic, drawn on the device"}
+
+
 # ---------------------------------------------------------------------------
 def cpu_baseline(pre, dec, args):
     """The CPU oracle (as it stands) on a bounded sample of each workload."""
@@ -295,6 +385,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["prefill", "decode", "both"], default="both")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="skip the 32-block decode stack line")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192,
                     help="prefill tokens the CPU oracle runs (default: the whole 8k workload)")
     ap.add_argument("--cpu-sample-seqs", type=int, default=64,
@@ -328,6 +420,13 @@ def main():
 
     pre = bench_prefill(args, hb, torch) if args.only in ("prefill", "both") else None
     dec = bench_decode(args, hb, torch) if args.only in ("decode", "both") else None
+    stack = None
+    if args.only in ("decode", "both") and not args.no_stack:
+        try:
+            stack = bench_stack(args, hb, torch)
+        except Exception as exc:   # the stack line is extra: report it, keep the main line
+            log(f"[bench] stack failed: {exc!r}")
+            stack = {"error": repr(exc)}
 
     rec = {"metric": "hybrid-head layer prefill tok/s @8k + decode tok/s @B128; % of MFMA/HBM peak",
            "higher_is_better": True, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -395,6 +494,8 @@ def main():
             rec.update(value=d["value"], ms_per_step=d["ms_per_step"],
                        config={"workload": d["workload"], "global_batch": B, "seq_len": 1,
                                "parallelism": "none"})
+    if stack is not None:
+        rec["stack"] = stack
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         cb = cpu_baseline(pre, dec, args)
