@@ -18,6 +18,7 @@ namespace hh {
 
 namespace {
 constexpr int DSPLIT = 1280;  // most virtual keys per split
+constexpr int kNonTemporal = 2;   // cache-policy bits of a buffer load: nt (streaming)
 constexpr int DTHREADS = 256;
 
 template <class T> struct KV8;
@@ -393,10 +394,16 @@ __global__ void __launch_bounds__(DTHREADS) decode_attn_dma(DecodeAttnArgs a) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rvm, (lds_void *)(kdst + BLK + q * 1024), 16, voff[q], 0, 0, 0);
       }
     } else {
+      // The cache blocks are streamed (nt): a step reads 1.7 GB of K/V once or
+      // twice, far more than the 256 MB last-level cache, and allocating it
+      // there evicts the weights and SSM states the step's other kernels
+      // reuse.  Measured on the three-layer step: 476 -> 446 us (streaming the
+      // window rings too beats caching them for their consumer's second read).
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rkc, (lds_void *)(kdst + q * 1024), 16, voff[q], 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rvc, (lds_void *)(kdst + BLK + q * 1024), 16, voff[q], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rkc, (lds_void *)(kdst + q * 1024), 16, voff[q], 0, 0, kNonTemporal);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rvc, (lds_void *)(kdst + BLK + q * 1024), 16, voff[q], 0, 0,
+                                                 kNonTemporal);
       }
     }
   };
