@@ -353,22 +353,25 @@ struct PartialEpi {
   }
 };
 
-// Sum the split-K planes and hand each 8-column group to the real epilogue.
+// Sum the split-K planes and hand each 4-column group to the real epilogue.
+// Every split's load is issued before the first add (splits <= kMaxSplits).
+constexpr int kMaxSplits = 16;
 template <class Epi>
 __global__ void __launch_bounds__(256)
 reduce_splits(const float *__restrict__ part, int splits, int M, int N, Epi epi) {
-  const int groups = N / 8;
+  const int groups = N / 4;
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (long)M * groups) return;
-  const int row = (int)(idx / groups), col = (int)(idx % groups) * 8;
-  float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int sp = 0; sp < splits; ++sp) {
-    const float4 *p = reinterpret_cast<const float4 *>(part + ((size_t)sp * M + row) * N + col);
-    const float4 a = p[0], b = p[1];
-    v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
-    v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
-  }
-  epi.template store<8>(row, epi.template col_info<8>(col), v);
+  const int row = (int)(idx / groups), col = (int)(idx % groups) * 4;
+  float4 p[kMaxSplits];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp)
+    if (sp < splits) p[sp] = *reinterpret_cast<const float4 *>(part + ((size_t)sp * M + row) * N + col);
+  float v[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp)
+    if (sp < splits) { v[0] += p[sp].x; v[1] += p[sp].y; v[2] += p[sp].z; v[3] += p[sp].w; }
+  epi.template store<4>(row, epi.template col_info<4>(col), v);
 }
 
 template <class Cfg, class Epi>
@@ -401,7 +404,7 @@ static int skinny_splits(int M, int K, int N) {
   const int tiles = ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
   if (tiles >= 128) return 1;
   const int ktiles = K / C::BK;
-  const int splits = std::max(1, std::min(ktiles / 8, (kSkinnyTargetWG + tiles - 1) / tiles));
+  const int splits = std::max(1, std::min({ktiles / 8, (kSkinnyTargetWG + tiles - 1) / tiles, kMaxSplits}));
   const int kps = (ktiles + splits - 1) / splits;
   return (ktiles + kps - 1) / kps;   // no empty slice
 }
@@ -419,7 +422,7 @@ static hipError_t run_skinny_cfg(const bf16 *A, int M, int K, const bf16 *B, int
   PartialEpi pe{part, M, N};
   hipLaunchKernelGGL((gemm_bf16_lds<Cfg, PartialEpi>), dim3(grid, splits), dim3(Cfg::NT), 0, s, A,
                      B, M, N, K, pe);
-  const long groups = (long)M * (N / 8);
+  const long groups = (long)M * (N / 4);
   hipLaunchKernelGGL((reduce_splits<Epi>), dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s,
                      part, splits, M, N, epi);
   return hipGetLastError();
