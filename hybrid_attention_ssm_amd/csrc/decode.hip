@@ -665,8 +665,13 @@ __global__ void __launch_bounds__(256) decode_ssm_step(DecodeSsmArgs a) {
   const float4 Bq = *reinterpret_cast<const float4 *>(a.bc + (size_t)b * 2 * NS + 4 * q);
   const float4 Cq = *reinterpret_cast<const float4 *>(a.bc + (size_t)b * 2 * NS + NS + 4 * q);
   const float4 Aq = *reinterpret_cast<const float4 *>(a.A + (size_t)c * NS + 4 * q);
-  float4 *hp = reinterpret_cast<float4 *>(a.h + ci * NS + 4 * q);
-  float4 h = *hp;
+  // The state is read and written once per step, a step's worth of other
+  // traffic apart: stream it (nt) rather than let it displace the weights
+  // from the last-level cache.
+  typedef float f32v4 __attribute__((ext_vector_type(4)));
+  f32v4 *hp = reinterpret_cast<f32v4 *>(a.h + ci * NS + 4 * q);
+  const f32v4 hv = __builtin_nontemporal_load(hp);
+  float4 h = make_float4(hv.x, hv.y, hv.z, hv.w);
   // tap j multiplies window row j (tap K-1 the current row)
   float cv = cb;
 #pragma unroll
@@ -683,7 +688,7 @@ __global__ void __launch_bounds__(256) decode_ssm_step(DecodeSsmArgs a) {
   y = fmaf(Cq.w, h.w, y);
   y = quad_sum(y);
   if (!live) return;
-  *hp = h;
+  __builtin_nontemporal_store(f32v4{h.x, h.y, h.z, h.w}, hp);
   if (q == 0) {
     // a producer's new token joins the cache once this step's attention (an
     // earlier launch on the stream) has read len
