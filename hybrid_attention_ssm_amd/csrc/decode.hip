@@ -326,15 +326,16 @@ __global__ void __launch_bounds__(DTHREADS) decode_attn_mfma(DecodeAttnArgs a) {
 }
 
 // Same computation with both K and V blocks streamed into LDS by DMA
-// (buffer_load_dwordx4 ... lds: full 128-byte rows, no VGPR staging), two
-// stages per wave, so a wave's next block is in flight while it works on the
-// current one.  The two stages are separate LDS arrays and the loop alternates
-// between them explicitly: reads of one stage then provably do not alias the
-// DMA into the other, and the compiler waits only for the block being read.  Needs the meta count to be a multiple of the 32-key block so
-// that a block is all meta or all cache (one buffer descriptor per block).
+// (buffer_load_dwordx4 ... lds: full 128-byte rows, no VGPR staging), three
+// stages per wave, so a wave's next two blocks are in flight while it works
+// on the current one.  The stages are separate LDS arrays and the loop
+// rotates through them explicitly: reads of one stage then provably do not
+// alias the DMA into another, and the compiler waits only for the block being
+// read.  Needs the meta count to be a multiple of the 32-key block so that a
+// block is all meta or all cache (one buffer descriptor per block).
 // LDS rows are 128 B with 16-byte chunk c of row r stored at chunk c ^ (r % 8).
 template <int HPG, int NW>
-__global__ void __launch_bounds__(NW * 64) decode_attn_dma(DecodeAttnArgs a) {
+__device__ __forceinline__ void attn_dma_body(const DecodeAttnArgs &a, int sp, int g, int b) {
 #if defined(__HIP_DEVICE_COMPILE__)
   typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf8;
   typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -347,8 +348,8 @@ __global__ void __launch_bounds__(NW * 64) decode_attn_dma(DecodeAttnArgs a) {
   static_assert(NW * HD * SO * 4 <= NW * SLICE / 2, "merge buffer fits the slices");
   __shared__ __attribute__((aligned(16))) char lds0[NW * SLICE / 2];
   __shared__ __attribute__((aligned(16))) char lds1[NW * SLICE / 2];
+  __shared__ __attribute__((aligned(16))) char lds2[NW * SLICE / 2];
   __shared__ float sm[NW][16], sl[NW][16];
-  const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
@@ -372,6 +373,7 @@ __global__ void __launch_bounds__(NW * 64) decode_attn_dma(DecodeAttnArgs a) {
   const int wrap = a.is_ring ? a.cap : 0x7fffffff;
   char *slice0 = lds0 + wave * (SLICE / 2);
   char *slice1 = lds1 + wave * (SLICE / 2);
+  char *slice2 = lds2 + wave * (SLICE / 2);
   // DMA of the 32-key block at virtual key kb into stage st: instruction q moves
   // rows 8q .. 8q+7 (lane: row 8q + lane/8, chunk (lane%8) ^ row%8)
   auto issue = [&](int kb, char *kdst) {
@@ -420,7 +422,13 @@ __global__ void __launch_bounds__(NW * 64) decode_attn_dma(DecodeAttnArgs a) {
       qf[hh] = __builtin_bit_cast(bf8, v);
     }
   }
-  wait_vmcnt<0>();   // Q (and the first block) have landed before the loop
+  const int step = NW * DB;
+  if (kb + step < v1) {              // the second block follows Q
+    issue(kb + step, slice1);
+    wait_vmcnt<8>();                 // Q and the first block have landed
+  } else {
+    wait_vmcnt<0>();                 // Q (and the first block) have landed
+  }
   const float sl2 = kLog2e * 0.125f;   // log2(e) / sqrt(64)
   float m_run = -INFINITY, l_run = 0.0f;
   f32x4 o[4];
@@ -501,20 +509,35 @@ __global__ void __launch_bounds__(NW * 64) decode_attn_dma(DecodeAttnArgs a) {
     }
   };
   if (kb < v1) {
-    while (true) {
-      issue(kb + NW * DB < v1 ? kb + NW * DB : kb, slice1);
-      wait_vmcnt<8>();
+    // Three stages: blocks kb + step and kb + 2 step are in flight while kb is
+    // processed.  Past the end nothing is issued, and the wait allows only the
+    // blocks that really are in flight (each issue is 8 loads, in order).
+    auto refill_wait = [&](int nxt, char *dst) {
+      if (nxt < v1) {
+        issue(nxt, dst);
+        wait_vmcnt<16>();
+      } else if (nxt - step < v1) {
+        wait_vmcnt<8>();
+      } else {
+        wait_vmcnt<0>();
+      }
       __builtin_amdgcn_sched_barrier(0);
+    };
+    while (true) {
+      refill_wait(kb + 2 * step, slice2);
       process(kb, slice0);
       __builtin_amdgcn_sched_barrier(0);
-      kb += NW * DB;
+      kb += step;
       if (kb >= v1) break;
-      issue(kb + NW * DB < v1 ? kb + NW * DB : kb, slice0);
-      wait_vmcnt<8>();
-      __builtin_amdgcn_sched_barrier(0);
+      refill_wait(kb + 2 * step, slice0);
       process(kb, slice1);
       __builtin_amdgcn_sched_barrier(0);
-      kb += NW * DB;
+      kb += step;
+      if (kb >= v1) break;
+      refill_wait(kb + 2 * step, slice1);
+      process(kb, slice2);
+      __builtin_amdgcn_sched_barrier(0);
+      kb += step;
       if (kb >= v1) break;
     }
     wait_vmcnt<0>();
@@ -548,6 +571,12 @@ __global__ void __launch_bounds__(NW * 64) decode_attn_dma(DecodeAttnArgs a) {
     if (d == 0) { out[0] = M; out[1] = Ls; }
   }
 #endif
+}
+
+// grid (nsplit, G, B)
+template <int HPG, int NW>
+__global__ void __launch_bounds__(NW * 64) decode_attn_dma(DecodeAttnArgs a) {
+  attn_dma_body<HPG, NW>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // grid (B*H); hd threads
@@ -594,15 +623,15 @@ hipError_t launch_decode_attention(const DecodeAttnArgs &a, hipStream_t s, bool 
   // always leave per-split partials
   bool direct = false;
   if (sizeof(T) == 2 && a.hd == 64 && a.m % DB == 0 && a.split % DB == 0) {
-    // Few workgroups (a window's worth of keys per sequence and head): 2-wave
-    // workgroups, four to a CU, so the grid does not end in a partial round
-    // of 4-wave ones (window layer at batch 128: 34.9 -> 30.6 us)
-    const bool two = (long)a.B * a.G * a.nsplit < 2048;
+    // 2-wave workgroups with three 8 KB stages per wave (48 KB, three to a
+    // CU).  Against 4-wave workgroups with two stages: the window layer's
+    // 640-workgroup grid no longer ends in a partial round (34.9 -> 30.6 us),
+    // and the global layer keeps two blocks per wave in flight (231.6 ->
+    // 223.2 us at batch 128, context 8k).
     switch (hpg) {
 #define HH_DECD_CASE(W) \
       case W: \
-        if (two) hipLaunchKernelGGL((decode_attn_dma<W, 2>), grid, dim3(128), 0, s, a); \
-        else hipLaunchKernelGGL((decode_attn_dma<W, 4>), grid, dim3(DTHREADS), 0, s, a); \
+        hipLaunchKernelGGL((decode_attn_dma<W, 2>), grid, dim3(128), 0, s, a); \
         break;
       HH_DECD_CASE(1) HH_DECD_CASE(2) HH_DECD_CASE(3) HH_DECD_CASE(4)
       HH_DECD_CASE(5) HH_DECD_CASE(6) HH_DECD_CASE(7) HH_DECD_CASE(8)
@@ -639,8 +668,8 @@ template hipError_t launch_decode_attention<bf16>(const DecodeAttnArgs &, hipStr
 
 // ---------------------------------------------------------------------------
 // one SSM step: four lanes per (sequence, channel), four states each, so the
-// state, A and B/C move as contiguous 16-byte vectors across the quad.  It
-// runs after the step's attention and also advances a producer's len.
+// state, A and B/C move as contiguous 16-byte vectors across the quad.  (A
+// producer's len advances in the decode norm, after the step's attention.)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float quad_sum(float v) {
   // quad_perm [1,0,3,2] then [2,3,0,1]
@@ -649,9 +678,14 @@ __device__ __forceinline__ float quad_sum(float v) {
   return v;
 }
 
+// Thread t owns quad t: (sequence, channel) t / 4 and its states 4 (t % 4)
+// .. +3.  Every load is independent and issued before any arithmetic; one
+// quad per thread at full occupancy keeps the most loads in flight (two or
+// four quads per thread measured slower: 15.5 -> 16.7 / 20.2 us).
 template <class T, int K>
 __global__ void __launch_bounds__(256) decode_ssm_step(DecodeSsmArgs a) {
   constexpr int NS = 16;
+  typedef float f32v4 __attribute__((ext_vector_type(4)));
   const long t = (long)blockIdx.x * 256 + threadIdx.x;
   const long idx = t >> 2;                  // sequence * D + channel
   const int q = (int)(t & 3);               // states 4q .. 4q+3
@@ -659,7 +693,6 @@ __global__ void __launch_bounds__(256) decode_ssm_step(DecodeSsmArgs a) {
   const long ci = live ? idx : 0;
   const int b = (int)(ci / a.D), c = (int)(ci % a.D);
   float *conv = a.conv + (size_t)b * (K - 1) * a.D + c;
-  // every load is independent: issue them all before any arithmetic
   float win[K], wk[K];
 #pragma unroll
   for (int j = 0; j < K - 1; ++j) win[j] = conv[(size_t)j * a.D];   // oldest first
@@ -675,10 +708,8 @@ __global__ void __launch_bounds__(256) decode_ssm_step(DecodeSsmArgs a) {
   // The state is read and written once per step, a step's worth of other
   // traffic apart: stream it (nt) rather than let it displace the weights
   // from the last-level cache.
-  typedef float f32v4 __attribute__((ext_vector_type(4)));
   f32v4 *hp = reinterpret_cast<f32v4 *>(a.h + ci * NS + 4 * q);
-  const f32v4 hv = __builtin_nontemporal_load(hp);
-  float4 h = make_float4(hv.x, hv.y, hv.z, hv.w);
+  f32v4 h = __builtin_nontemporal_load(hp);
   // tap j multiplies window row j (tap K-1 the current row)
   float cv = cb;
 #pragma unroll
@@ -695,11 +726,8 @@ __global__ void __launch_bounds__(256) decode_ssm_step(DecodeSsmArgs a) {
   y = fmaf(Cq.w, h.w, y);
   y = quad_sum(y);
   if (!live) return;
-  __builtin_nontemporal_store(f32v4{h.x, h.y, h.z, h.w}, hp);
+  __builtin_nontemporal_store(h, hp);
   if (q == 0) {
-    // a producer's new token joins the cache once this step's attention (an
-    // earlier launch on the stream) has read len
-    if (a.len_bump && c == 0 && (a.is_ring || a.len_bump[b] < a.cap)) a.len_bump[b] += 1;
 #pragma unroll
     for (int j = 0; j < K - 1; ++j) conv[(size_t)j * a.D] = win[j + 1];
     reinterpret_cast<T *>(a.y)[idx] = from_f32<T>(y * silu_f(zv));
@@ -718,6 +746,7 @@ hipError_t launch_decode_ssm(const DecodeSsmArgs &a, hipStream_t s) {
   }
   return hipGetLastError();
 }
+
 template hipError_t launch_decode_ssm<float>(const DecodeSsmArgs &, hipStream_t);
 template hipError_t launch_decode_ssm<bf16>(const DecodeSsmArgs &, hipStream_t);
 

@@ -203,7 +203,10 @@ gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         strip[(8 * (r >> 2) + 4 * lh + (r & 3)) * SROW + j * 32 + lr] = acc[i][j][r];
-    __syncthreads();
+    // the strip is this wave's own: LDS keeps one wave's accesses in order,
+    // so only the compiler must not move the reads above the writes
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll 1
     for (int it = 0; it < 32 / RPI; ++it) {
       const int rr = it * RPI + lane / LPR;
@@ -216,7 +219,8 @@ gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int
         if (ok1) epi.template store<4>(row, ci1, vb);
       }
     }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
   }
 #endif
 }

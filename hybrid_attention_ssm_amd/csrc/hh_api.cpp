@@ -329,6 +329,11 @@ hh_status decode_t(const Shape &s, const hh_weights *w, const void *x, int B, co
   da.is_ring = kv->is_ring; da.window = window; da.is_global = is_global;
   da.split = L.split;
   da.nsplit = L.nsplit;
+  hh::DecodeSsmArgs sa{};
+  sa.xs = e.xs; sa.z = e.z; sa.dt = e.dt; sa.bc = e.bc;
+  sa.A = w->A; sa.conv_w = w->conv_w; sa.conv_b = w->conv_b;
+  sa.h = state->h; sa.conv = state->conv; sa.y = at(ws, L.y);
+  sa.B = B; sa.D = s.D; sa.N = s.N; sa.k = s.k;
   hipError_t err;
   bool o_ready = false;
   {
@@ -336,14 +341,6 @@ hh_status decode_t(const Shape &s, const hh_weights *w, const void *x, int B, co
     err = hh::launch_decode_attention<T>(da, st, /*defer_combine=*/true, &o_ready);
   }
   if (err != hipSuccess) return hip_fail(err, "decode attention");
-
-  hh::DecodeSsmArgs sa{};
-  sa.xs = e.xs; sa.z = e.z; sa.dt = e.dt; sa.bc = e.bc;
-  sa.A = w->A; sa.conv_w = w->conv_w; sa.conv_b = w->conv_b;
-  sa.h = state->h; sa.conv = state->conv; sa.y = at(ws, L.y);
-  sa.B = B; sa.D = s.D; sa.N = s.N; sa.k = s.k;
-  sa.len_bump = prod ? kv->len : nullptr;
-  sa.cap = kv->cap; sa.is_ring = kv->is_ring;
   {
     Stage sg(st, "decode_ssm");
     err = hh::launch_decode_ssm<T>(sa, st);
@@ -354,6 +351,9 @@ hh_status decode_t(const Shape &s, const hh_weights *w, const void *x, int B, co
   na.o = da.o; na.y = sa.y; na.beta_attn = w->beta_attn; na.beta_ssm = w->beta_ssm;
   na.f = at(ws, L.f);
   na.rows = B; na.Wa = s.Wa; na.D = s.D; na.eps = s.eps;
+  if (prod) {   // the new token joins the producer's cache after this step's attention
+    na.len_bump = kv->len; na.bump_n = B; na.bump_cap = kv->cap; na.bump_ring = kv->is_ring;
+  }
   if (!o_ready) {   // merge the attention's split partials here
     na.part = da.part; na.H = s.H; na.hd = s.hd; na.nsplit = da.nsplit;
   }

@@ -289,6 +289,11 @@ struct NormArgs {
   // (the cache now holds the prompt's positions); null: nothing
   int32_t *set_len;
   int set_len_n, set_len_value;
+  // decode step of a producer: its new token joins the cache, len[b] += 1 for
+  // b < bump_n (a ring always, a linear cache while below bump_cap); the norm
+  // runs after every reader of len in the step (attention); null: nothing
+  int32_t *len_bump;
+  int bump_n, bump_cap, bump_ring;
 };
 template <class T> hipError_t launch_norm_fuse(const NormArgs &a, hipStream_t s);
 // out[r] = g * x[r] / sqrt(mean(x[r]^2) + eps) for each of `rows` rows of d
@@ -326,8 +331,6 @@ struct DecodeSsmArgs {
   float *h;                // [B, D, N] in/out
   float *conv;             // [B, k-1, D] fp32 in/out
   void *y;                 // [B, D]
-  int32_t *len_bump;       // producer: len[b] += 1 (ring, or below cap); else null
-  int cap, is_ring;
   int B, D, N, k;
 };
 template <class T> hipError_t launch_decode_ssm(const DecodeSsmArgs &a, hipStream_t s);

@@ -16,10 +16,15 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// block 0 records the prompt length of a producer's cache (see NormArgs)
+// block 0 records the length of a producer's cache (see NormArgs): the
+// prompt's length after a prefill, one more token after a decode step
 __device__ __forceinline__ void record_len(const NormArgs &a) {
-  if (a.set_len && blockIdx.x == 0)
+  if (blockIdx.x != 0) return;
+  if (a.set_len)
     for (int i = threadIdx.x; i < a.set_len_n; i += blockDim.x) a.set_len[i] = a.set_len_value;
+  if (a.len_bump)
+    for (int i = threadIdx.x; i < a.bump_n; i += blockDim.x)
+      if (a.bump_ring || a.len_bump[i] < a.bump_cap) a.len_bump[i] += 1;
 }
 
 template <class T> struct Vec;
