@@ -29,6 +29,7 @@ class LayerDims:
     n_meta: int
     dtype: str  # "f32" or "bf16"
     eps: float = 1e-6
+    rope_base: float = 0.0  # rotary embedding base of Q and K; 0: none
 
     @property
     def attn_width(self) -> int:
@@ -46,7 +47,8 @@ class LayerDims:
         return dict(d_model=self.d_model, n_heads=self.n_heads,
                     n_kv_heads=self.n_kv_heads, head_dim=self.head_dim,
                     d_inner=self.d_inner, d_state=self.d_state,
-                    d_conv=self.d_conv, n_meta=self.n_meta, eps=self.eps)
+                    d_conv=self.d_conv, n_meta=self.n_meta, eps=self.eps,
+                    rope_base=self.rope_base)
 
 
 @dataclass(frozen=True)

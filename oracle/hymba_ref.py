@@ -38,6 +38,14 @@ Readings where the pages are silent or ambiguous (each is a stated choice):
   * query head h reads KV head floor(h / (H/G))
   * a KV-sharing consumer layer has no K/V projection rows and attends over
     its producer's K/V                   [authors' reply, cache optimisation]
+  * rotary position embedding (optional; the pages train with RoPE and change
+    its base for the 8k stage, giving neither the base nor the convention):
+    with dims["rope_base"] = b > 0, Q and K are rotated after the projection
+    and before attention and caching, in the rotate-half pairing: dims i and
+    i + hd/2 of a head form pair i, turned by the angle pos * b^(-2i/hd).
+    pos is the row of X~ = [R; X], so meta row j sits at position j and real
+    position p at m + p; a decode token at real position p is at m + p.
+    b = 0 (the default) leaves Q and K as projected.   [paper §3 training]
 
 The block around the layer (the pages name its MLP width, 5504 at 1.5B in the
 architecture table, and draw it in their architecture figure, but do not
@@ -85,6 +93,31 @@ def _dims(dims):
     g = dict(dims)
     return (g["d_model"], g["n_heads"], g["n_kv_heads"], g["head_dim"],
             g["d_inner"], g["d_state"], g["d_conv"], g["n_meta"], g["eps"])
+
+
+def _rope_base(dims):
+    return float(dict(dims).get("rope_base", 0.0) or 0.0)
+
+
+# ---------------------------------------------------------------------------
+# rotary position embedding (header reading: rotate-half pairs, positions are
+# the rows of X~)
+# ---------------------------------------------------------------------------
+def rope(v, pos, base):
+    """Rotate the last axis of v [..., hd] for positions pos (shape v.shape[:-1]
+    or broadcastable to it).  Pair i = (v[..., i], v[..., i + hd/2]) turns by
+    pos * base^(-2i/hd): (a, b) -> (a cos t - b sin t, b cos t + a sin t).
+    base 0: v unchanged."""
+    v = _f64(v)
+    if not base:
+        return v.copy()
+    hd = v.shape[-1]
+    half = hd // 2
+    inv_freq = base ** (-2.0 * np.arange(half, dtype=F64) / hd)
+    t = np.asarray(pos, dtype=F64)[..., None] * inv_freq
+    a, b = v[..., :half], v[..., half:]
+    c, s = np.cos(t), np.sin(t)
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
 
 
 # ---------------------------------------------------------------------------
@@ -231,6 +264,7 @@ def prefill(dims, weights, R, x, window, is_global, shared_kv=None, cache=None,
     Bsz, n, _ = x.shape
     rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
     scale = 1.0 / np.sqrt(hd)
+    rope_base = _rope_base(dims)
     out = np.empty((Bsz, len(rows), d))
     K_all = np.empty((Bsz, m + n, G, hd))
     V_all = np.empty((Bsz, m + n, G, hd))
@@ -241,9 +275,10 @@ def prefill(dims, weights, R, x, window, is_global, shared_kv=None, cache=None,
     for b in range(Bsz):
         Xt = np.concatenate([R, x[b]])                       # X~ = [R, X]
         parts = split_projection(Xt @ w["w_in"].T, dims, w["kv_producer"])
-        Q = parts["q"].reshape(m + n, H, hd)
+        pos = np.arange(m + n)[:, None]                      # row of X~
+        Q = rope(parts["q"].reshape(m + n, H, hd), pos, rope_base)
         if w["kv_producer"]:
-            K = parts["k"].reshape(m + n, G, hd)
+            K = rope(parts["k"].reshape(m + n, G, hd), pos, rope_base)
             V = parts["v"].reshape(m + n, G, hd)
         else:
             K, V = _f64(shared_kv[0][b]), _f64(shared_kv[1][b])
@@ -296,7 +331,8 @@ def meta_prefix(dims, weights, R):
     parts = split_projection(R @ w["w_in"].T, dims, w["kv_producer"])
     res = {}
     if w["kv_producer"]:
-        res["k"] = parts["k"].reshape(m, G, hd).transpose(1, 0, 2).copy()
+        k_rot = rope(parts["k"].reshape(m, G, hd), np.arange(m)[:, None], _rope_base(dims))
+        res["k"] = k_rot.transpose(1, 0, 2).copy()
         res["v"] = parts["v"].reshape(m, G, hd).transpose(1, 0, 2).copy()
     delta = softplus(parts["dt"] + w["dt_bias"])
     u = silu(causal_conv(parts["xs"], w["conv_w"], w["conv_b"], np.zeros((k - 1, D))))
@@ -340,20 +376,20 @@ def decode_step(dims, weights, x_t, meta_k, meta_v, window, is_global, cache, h,
     out = np.empty((len(seqs), d))
     h_new = np.empty((len(seqs), D, N))
     conv_new = np.empty((len(seqs), k - 1, D))
+    rope_base = _rope_base(dims)
     for r, b in enumerate(seqs):
         parts = split_projection(x_t[b] @ w["w_in"].T, dims, w["kv_producer"])
+        p = int(length[b]) if w["kv_producer"] else int(length[b]) - 1
         if w["kv_producer"]:
-            p = int(length[b])
             slot = p % cap if ring else p
-            ck[b, :, slot] = parts["k"].reshape(G, hd)
+            ck[b, :, slot] = rope(parts["k"].reshape(G, hd), m + p, rope_base)
             cv[b, :, slot] = parts["v"].reshape(G, hd)
-        else:
-            p = int(length[b]) - 1
         lo = 0 if is_global else max(0, p - window + 1)
         slots = [(q % cap if ring else q) for q in range(lo, p + 1)]
         K = np.concatenate([mk, ck[b][:, slots].transpose(1, 0, 2)])   # [m+L, G, hd]
         V = np.concatenate([mv, cv[b][:, slots].transpose(1, 0, 2)])
-        o, _ = attend(parts["q"].reshape(H, hd), K, V, np.arange(K.shape[0]), scale)
+        q = rope(parts["q"].reshape(H, hd), m + p, rope_base)
+        o, _ = attend(q, K, V, np.arange(K.shape[0]), scale)
         win = np.concatenate([_f64(conv[b]), parts["xs"][None, :]])   # [k, D]
         c = _f64(w["conv_b"]) + np.sum(w["conv_w"].T * win, axis=0)
         u = silu(c)

@@ -136,3 +136,48 @@ def test_pins_catch_mutant(name, monkeypatch):
     attr, fn = MUTANTS[name]
     monkeypatch.setattr(ref, attr, fn)
     assert _max_err() > 1e-4, f"mutant '{name}' not caught"
+
+
+# rotary embedding: caught by the library composition (complex multiplication)
+from dataclasses import replace as _replace
+
+_orig_rope = ref.rope
+
+
+def _rope_err():
+    from tests.test_oracle_pins import GQA_ROPE
+    x, R, w = _layer(GQA_ROPE, 26, seed=43)
+    got = ref.prefill(GQA_ROPE.as_dict(), w, R, x, 7, False)
+    want = layer_by_library(GQA_ROPE, w, R, x[0], 7, False)
+    return float(np.abs(got["out"][0] - want["out"]).max())
+
+
+def _rope_adjacent_pairs(v, pos, base):
+    v = np.asarray(v, dtype=np.float64)
+    hd = v.shape[-1]
+    perm = np.concatenate([np.arange(0, hd, 2), np.arange(1, hd, 2)])   # (2i, 2i+1) pairs
+    inv = np.argsort(perm)
+    return _orig_rope(v[..., perm], pos, base)[..., inv]
+
+
+def _rope_half_frequency_exponent(v, pos, base):
+    return _orig_rope(v, pos, base ** 0.5)
+
+
+ROPE_MUTANTS = {
+    "rope turns the other way": lambda v, pos, base: _orig_rope(v, -np.asarray(pos), base),
+    "rope pairs adjacent dims": _rope_adjacent_pairs,
+    "rope frequency exponent halved": _rope_half_frequency_exponent,
+    "rope positions without the meta rows": lambda v, pos, base: _orig_rope(
+        v, np.maximum(np.asarray(pos) - 3, 0), base),
+}
+
+
+def test_unmutated_rope_agrees():
+    assert _rope_err() < 1e-9
+
+
+@pytest.mark.parametrize("name", sorted(ROPE_MUTANTS))
+def test_rope_pin_catches_mutant(name, monkeypatch):
+    monkeypatch.setattr(ref, "rope", ROPE_MUTANTS[name])
+    assert _rope_err() > 1e-4, f"mutant '{name}' not caught"

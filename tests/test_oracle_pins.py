@@ -11,6 +11,7 @@ import math
 import os
 
 import numpy as np
+from dataclasses import replace
 import pytest
 import torch
 import torch.nn.functional as TF
@@ -47,6 +48,18 @@ GQA = LayerDims(d_model=48, n_heads=4, n_kv_heads=2, head_dim=8, d_inner=24,
 # ---------------------------------------------------------------------------
 # the layer composed from library routines; SSM via Eq. (2)'s alpha matrix
 # ---------------------------------------------------------------------------
+def rope_by_complex(v, pos, base):
+    """RoPE as complex multiplication: (v_i + j v_{i+hd/2}) * e^{j pos f_i} with
+    f_i = base^(-2i/hd), real and imaginary parts back in the two halves."""
+    v = torch.as_tensor(np.asarray(v, dtype=np.float64)) if not torch.is_tensor(v) else v
+    half = v.shape[-1] // 2
+    f = torch.tensor(float(base), dtype=torch.float64) ** (
+        -2.0 * torch.arange(half, dtype=torch.float64) / v.shape[-1])
+    ang = torch.as_tensor(pos, dtype=torch.float64)[..., None] * f
+    z = torch.complex(v[..., :half], v[..., half:]) * torch.polar(torch.ones_like(ang), ang)
+    return torch.cat([z.real, z.imag], dim=-1)
+
+
 def layer_by_library(dims: LayerDims, w, R, xb, window, is_global):
     t = lambda a: torch.as_tensor(np.asarray(a, dtype=np.float64))
     m, n = R.shape[0], xb.shape[0]
@@ -57,6 +70,9 @@ def layer_by_library(dims: LayerDims, w, R, xb, window, is_global):
     P = TF.linear(Xt, t(w["w_in"]))
     q, kk, v, xs, z, dt, Bm, Cm = torch.split(
         P, [H * hd, G * hd, G * hd, D, D, D, N, N], dim=-1)
+    if dims.rope_base:
+        q = rope_by_complex(q.view(T, H, hd), torch.arange(T)[:, None], dims.rope_base).reshape(T, H * hd)
+        kk = rope_by_complex(kk.view(T, G, hd), torch.arange(T)[:, None], dims.rope_base).reshape(T, G * hd)
     # A-shape mask: meta keys always, real keys in the window (or causal)
     i = torch.arange(T)[:, None]
     j = torch.arange(T)[None, :]
@@ -93,8 +109,12 @@ def layer_by_library(dims: LayerDims, w, R, xb, window, is_global):
                 xs=xs.numpy(), O=O[m:].numpy(), Y=Y[m:].numpy())
 
 
+GQA_ROPE = replace(GQA, rope_base=100.0)
+
+
 @pytest.mark.parametrize("dims,n,window,is_global", [
-    (TINY, 40, 16, False), (TINY, 24, 16, True), (GQA, 30, 7, False), (GQA, 17, 5, True)])
+    (TINY, 40, 16, False), (TINY, 24, 16, True), (GQA, 30, 7, False), (GQA, 17, 5, True),
+    (GQA_ROPE, 30, 7, False), (replace(TINY, rope_base=10000.0), 24, 16, True)])
 def test_layer_matches_library_composition(dims, n, window, is_global):
     x, R, w = _layer(dims, n, seed=11)
     got = ref.prefill(dims.as_dict(), w, R, x, window, is_global)
@@ -299,12 +319,13 @@ def test_consumer_reads_producer_kv():
     np.testing.assert_allclose(cons["out"], prod["out"], rtol=1e-13)
 
 
-@pytest.mark.parametrize("is_global,n0,steps,cap", [
-    (False, 5, 4, 6), (False, 9, 6, 6), (True, 5, 4, 16)])
-def test_prefill_then_decode_equals_longer_prefill(is_global, n0, steps, cap):
+@pytest.mark.parametrize("is_global,n0,steps,cap,dims", [
+    (False, 5, 4, 6, GQA), (False, 9, 6, 6, GQA), (True, 5, 4, 16, GQA),
+    (False, 9, 6, 6, GQA_ROPE), (True, 5, 4, 16, GQA_ROPE)])
+def test_prefill_then_decode_equals_longer_prefill(is_global, n0, steps, cap, dims):
     """prefill(n) + k decode steps == prefill(n + k): outputs, state, conv
-    tail and cache slots (including ring wrap-around when n + k > cap)."""
-    dims = GQA
+    tail and cache slots (including ring wrap-around when n + k > cap); with
+    RoPE this also pins the decode token's position to the prefill's."""
     window = cap
     x, R, w = _layer(dims, n0 + steps, seed=10, batch=2)
     B = x.shape[0]
@@ -450,3 +471,44 @@ def test_block_prefill_then_decode_equals_longer_prefill():
         cache = dict(k=r["cache_k"], v=r["cache_v"], len=r["len"], is_ring=True)
         h, conv = r["h"], r["conv"]
     np.testing.assert_allclose(h, full["h"], rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# rotary position embedding
+# ---------------------------------------------------------------------------
+def test_rope_equals_complex_multiplication():
+    rng = np.random.default_rng(40)
+    for hd, base in ((8, 100.0), (64, 10000.0), (32, 500000.0)):
+        v = rng.standard_normal((7, 3, hd))
+        pos = rng.integers(0, 9000, size=(7, 1))
+        want = rope_by_complex(v, pos, base).numpy()
+        # angles reach 9000 rad: fp64 sin/cos of them agree to ~1e-12
+        np.testing.assert_allclose(ref.rope(v, pos, base), want, rtol=1e-10, atol=1e-10)
+
+
+def test_rope_is_a_position_linear_rotation():
+    rng = np.random.default_rng(41)
+    hd, base = 16, 1000.0
+    v = rng.standard_normal((5, hd))
+    half = hd // 2
+    r = ref.rope(v, 37, base)
+    # each pair keeps its length; position 0 and base 0 change nothing
+    np.testing.assert_allclose(r[:, :half] ** 2 + r[:, half:] ** 2,
+                               v[:, :half] ** 2 + v[:, half:] ** 2, rtol=1e-12)
+    np.testing.assert_array_equal(ref.rope(v, 0, base), v)
+    np.testing.assert_array_equal(ref.rope(v, 37, 0.0), v)
+    # turning by p1 then p2 is turning by p1 + p2
+    np.testing.assert_allclose(ref.rope(ref.rope(v, 11, base), 26, base), r, rtol=1e-12, atol=1e-12)
+    # scores depend on the distance only
+    q, k = rng.standard_normal(hd), rng.standard_normal(hd)
+    s1 = ref.rope(q, 50, base) @ ref.rope(k, 20, base)
+    s2 = ref.rope(q, 1030, base) @ ref.rope(k, 1000, base)
+    np.testing.assert_allclose(s1, s2, rtol=1e-10)
+
+
+def test_meta_prefix_keys_carry_meta_positions():
+    x, R, w = _layer(GQA_ROPE, 6, seed=42)
+    mp = ref.meta_prefix(GQA_ROPE.as_dict(), w, R)
+    pre = ref.prefill(GQA_ROPE.as_dict(), w, R, x, 4, False)
+    m = GQA_ROPE.n_meta
+    np.testing.assert_allclose(mp["k"], pre["K_all"][0, :m].transpose(1, 0, 2), rtol=1e-12, atol=1e-12)
