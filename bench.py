@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 
 MFMA_BF16_PEAK = 2.5166e15   # dense bf16 FLOP/s, MI355X
 HBM_PEAK = 8.0e12            # bytes/s, MI355X HBM3E
+ROPE_BASE = 10000.0          # rotary base of the RoPE prefill line (the value does not change the work)
 
 
 def log(msg):
@@ -102,13 +103,17 @@ def decode_bytes(dims, B, layers, p, window, ring_cap, global_cap):
 
 
 # ---------------------------------------------------------------------------
-def bench_prefill(args, hb, torch):
+def bench_prefill(args, hb, torch, rope_base=0.0):
+    """The 8k SWA prefill; rope_base > 0 times the same layer with Q and K
+    turned by the rotary embedding (same inputs)."""
+    from dataclasses import replace
     from hybrid_attention_ssm_amd.configs import CFG1_SWA_8K
     from hybrid_attention_ssm_amd.synth import prefill_inputs
     w = CFG1_SWA_8K
-    dims = w.dims
+    dims = replace(w.dims, rope_base=rope_base) if rope_base else w.dims
     B, n, W = w.batch, w.seqlen, w.window
-    log(f"[bench] prefill setup {w.name}")
+    tag = f" (RoPE base {rope_base:g})" if rope_base else ""
+    log(f"[bench] prefill setup {w.name}{tag}")
     inp = prefill_inputs(w)
     sd = hb.storage_dtype(dims)
     dev = "cuda"
@@ -150,7 +155,7 @@ def bench_prefill(args, hb, torch):
     hb.hh_timing_enable(False)
     fl = prefill_flops(dims, B, n, W, False)
     st_ms = {name: tot / cnt for name, (cnt, tot) in stages.items()}
-    log(f"[bench] prefill {ms_step:.3f} ms/step; stages " +
+    log(f"[bench] prefill{tag} {ms_step:.3f} ms/step; stages " +
         ", ".join(f"{k}={v * 1e3:.1f}us" for k, v in st_ms.items()))
     return dict(workload=w.name, dims=dims, B=B, n=n, W=W, ms_step=ms_step, stages=st_ms,
                 flops=fl, inp=inp)
@@ -387,6 +392,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the 32-block decode stack line")
+    ap.add_argument("--no-rope", action="store_true",
+                    help="skip the prefill line with the rotary embedding of Q and K")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192,
                     help="prefill tokens the CPU oracle runs (default: the whole 8k workload)")
     ap.add_argument("--cpu-sample-seqs", type=int, default=64,
@@ -419,6 +426,9 @@ def main():
         return
 
     pre = bench_prefill(args, hb, torch) if args.only in ("prefill", "both") else None
+    pre_rope = None
+    if pre is not None and not args.no_rope:
+        pre_rope = bench_prefill(args, hb, torch, rope_base=ROPE_BASE)
     dec = bench_decode(args, hb, torch) if args.only in ("decode", "both") else None
     stack = None
     if args.only in ("decode", "both") and not args.no_stack:
@@ -455,6 +465,14 @@ def main():
             rec["scan"] = {"us": t_scan * 1e3, "algorithmic_bytes": sb,
                            "GB_per_s": sb / (t_scan * 1e-3) / 1e9, "frac_hbm": sb / (t_scan * 1e-3) / HBM_PEAK,
                            "recurrence_exps": ex, "exps_per_s": ex / (t_scan * 1e-3)}
+        if pre_rope is not None:
+            # the same workload with RoPE on Q and K (turned in the in-projection's epilogue)
+            t_in_r = pre_rope["stages"].get("inproj")
+            rec["rope"] = {"rope_base": ROPE_BASE, "ms_per_step": pre_rope["ms_step"],
+                           "value": pre["B"] * pre["n"] / (pre_rope["ms_step"] * 1e-3), "unit": "tok/s",
+                           "mfma_frac_layer": fl["total"] / (pre_rope["ms_step"] * 1e-3) / MFMA_BF16_PEAK,
+                           "stage_us": {k: v * 1e3 for k, v in pre_rope["stages"].items()},
+                           "inproj_extra_us": (t_in_r - t_in) * 1e3 if (t_in_r and t_in) else None}
         if t_in:
             ach = fl["inproj"] / (t_in * 1e-3)
             tr = measured_traffic("gemm_bf16_lds", pre["workload"])

@@ -35,6 +35,22 @@ __device__ __forceinline__ bool tile_of(int tiles_m, int tiles_n, int &tm, int &
   return true;
 }
 
+// An epilogue may remap which row of B (the weights) feeds output column n
+// (src_row; the in-projection does for RoPE).  Without one, row n.
+template <class E, class = void> struct HasRowMap : std::false_type {};
+template <class E>
+struct HasRowMap<E, std::void_t<decltype(&E::src_row)>> : std::true_type {};
+template <class Epi>
+__device__ __forceinline__ int b_row(const Epi &epi, int n) {
+  if constexpr (HasRowMap<Epi>::value) return epi.src_row(n);
+  else return n;
+}
+// An epilogue may also take a lane's two column groups of a row together
+// (store_pair; the in-projection's rotary embedding pairs them).
+template <class E, class = void> struct HasPairStore : std::false_type {};
+template <class E>
+struct HasPairStore<E, std::void_t<decltype(&E::template store_pair<4>)>> : std::true_type {};
+
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel, operands streamed straight into LDS
 //
@@ -99,7 +115,7 @@ gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int
   for (int j = 0; j < Cfg::B_INS; ++j) {
     const int u = (wave * Cfg::B_INS + j) * 64 + lane;
     const int row = u / Cfg::KCH, kc = Cfg::swz(row, u % Cfg::KCH) - row * Cfg::KCH;
-    voffB[j] = (row * K + kc * 8) * 2;
+    voffB[j] = ((b_row(epi, n0 + row) - n0) * K + kc * 8) * 2;
   }
   typedef __attribute__((address_space(3))) void lds_void;
   auto issue = [&](int kt, int st) {
@@ -215,6 +231,12 @@ gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int
       const float va[4] = {a.x, a.y, a.z, a.w}, vb[4] = {b.x, b.y, b.z, b.w};
       const int row = m0 + wm * Cfg::WM + i * 32 + rr;
       if (row < M) {
+        if constexpr (HasPairStore<Epi>::value) {
+          if (ok0 && ok1) {
+            epi.template store_pair<4>(row, ci0, va, ci1, vb);
+            continue;
+          }
+        }
         if (ok0) epi.template store<4>(row, ci0, va);
         if (ok1) epi.template store<4>(row, ci1, vb);
       }
@@ -247,7 +269,7 @@ gemm_f32_tiled(const float *__restrict__ A, const float *__restrict__ B, int M, 
       const int e = threadIdx.x + i * 256;
       const int r = e >> 4, kk = e & 15;
       sA[kk][r] = (m0 + r < M && k0 + kk < K) ? A[(size_t)(m0 + r) * K + k0 + kk] : 0.0f;
-      sB[kk][r] = (n0 + r < N && k0 + kk < K) ? B[(size_t)(n0 + r) * K + k0 + kk] : 0.0f;
+      sB[kk][r] = (n0 + r < N && k0 + kk < K) ? B[(size_t)b_row(epi, n0 + r) * K + k0 + kk] : 0.0f;
     }
     __syncthreads();
 #pragma unroll
@@ -281,15 +303,27 @@ gemm_f32_tiled(const float *__restrict__ A, const float *__restrict__ B, int M, 
 // Epilogue interface: col_info<W>(col) resolves, once per lane, a group of W
 // consecutive output columns (col % W == 0); store<W>(row, info, v) writes
 // the group's W values of one row.
-template <class T>
+// ROPE (a RopeMode): how Q and K meet the rotary embedding in the epilogue;
+// under ROPE_PAIRED_COLS the weight rows of their heads are read in pair
+// order (src_row), under ROPE_SPLIT_GROUPS the kernel's lane owns both
+// halves of its pairs (store_pair)
+template <class T, int ROPE>
 struct InProjEpi {
   InProjOut e;
   template <int W> using Col = ColInfo<W>;
+  __device__ __forceinline__ int src_row(int n) const {
+    return ROPE == ROPE_PAIRED_COLS ? inproj_src_row(e, n) : n;
+  }
   template <int W>
-  __device__ __forceinline__ Col<W> col_info(int col) const { return inproj_col<W>(e, col); }
+  __device__ __forceinline__ Col<W> col_info(int col) const { return inproj_col<W, ROPE>(e, col); }
   template <int W>
   __device__ __forceinline__ void store(int row, const Col<W> &ci, const float v[W]) const {
-    inproj_storeW<T, W>(e, row, ci, v);
+    inproj_storeW<T, W, ROPE>(e, row, ci, v);
+  }
+  template <int W>
+  __device__ __forceinline__ void store_pair(int row, const Col<W> &ci0, const float va[W],
+                                             const Col<W> &ci1, const float vb[W]) const {
+    inproj_store_pair<T, W, ROPE>(e, row, ci0, va, ci1, vb);
   }
 };
 
@@ -463,12 +497,21 @@ static hipError_t run_f32(const float *A, int M, int K, const float *B, int N, c
 template <>
 hipError_t launch_inproj<bf16>(const bf16 *x, int M, int K, const bf16 *w, int Ncols,
                                const InProjOut &e, float *part, hipStream_t s) {
-  return run_bf16_auto(x, M, K, w, Ncols, InProjEpi<bf16>{e}, part, s);
+  if (e.rope_base == 0.0f) return run_bf16_auto(x, M, K, w, Ncols, InProjEpi<bf16, ROPE_NONE>{e}, part, s);
+  // RoPE: the 256x256 tile's lanes own both halves of their pairs when a
+  // wave's 64 columns are one head; the few-row tile reads the weight rows in
+  // pair order instead, and is not split over K (the partial GEMMs would not
+  // see that order)
+  if (M >= 1024 && e.hd == CfgLds::WN)
+    return run_lds<CfgLds>(x, M, K, w, Ncols, InProjEpi<bf16, ROPE_SPLIT_GROUPS>{e}, s);
+  if (M >= 1024) return run_lds<CfgLds>(x, M, K, w, Ncols, InProjEpi<bf16, ROPE_PAIRED_COLS>{e}, s);
+  return run_skinny(x, M, K, w, Ncols, InProjEpi<bf16, ROPE_PAIRED_COLS>{e}, nullptr, s);
 }
 template <>
 hipError_t launch_inproj<float>(const float *x, int M, int K, const float *w, int Ncols,
                                 const InProjOut &e, float *, hipStream_t s) {
-  return run_f32(x, M, K, w, Ncols, InProjEpi<float>{e}, s);
+  if (e.rope_base != 0.0f) return run_f32(x, M, K, w, Ncols, InProjEpi<float, ROPE_PAIRED_COLS>{e}, s);
+  return run_f32(x, M, K, w, Ncols, InProjEpi<float, ROPE_NONE>{e}, s);
 }
 template <>
 hipError_t launch_outproj<bf16>(const bf16 *f, int M, int K, const bf16 *w, int Ncols, bf16 *out,

@@ -3,6 +3,7 @@
 // first launch, so a rejected call touches no buffer.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -74,7 +75,7 @@ size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 struct Shape {
   int d, H, G, hd, D, N, k, m, Wa, KV, n_in, dtype;
   size_t es;
-  float eps;
+  float eps, rope_base;
 };
 
 hh_status check_dims(const hh_dims *dm, int kv_producer, Shape &s) {
@@ -101,6 +102,8 @@ hh_status check_dims(const hh_dims *dm, int kv_producer, Shape &s) {
                                     "to be multiples of 64");
   if (!(dm->rms_eps >= 0.0f) || dm->rms_eps > 1.0f)
     return fail(HH_ERR_INVALID_ARG, "rms_eps must be in [0, 1]");
+  if (!(dm->rope_base == 0.0f || (dm->rope_base > 1.0f && dm->rope_base < 1e30f)))
+    return fail(HH_ERR_INVALID_ARG, "rope_base must be 0 (no rotary embedding) or a finite base > 1");
   s.d = dm->d_model; s.H = dm->n_heads; s.G = dm->n_kv_heads; s.hd = dm->head_dim;
   s.D = dm->d_inner; s.N = dm->d_state; s.k = dm->d_conv; s.m = dm->n_meta;
   s.Wa = s.H * s.hd;
@@ -109,7 +112,18 @@ hh_status check_dims(const hh_dims *dm, int kv_producer, Shape &s) {
   s.dtype = dm->dtype;
   s.es = dm->dtype == HH_BF16 ? 2 : 4;
   s.eps = dm->rms_eps;
+  s.rope_base = dm->rope_base;
   return HH_OK;
+}
+
+// rotary embedding of the in-projection: pair i turns by pos * f0 * ratio^i
+// revolutions (f0 = 1/(2 pi), ratio = base^(-2/hd), in double)
+void set_rope(hh::InProjOut &e, const Shape &s, int len_bias) {
+  e.rope_base = s.rope_base;
+  e.rope_m = s.m;
+  e.len_bias = len_bias;
+  e.rope_f0 = 0.15915494309189533577;
+  e.rope_ratio = s.rope_base != 0.0f ? std::pow((double)s.rope_base, -2.0 / s.hd) : 1.0;
 }
 
 hh_status check_weights(const hh_weights *w, const Shape &s) {
@@ -223,6 +237,7 @@ hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, i
   e.dt = reinterpret_cast<float *>(at(ws, L.off[HH_WS_DELTA]));
   e.bc = reinterpret_cast<float *>(at(ws, L.off[HH_WS_BC]));
   e.dt_bias = w->dt_bias;
+  set_rope(e, s, 0);
   hh_status r = run_inproj<T>(s, w, x, rows, e, part_ptr(ws, L.off[HH_WS_GEMM]), st);
   if (r != HH_OK) return r;
 
@@ -289,6 +304,7 @@ hh_status meta_prefix_t(const Shape &s, const hh_weights *w, const void *R, void
   e.dt = reinterpret_cast<float *>(at(ws, L.off[HH_WS_DELTA]));
   e.bc = reinterpret_cast<float *>(at(ws, L.off[HH_WS_BC]));
   e.dt_bias = w->dt_bias;
+  set_rope(e, s, 0);
   hh_status r = run_inproj<T>(s, w, R, s.m, e, part_ptr(ws, L.off[HH_WS_GEMM]), st);
   if (r != HH_OK) return r;
   hh::ScanArgs sa{};
@@ -317,6 +333,7 @@ hh_status decode_t(const Shape &s, const hh_weights *w, const void *x, int B, co
   e.dt = reinterpret_cast<float *>(at(ws, L.dt));
   e.bc = reinterpret_cast<float *>(at(ws, L.bc));
   e.dt_bias = w->dt_bias;
+  set_rope(e, s, prod ? 0 : -1);
   hh_status r = run_inproj<T>(s, w, x, B, e, part_ptr(ws, L.gemm), st);
   if (r != HH_OK) return r;
 

@@ -4,6 +4,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -77,7 +78,37 @@ struct InProjOut {
   float *dt;                  // [rows, D] softplus(dt + bias)
   float *bc;                  // [rows, 2N] B then C
   const float *dt_bias;       // [D]
+  // Rotary embedding of Q and K (rope_base 0: none).  Position of a row:
+  // meta mode, the row; prefill, rope_m + row % n_rows_per_seq; decode,
+  // rope_m + len[row] + len_bias (-1 for a consumer, whose producer has
+  // already counted the token).  Pair i turns by pos * rope_f0 * rope_ratio^i
+  // revolutions (rope_f0 = 1/(2 pi), rope_ratio = base^(-2/hd), from the host
+  // in double).
+  float rope_base;
+  int rope_m, len_bias;
+  double rope_f0, rope_ratio;
 };
+
+// How the in-projection's epilogue meets the rotation pairs (dims i and
+// i + hd/2 of a Q or K head):
+//   ROPE_PAIRED_COLS  the GEMM reads each head's weight rows in pair order
+//                     (inproj_src_row), so a group of W columns holds W/2
+//                     whole pairs, stored back at their natural columns;
+//   ROPE_SPLIT_GROUPS the GEMM hands over two groups at once, dims d..d+W-1
+//                     and d+hd/2.. of one head (store_pair): a lane of the
+//                     256x256-tile kernel owns exactly these, as its wave's 64
+//                     columns are one head.
+enum RopeMode : int { ROPE_NONE = 0, ROPE_PAIRED_COLS = 1, ROPE_SPLIT_GROUPS = 2 };
+
+// Weight row feeding output column n under ROPE_PAIRED_COLS: the columns of
+// each Q and K head come out in pair order, dims (0, hd/2, 1, hd/2+1, ...).
+// Heads never straddle a GEMM tile (Q starts at 0, K at H*hd, tiles are
+// multiples of 64 wide).
+__device__ __forceinline__ int inproj_src_row(const InProjOut &e, int n) {
+  if (n >= e.Wa + e.KV) return n;
+  const int j = n % e.hd;
+  return n - j + ((j & 1) ? e.hd / 2 : 0) + (j >> 1);
+}
 
 // Store 8 consecutive columns col..col+7 of one row (col % 8 == 0).  Every
 // column-block boundary of the map is a multiple of 8, so the 8 values always
@@ -150,19 +181,39 @@ struct ColInfo {
   int c;         // column offset inside the block
   int g, d;      // K/V: head and position inside the head
   float bias[W];
+  // RoPE (Q, K): pair j of the group turns by pos * f_j revolutions, f_j =
+  // base^(-2i/hd) / (2 pi) held as hi + lo floats (i the pair's low dim);
+  // W/2 pairs under ROPE_PAIRED_COLS, W under ROPE_SPLIT_GROUPS
+  float rf_hi[W], rf_lo[W];
 };
 
-template <int W>
+template <int W, int ROPE>
 __device__ __forceinline__ ColInfo<W> inproj_col(const InProjOut &e, int col) {
   ColInfo<W> ci{};
   const int Wa = e.Wa, KV = e.KV, D = e.D;
-  if (col < Wa) { ci.seg = 0; ci.c = col; return ci; }
+  auto rope_freqs = [&](int c) {   // c: column inside the Q or K block
+    if constexpr (ROPE != ROPE_NONE) {
+      constexpr int NP = ROPE == ROPE_PAIRED_COLS ? W / 2 : W;
+      const int i0 = ROPE == ROPE_PAIRED_COLS ? (c % e.hd) >> 1 : c % e.hd;
+      double f = e.rope_f0, r = e.rope_ratio;   // f0 * ratio^i0 by squaring
+      for (int k = i0; k; k >>= 1, r *= r)
+        if (k & 1) f *= r;
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        ci.rf_hi[j] = (float)f;
+        ci.rf_lo[j] = (float)(f - (double)ci.rf_hi[j]);
+        f *= e.rope_ratio;
+      }
+    }
+  };
+  if (col < Wa) { ci.seg = 0; ci.c = col; rope_freqs(col); return ci; }
   col -= Wa;
   if (col < 2 * KV) {
     ci.seg = col < KV ? 1 : 2;
     ci.c = col < KV ? col : col - KV;
     ci.g = ci.c / e.hd;
     ci.d = ci.c - ci.g * e.hd;
+    if (ci.seg == 1) rope_freqs(ci.c);
     return ci;
   }
   col -= 2 * KV;
@@ -183,36 +234,114 @@ __device__ __forceinline__ ColInfo<W> inproj_col(const InProjOut &e, int col) {
   return ci;
 }
 
-template <class T, int W>
+// sin and cos of 2 pi r for |r| <= 1/2 (and a little beyond): quarter turns
+// are split off (x = 4r = q + f, |f| <= 1/2), then the Taylor series of sin
+// and cos at t = f pi/2, |t| <= pi/4, through t^9 and t^10 (truncation below
+// 2e-9), and the quadrant q turns the pair (selects, no branches).
+__device__ __forceinline__ void sincos_rev(float r, float &sn, float &cs) {
+  const float x = 4.0f * r;
+  const float q = rintf(x);
+  const float t = (x - q) * 1.5707963267948966f;
+  const float t2 = t * t;
+  const float sp = fmaf(t * t2, fmaf(t2, fmaf(t2, fmaf(t2, 2.7557319223985893e-6f, -1.9841269841269841e-4f),
+                                              8.3333333333333333e-3f), -1.6666666666666667e-1f), t);
+  const float cp = fmaf(t2, fmaf(t2, fmaf(t2, fmaf(t2, fmaf(t2, -2.7557319223985888e-7f, 2.4801587301587302e-5f),
+                                                   -1.3888888888888889e-3f), 4.1666666666666667e-2f), -0.5f), 1.0f);
+  const int qi = (int)q;
+  const float s1 = (qi & 1) ? cp : sp, c1 = (qi & 1) ? -sp : cp;
+  sn = (qi & 2) ? -s1 : s1;
+  cs = (qi & 2) ? -c1 : c1;
+}
+
+// Turn the pair (x, y) = (dim i, dim i + hd/2) by pos * f revolutions, f =
+// hi + lo.  The angle is reduced in revolutions with the exact product
+// pos * hi (plus pos * lo), so only |r| <= 1/2 turn reaches sincos_rev.
+__device__ __forceinline__ void rope_pair(float hi, float lo, float p, float &x, float &y) {
+  const float a = p * hi;
+  const float b = fmaf(p, lo, fmaf(p, hi, -a));
+  float sn, cs;
+  sincos_rev((a - rintf(a)) + b, sn, cs);
+  const float nx = fmaf(x, cs, -y * sn), ny = fmaf(y, cs, x * sn);
+  x = nx;
+  y = ny;
+}
+
+// position of a row of the in-projection for the rotary embedding
+__device__ __forceinline__ int rope_position(const InProjOut &e, int row) {
+  if (e.mode == EPI_META) return row;
+  if (e.mode == EPI_DECODE) return e.rope_m + e.len[row] + e.len_bias;
+  return e.rope_m + row % e.n_rows_per_seq;
+}
+
+// One row's group of W consecutive columns of the fused projection (see
+// ColInfo) to its destination.  Under ROPE_PAIRED_COLS the Q and K groups
+// arrive in pair order and are turned here; under ROPE_SPLIT_GROUPS they
+// come through inproj_store_pair, already turned.
+template <class T, int W, int ROPE>
 __device__ __forceinline__ void inproj_storeW(const InProjOut &e, int row, const ColInfo<W> &ci,
                                               const float v[W]) {
   const int Wa = e.Wa, D = e.D;
+  // turn the group's W/2 pairs (in pair order) into low and high dims
+  auto turn = [&](float lo[W / 2], float hi[W / 2]) {
+    const float p = (float)rope_position(e, row);
+#pragma unroll
+    for (int j = 0; j < W / 2; ++j) {
+      lo[j] = v[2 * j];
+      hi[j] = v[2 * j + 1];
+      rope_pair(ci.rf_hi[j], ci.rf_lo[j], p, lo[j], hi[j]);
+    }
+  };
   switch (ci.seg) {
-    case 0: storeW_T<T, W>(reinterpret_cast<T *>(e.q) + (size_t)row * Wa + ci.c, v); return;
+    case 0: {
+      T *dst = reinterpret_cast<T *>(e.q) + (size_t)row * Wa;
+      if constexpr (ROPE == ROPE_PAIRED_COLS) {
+        float lo[W / 2], hi[W / 2];
+        turn(lo, hi);
+        const int base = ci.c - ci.c % e.hd, i0 = (ci.c % e.hd) >> 1;
+        storeW_T<T, W / 2>(dst + base + i0, lo);
+        storeW_T<T, W / 2>(dst + base + e.hd / 2 + i0, hi);
+        return;
+      }
+      storeW_T<T, W>(dst + ci.c, v);
+      return;
+    }
     case 1:
     case 2: {
       const bool isv = ci.seg == 2;
       const int G = e.KV / e.hd;
-      if (e.mode == EPI_DECODE) {
-        const int p = e.len[row];
-        if (p < 0 || (!e.is_ring && p >= e.cap)) return;
-        const int slot = e.is_ring ? p % e.cap : p;
-        T *dst = reinterpret_cast<T *>(isv ? e.cache_v : e.cache_k);
-        storeW_T<T, W>(dst + (((size_t)row * G + ci.g) * e.cap + slot) * e.hd + ci.d, v);
-        return;
-      }
-      const int n = e.n_rows_per_seq;
-      const int b = row / n, p = row - b * n;
-      T *full = reinterpret_cast<T *>(isv ? e.v_full : e.k_full);
-      storeW_T<T, W>(full + (((size_t)b * G + ci.g) * n + p) * e.hd + ci.d, v);
-      if (e.mode == EPI_PREFILL && e.cache_k) {
-        const bool keep = e.is_ring ? (p >= n - e.cap) : (p < e.cap);
-        if (keep) {
+      // dims d0.. of the head get the W values (n at most W), for every copy
+      auto put = [&](int d0, const float *vals, auto width) {
+        constexpr int WW = decltype(width)::value;
+        if (e.mode == EPI_DECODE) {
+          const int p = e.len[row];
+          if (p < 0 || (!e.is_ring && p >= e.cap)) return;
           const int slot = e.is_ring ? p % e.cap : p;
           T *dst = reinterpret_cast<T *>(isv ? e.cache_v : e.cache_k);
-          storeW_T<T, W>(dst + (((size_t)b * G + ci.g) * e.cap + slot) * e.hd + ci.d, v);
+          storeW_T<T, WW>(dst + (((size_t)row * G + ci.g) * e.cap + slot) * e.hd + d0, vals);
+          return;
         }
+        const int n = e.n_rows_per_seq;
+        const int b = row / n, p = row - b * n;
+        T *full = reinterpret_cast<T *>(isv ? e.v_full : e.k_full);
+        storeW_T<T, WW>(full + (((size_t)b * G + ci.g) * n + p) * e.hd + d0, vals);
+        if (e.mode == EPI_PREFILL && e.cache_k) {
+          const bool keep = e.is_ring ? (p >= n - e.cap) : (p < e.cap);
+          if (keep) {
+            const int slot = e.is_ring ? p % e.cap : p;
+            T *dst = reinterpret_cast<T *>(isv ? e.cache_v : e.cache_k);
+            storeW_T<T, WW>(dst + (((size_t)b * G + ci.g) * e.cap + slot) * e.hd + d0, vals);
+          }
+        }
+      };
+      if (ROPE == ROPE_PAIRED_COLS && !isv) {
+        float lo[W / 2], hi[W / 2];
+        turn(lo, hi);
+        const int i0 = ci.d >> 1;
+        put(i0, lo, std::integral_constant<int, W / 2>{});
+        put(e.hd / 2 + i0, hi, std::integral_constant<int, W / 2>{});
+        return;
       }
+      put(ci.d, v, std::integral_constant<int, W>{});
       return;
     }
     case 3: storeW_T<float, W>(e.xs + (size_t)row * D + ci.c, v); return;
@@ -226,6 +355,30 @@ __device__ __forceinline__ void inproj_storeW(const InProjOut &e, int row, const
     }
     default: storeW_T<float, W>(e.bc + (size_t)row * 2 * e.N + ci.c, v); return;
   }
+}
+
+// ROPE_SPLIT_GROUPS: a lane's two groups of one row, dims d..d+W-1 (ci0, va)
+// and d+hd/2.. (ci1, vb) of the same Q or K head, turned pairwise and stored;
+// other blocks of the map are stored as they are.
+template <class T, int W, int ROPE>
+__device__ __forceinline__ void inproj_store_pair(const InProjOut &e, int row, const ColInfo<W> &ci0,
+                                                  const float va[W], const ColInfo<W> &ci1,
+                                                  const float vb[W]) {
+  if (ROPE == ROPE_SPLIT_GROUPS && (ci0.seg == 0 || ci0.seg == 1)) {
+    const float p = (float)rope_position(e, row);
+    float x[W], y[W];
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+      x[j] = va[j];
+      y[j] = vb[j];
+      rope_pair(ci0.rf_hi[j], ci0.rf_lo[j], p, x[j], y[j]);
+    }
+    inproj_storeW<T, W, ROPE_NONE>(e, row, ci0, x);
+    inproj_storeW<T, W, ROPE_NONE>(e, row, ci1, y);
+    return;
+  }
+  inproj_storeW<T, W, ROPE>(e, row, ci0, va);
+  inproj_storeW<T, W, ROPE>(e, row, ci1, vb);
 }
 
 // ---- launchers (each returns hipGetLastError() of its launches) ------------

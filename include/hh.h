@@ -67,12 +67,24 @@ typedef enum {
 } hh_status;
 
 /* Layer shape.  n_heads = H query heads, n_kv_heads = G query groups,
- * d_inner = D SSM channels, d_state = N, d_conv = k taps, n_meta = m. */
+ * d_inner = D SSM channels, d_state = N, d_conv = k taps, n_meta = m.
+ *
+ * rope_base: rotary position embedding of Q and K (Hymba paper §3: the
+ * model is trained with RoPE and its base is changed for the 8k stage; the
+ * pages give neither the base nor the convention).  0 = none.  Otherwise
+ * dims i and i + head_dim/2 of every Q and K head form pair i and are turned
+ * by the angle pos * rope_base^(-2i/head_dim), (a, b) -> (a cos - b sin,
+ * b cos + a sin), right after the input projection, so the meta K/V, the
+ * prefill K/V and the cache all hold rotated keys.  pos counts the rows of
+ * [R; X]: meta token j is at position j, real position p at n_meta + p (a
+ * decode token at real position len[b], or len[b] - 1 for a KV-sharing
+ * consumer, likewise).  Must be 0 or a finite value > 1. */
 typedef struct {
   int32_t d_model, n_heads, n_kv_heads, head_dim;
   int32_t d_inner, d_state, d_conv, n_meta;
   int32_t dtype;   /* hh_dtype */
   float rms_eps;   /* epsilon inside the RMS norm of both branches */
+  float rope_base; /* rotary embedding base of Q and K; 0 = none */
 } hh_dims;
 
 /* One layer's parameters (all device pointers, read only).

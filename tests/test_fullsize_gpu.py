@@ -10,6 +10,8 @@ Decode (batch 128, 3 layers): the oracle steps a sample of sequences through
 the same three layers; compared are their outputs, states and the appended
 cache slots, and every other cache slot must be unchanged bit for bit.
 """
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -32,7 +34,14 @@ def _rows(n, W, seed, extra=16):
     return np.array(sorted(r))
 
 
-@pytest.mark.parametrize("w", [CFG1_SWA_8K, CFG2_GLOBAL_8K, CFG4_SWA_32K], ids=lambda w: w.name)
+# the 8k SWA workload with RoPE: positions up to m + 8191 test the angle's
+# argument reduction
+CFG1_SWA_8K_ROPE = replace(CFG1_SWA_8K, name=CFG1_SWA_8K.name + "_rope",
+                           dims=replace(CFG1_SWA_8K.dims, rope_base=10000.0))
+
+
+@pytest.mark.parametrize("w", [CFG1_SWA_8K, CFG2_GLOBAL_8K, CFG4_SWA_32K, CFG1_SWA_8K_ROPE],
+                         ids=lambda w: w.name)
 def test_prefill_full_size(w):
     dims = w.dims
     print(f"case {w.name} B={w.batch} n={w.seqlen}", flush=True)
