@@ -30,14 +30,20 @@ class LayerDims:
     dtype: str  # "f32" or "bf16"
     eps: float = 1e-6
     rope_base: float = 0.0  # rotary embedding base of Q and K; 0: none
+    ssm_heads: int = 0      # Mamba2 SSM heads (per-head Delta and scalar A); 0: Mamba
 
     @property
     def attn_width(self) -> int:
         return self.n_heads * self.head_dim
 
+    @property
+    def dt_width(self) -> int:
+        """Columns of the dt block: one per SSM head (Mamba2) or per channel."""
+        return self.ssm_heads or self.d_inner
+
     def n_in(self, kv_producer: bool = True) -> int:
         kv = 2 * self.n_kv_heads * self.head_dim if kv_producer else 0
-        return self.attn_width + kv + 3 * self.d_inner + 2 * self.d_state
+        return self.attn_width + kv + 2 * self.d_inner + self.dt_width + 2 * self.d_state
 
     @property
     def fused_width(self) -> int:
@@ -48,7 +54,7 @@ class LayerDims:
                     n_kv_heads=self.n_kv_heads, head_dim=self.head_dim,
                     d_inner=self.d_inner, d_state=self.d_state,
                     d_conv=self.d_conv, n_meta=self.n_meta, eps=self.eps,
-                    rope_base=self.rope_base)
+                    rope_base=self.rope_base, ssm_heads=self.ssm_heads)
 
 
 @dataclass(frozen=True)

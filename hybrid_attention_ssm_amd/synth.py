@@ -58,9 +58,11 @@ def layer_weights(rng, dims: LayerDims, kv_producer: bool = True) -> dict:
     w_in = _store(dims, _normal(rng, (dims.n_in(True), d), (1.0 / d) ** 0.5))
     if not kv_producer:
         w_in = np.ascontiguousarray(np.concatenate([w_in[:Wa], w_in[Wa + 2 * kv:]]))
-    dt = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), size=D))
+    dtw = dims.dt_width                       # D channels, or Mamba2 heads
+    dt = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), size=dtw))
     dt_bias = np.log(np.expm1(dt)).astype(np.float32)
-    A = (-np.exp(rng.uniform(np.log(1.0), np.log(16.0), size=(D, N)))).astype(np.float32)
+    a_shape = (dims.ssm_heads,) if dims.ssm_heads else (D, N)
+    A = (-np.exp(rng.uniform(np.log(1.0), np.log(16.0), size=a_shape))).astype(np.float32)
     conv_w = _store(dims, _normal(rng, (D, k), (1.0 / k) ** 0.5))
     conv_b = np.zeros(D, np.float32)
     w_out = _store(dims, _normal(rng, (d, Wa + D), (1.0 / (Wa + D)) ** 0.5))

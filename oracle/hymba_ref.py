@@ -46,6 +46,16 @@ Readings where the pages are silent or ambiguous (each is a stated choice):
     pos is the row of X~ = [R; X], so meta row j sits at position j and real
     position p at m + p; a decode token at real position p is at m + p.
     b = 0 (the default) leaves Q and K as projected.   [paper §3 training]
+  * Mamba2 SSM heads (optional; the authors' reply on Mamba vs Mamba2 says
+    the hybrid head works with either and reports a model trained with
+    Mamba2 heads, without their shapes): with dims["ssm_heads"] = S > 0 the
+    D channels form S heads of P = D / S consecutive channels; the dt block
+    of the projection has S columns, so Delta_t is per head, and A is one
+    negative scalar per head.  The recurrence is Eq. 2 with those shared:
+    h_t[c,s] = exp(Delta_t[h] A[h]) h_{t-1}[c,s] + Delta_t[h] u_t[c] B_t[s],
+    h = c // P (Mamba-2's scalar-times-identity state matrix).  Everything
+    else (conv on xs, SiLU gate, no skip term, B and C shared by all
+    channels) is as for the Mamba heads.  S = 0 (the default): Mamba.
 
 The block around the layer (the pages name its MLP width, 5504 at 1.5B in the
 architecture table, and draw it in their architecture figure, but do not
@@ -99,6 +109,26 @@ def _rope_base(dims):
     return float(dict(dims).get("rope_base", 0.0) or 0.0)
 
 
+def _ssm_heads(dims):
+    return int(dict(dims).get("ssm_heads", 0) or 0)
+
+
+def ssm_params(delta, A, dims):
+    """Per-channel Delta [..., D] and per-(channel, state) A [D, N] of the SSM
+    heads: unchanged for Mamba heads; for Mamba2 heads (header reading) each
+    head's Delta and scalar A are shared by its P = D / S channels and A by
+    every state."""
+    S = _ssm_heads(dims)
+    if not S:
+        return _f64(delta), _f64(A)
+    g = dict(dims)
+    D, N = g["d_inner"], g["d_state"]
+    P = D // S
+    delta_c = np.repeat(_f64(delta), P, axis=-1)
+    A_c = np.repeat(np.repeat(_f64(A).reshape(S, 1), P, axis=0), N, axis=1)
+    return delta_c, A_c
+
+
 # ---------------------------------------------------------------------------
 # rotary position embedding (header reading: rotate-half pairs, positions are
 # the rows of X~)
@@ -131,7 +161,8 @@ def split_projection(P, dims, kv_producer=True):
     """
     d, H, G, hd, D, N, k, m, eps = _dims(dims)
     names = ["q"] + (["k", "v"] if kv_producer else []) + ["xs", "z", "dt", "B", "C"]
-    sizes = [H * hd] + ([G * hd, G * hd] if kv_producer else []) + [D, D, D, N, N]
+    dtw = _ssm_heads(dims) or D                 # Delta per head (Mamba2) or per channel
+    sizes = [H * hd] + ([G * hd, G * hd] if kv_producer else []) + [D, D, dtw, N, N]
     if P.shape[-1] != sum(sizes):
         raise ValueError(f"projection width {P.shape[-1]} != {sum(sizes)}")
     parts, c = {}, 0
@@ -288,10 +319,10 @@ def prefill(dims, weights, R, x, window, is_global, shared_kv=None, cache=None,
             i = m + int(p)
             o, _ = attend(Q[i], K, V, allowed_rows(i, m, window, is_global), scale)
             O[r] = o.reshape(-1)
-        delta = softplus(parts["dt"] + w["dt_bias"])
+        delta, A = ssm_params(softplus(parts["dt"] + w["dt_bias"]), w["A"], dims)
         xs = parts["xs"]
         u = silu(causal_conv(xs, w["conv_w"], w["conv_b"], np.zeros((k - 1, D))))
-        y, h = selective_scan(u, delta, w["A"], parts["B"], parts["C"], np.zeros((D, N)))
+        y, h = selective_scan(u, delta, A, parts["B"], parts["C"], np.zeros((D, N)))
         Y = y * silu(parts["z"])
         Yr = Y[m + rows]
         F = fuse(O, Yr, w["beta_attn"], w["beta_ssm"], eps)
@@ -334,9 +365,9 @@ def meta_prefix(dims, weights, R):
         k_rot = rope(parts["k"].reshape(m, G, hd), np.arange(m)[:, None], _rope_base(dims))
         res["k"] = k_rot.transpose(1, 0, 2).copy()
         res["v"] = parts["v"].reshape(m, G, hd).transpose(1, 0, 2).copy()
-    delta = softplus(parts["dt"] + w["dt_bias"])
+    delta, A = ssm_params(softplus(parts["dt"] + w["dt_bias"]), w["A"], dims)
     u = silu(causal_conv(parts["xs"], w["conv_w"], w["conv_b"], np.zeros((k - 1, D))))
-    _, h = selective_scan(u, delta, w["A"], parts["B"], parts["C"], np.zeros((D, N)))
+    _, h = selective_scan(u, delta, A, parts["B"], parts["C"], np.zeros((D, N)))
     res["h0"] = h
     res["conv_tail"] = _tail(parts["xs"], k)
     return res
@@ -393,8 +424,8 @@ def decode_step(dims, weights, x_t, meta_k, meta_v, window, is_global, cache, h,
         win = np.concatenate([_f64(conv[b]), parts["xs"][None, :]])   # [k, D]
         c = _f64(w["conv_b"]) + np.sum(w["conv_w"].T * win, axis=0)
         u = silu(c)
-        delta = softplus(parts["dt"] + w["dt_bias"])
-        hb = np.exp(delta[:, None] * w["A"]) * _f64(h[b]) + (delta * u)[:, None] * parts["B"][None, :]
+        delta, A = ssm_params(softplus(parts["dt"] + w["dt_bias"]), w["A"], dims)
+        hb = np.exp(delta[:, None] * A) * _f64(h[b]) + (delta * u)[:, None] * parts["B"][None, :]
         y = hb @ parts["C"]
         Y = y * silu(parts["z"])
         F = fuse(o.reshape(-1), Y, w["beta_attn"], w["beta_ssm"], eps)

@@ -181,3 +181,43 @@ def test_unmutated_rope_agrees():
 def test_rope_pin_catches_mutant(name, monkeypatch):
     monkeypatch.setattr(ref, "rope", ROPE_MUTANTS[name])
     assert _rope_err() > 1e-4, f"mutant '{name}' not caught"
+
+
+# Mamba2 heads: caught by the library composition (SSD matrix form)
+_orig_ssm_params = ref.ssm_params
+
+
+def _m2_err():
+    from tests.test_oracle_pins import GQA_M2
+    x, R, w = _layer(GQA_M2, 26, seed=46)
+    got = ref.prefill(GQA_M2.as_dict(), w, R, x, 7, False)
+    want = layer_by_library(GQA_M2, w, R, x[0], 7, False)
+    return float(np.abs(got["out"][0] - want["out"]).max())
+
+
+def _m2_interleaved_heads(delta, A, dims):
+    S = dict(dims).get("ssm_heads", 0)
+    if not S:
+        return _orig_ssm_params(delta, A, dims)
+    D, N = dict(dims)["d_inner"], dict(dims)["d_state"]
+    head = np.arange(D) % S                      # channel c -> head c % S instead of c // P
+    return np.asarray(delta, dtype=np.float64)[..., head], np.repeat(np.asarray(A, np.float64)[head][:, None], N, axis=1)
+
+
+def _m2_first_head_decay(delta, A, dims):
+    d, a = _orig_ssm_params(delta, A, dims)
+    return d, np.full_like(a, a[0, 0])           # every head decays like head 0
+
+
+M2_MUTANTS = {"Mamba2 heads interleaved": _m2_interleaved_heads,
+              "Mamba2 decay of head 0 everywhere": _m2_first_head_decay}
+
+
+def test_unmutated_mamba2_agrees():
+    assert _m2_err() < 1e-9
+
+
+@pytest.mark.parametrize("name", sorted(M2_MUTANTS))
+def test_mamba2_pin_catches_mutant(name, monkeypatch):
+    monkeypatch.setattr(ref, "ssm_params", M2_MUTANTS[name])
+    assert _m2_err() > 1e-4, f"mutant '{name}' not caught"

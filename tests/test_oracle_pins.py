@@ -68,8 +68,9 @@ def layer_by_library(dims: LayerDims, w, R, xb, window, is_global):
                          dims.d_inner, dims.d_state, dims.d_conv)
     Xt = torch.cat([t(R), t(xb)])
     P = TF.linear(Xt, t(w["w_in"]))
+    S = dims.ssm_heads
     q, kk, v, xs, z, dt, Bm, Cm = torch.split(
-        P, [H * hd, G * hd, G * hd, D, D, D, N, N], dim=-1)
+        P, [H * hd, G * hd, G * hd, D, D, S or D, N, N], dim=-1)
     if dims.rope_base:
         q = rope_by_complex(q.view(T, H, hd), torch.arange(T)[:, None], dims.rope_base).reshape(T, H * hd)
         kk = rope_by_complex(kk.view(T, G, hd), torch.arange(T)[:, None], dims.rope_base).reshape(T, G * hd)
@@ -92,7 +93,23 @@ def layer_by_library(dims: LayerDims, w, R, xb, window, is_global):
     y = torch.zeros(T, D, dtype=torch.float64)
     hT = torch.zeros(D, N, dtype=torch.float64)
     lower = (j <= i)
-    for ch in range(D):
+    if S:
+        # Mamba2 heads in the SSD matrix form: per head a scalar decay, so
+        # y = ((C B^T) o L o Delta_tau) u with L[i, j] = exp(A_h sum_{k=j+1..i} Delta_k)
+        Pc = D // S
+        CB = Cm @ Bm.T                                    # [T, T]
+        for hh in range(S):
+            diff = torch.where(lower, cs[:, hh][:, None] - cs[:, hh][None, :], torch.zeros(()))
+            Lm = torch.where(lower, torch.exp(A[hh] * diff), torch.zeros(()))
+            M = CB * Lm * delta[:, hh][None, :]
+            cols = slice(hh * Pc, (hh + 1) * Pc)
+            y[:, cols] = M @ u[:, cols]
+            wT = torch.exp(A[hh] * (cs[-1, hh] - cs[:, hh])) * delta[:, hh]     # [T]
+            hT[cols] = (u[:, cols] * wT[:, None]).T @ Bm
+        D_loop = 0
+    else:
+        D_loop = D
+    for ch in range(D_loop):
         # prod_{k=j+1..i} exp(A Delta_k) = exp(A (cs_i - cs_j)) for j <= i
         diff = torch.where(lower, cs[:, ch][:, None] - cs[:, ch][None, :], torch.zeros(()))
         E = torch.exp(A[ch][None, None, :] * diff[:, :, None])          # [T, T, N]
@@ -110,11 +127,13 @@ def layer_by_library(dims: LayerDims, w, R, xb, window, is_global):
 
 
 GQA_ROPE = replace(GQA, rope_base=100.0)
+GQA_M2 = replace(GQA, ssm_heads=3)                   # Mamba2 heads of 8 channels
 
 
 @pytest.mark.parametrize("dims,n,window,is_global", [
     (TINY, 40, 16, False), (TINY, 24, 16, True), (GQA, 30, 7, False), (GQA, 17, 5, True),
-    (GQA_ROPE, 30, 7, False), (replace(TINY, rope_base=10000.0), 24, 16, True)])
+    (GQA_ROPE, 30, 7, False), (replace(TINY, rope_base=10000.0), 24, 16, True),
+    (GQA_M2, 30, 7, False), (replace(TINY, ssm_heads=8), 24, 16, True)])
 def test_layer_matches_library_composition(dims, n, window, is_global):
     x, R, w = _layer(dims, n, seed=11)
     got = ref.prefill(dims.as_dict(), w, R, x, window, is_global)
@@ -321,7 +340,7 @@ def test_consumer_reads_producer_kv():
 
 @pytest.mark.parametrize("is_global,n0,steps,cap,dims", [
     (False, 5, 4, 6, GQA), (False, 9, 6, 6, GQA), (True, 5, 4, 16, GQA),
-    (False, 9, 6, 6, GQA_ROPE), (True, 5, 4, 16, GQA_ROPE)])
+    (False, 9, 6, 6, GQA_ROPE), (True, 5, 4, 16, GQA_ROPE), (False, 9, 6, 6, GQA_M2)])
 def test_prefill_then_decode_equals_longer_prefill(is_global, n0, steps, cap, dims):
     """prefill(n) + k decode steps == prefill(n + k): outputs, state, conv
     tail and cache slots (including ring wrap-around when n + k > cap); with
@@ -512,3 +531,31 @@ def test_meta_prefix_keys_carry_meta_positions():
     pre = ref.prefill(GQA_ROPE.as_dict(), w, R, x, 4, False)
     m = GQA_ROPE.n_meta
     np.testing.assert_allclose(mp["k"], pre["K_all"][0, :m].transpose(1, 0, 2), rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Mamba2 SSM heads
+# ---------------------------------------------------------------------------
+def test_mamba2_heads_of_one_channel_are_mamba_with_state_independent_decay():
+    """S = D heads of one channel each: Mamba heads whose A row is one value."""
+    dims2 = replace(GQA, ssm_heads=GQA.d_inner)
+    x, R, w2 = _layer(dims2, 12, seed=44)
+    w1 = dict(w2, A=np.repeat(np.asarray(w2["A"]).reshape(-1, 1), GQA.d_state, axis=1))
+    a = ref.prefill(dims2.as_dict(), w2, R, x, 5, False)
+    b = ref.prefill(GQA.as_dict(), w1, R, x, 5, False)
+    np.testing.assert_allclose(a["out"], b["out"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(a["h"], b["h"], rtol=1e-12, atol=1e-14)
+
+
+def test_mamba2_meta_prefix_matches_prefill_state():
+    x, R, w = _layer(GQA_M2, 1, seed=45)
+    mp = ref.meta_prefix(GQA_M2.as_dict(), w, R)
+    # the state after the meta rows is the state a prefill starts its real rows from:
+    # a prefill of one real token from zero equals one decode step from mp
+    pre = ref.prefill(GQA_M2.as_dict(), w, R, x, 4, False)
+    cache = dict(k=np.zeros((1, GQA_M2.n_kv_heads, 4, GQA_M2.head_dim)), v=np.zeros((1, GQA_M2.n_kv_heads, 4, GQA_M2.head_dim)),
+                 len=np.zeros(1, np.int64), is_ring=True)
+    r = ref.decode_step(GQA_M2.as_dict(), w, x[:, 0], mp["k"], mp["v"], 4, False, cache,
+                        mp["h0"][None], mp["conv_tail"][None])
+    np.testing.assert_allclose(r["out"], pre["out"][:, 0], rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(r["h"], pre["h"], rtol=1e-10, atol=1e-12)
