@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 MFMA_BF16_PEAK = 2.5166e15   # dense bf16 FLOP/s, MI355X
 HBM_PEAK = 8.0e12            # bytes/s, MI355X HBM3E
 ROPE_BASE = 10000.0          # rotary base of the RoPE prefill line (the value does not change the work)
+MAMBA2_HEADS = 64            # SSM heads of the Mamba2 prefill line (50 channels each)
 
 
 def log(msg):
@@ -103,16 +104,19 @@ def decode_bytes(dims, B, layers, p, window, ring_cap, global_cap):
 
 
 # ---------------------------------------------------------------------------
-def bench_prefill(args, hb, torch, rope_base=0.0):
+def bench_prefill(args, hb, torch, rope_base=0.0, ssm_heads=0):
     """The 8k SWA prefill; rope_base > 0 times the same layer with Q and K
-    turned by the rotary embedding (same inputs)."""
+    turned by the rotary embedding (same inputs), ssm_heads > 0 with Mamba2
+    SSM heads (inputs drawn for that layout)."""
     from dataclasses import replace
     from hybrid_attention_ssm_amd.configs import CFG1_SWA_8K
     from hybrid_attention_ssm_amd.synth import prefill_inputs
     w = CFG1_SWA_8K
-    dims = replace(w.dims, rope_base=rope_base) if rope_base else w.dims
+    dims = replace(w.dims, rope_base=rope_base, ssm_heads=ssm_heads)
+    w = replace(w, dims=dims)
     B, n, W = w.batch, w.seqlen, w.window
-    tag = f" (RoPE base {rope_base:g})" if rope_base else ""
+    tag = ((f" (RoPE base {rope_base:g})" if rope_base else "") +
+           (f" (Mamba2 heads: {ssm_heads})" if ssm_heads else ""))
     log(f"[bench] prefill setup {w.name}{tag}")
     inp = prefill_inputs(w)
     sd = hb.storage_dtype(dims)
@@ -394,6 +398,8 @@ def main():
                     help="skip the 32-block decode stack line")
     ap.add_argument("--no-rope", action="store_true",
                     help="skip the prefill line with the rotary embedding of Q and K")
+    ap.add_argument("--no-mamba2", action="store_true",
+                    help="skip the prefill line with Mamba2 SSM heads")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192,
                     help="prefill tokens the CPU oracle runs (default: the whole 8k workload)")
     ap.add_argument("--cpu-sample-seqs", type=int, default=64,
@@ -426,9 +432,11 @@ def main():
         return
 
     pre = bench_prefill(args, hb, torch) if args.only in ("prefill", "both") else None
-    pre_rope = None
+    pre_rope = pre_m2 = None
     if pre is not None and not args.no_rope:
         pre_rope = bench_prefill(args, hb, torch, rope_base=ROPE_BASE)
+    if pre is not None and not args.no_mamba2:
+        pre_m2 = bench_prefill(args, hb, torch, ssm_heads=MAMBA2_HEADS)
     dec = bench_decode(args, hb, torch) if args.only in ("decode", "both") else None
     stack = None
     if args.only in ("decode", "both") and not args.no_stack:
@@ -473,6 +481,20 @@ def main():
                            "mfma_frac_layer": fl["total"] / (pre_rope["ms_step"] * 1e-3) / MFMA_BF16_PEAK,
                            "stage_us": {k: v * 1e3 for k, v in pre_rope["stages"].items()},
                            "inproj_extra_us": (t_in_r - t_in) * 1e3 if (t_in_r and t_in) else None}
+        if pre_m2 is not None:
+            # the same workload with Mamba2 SSM heads: the dt block shrinks to one column per head
+            # and the scan takes one exp per (token, channel)
+            dd = pre_m2["dims"]
+            T = pre["B"] * pre["n"]
+            fl2 = pre_m2["flops"]
+            t_scan2 = pre_m2["stages"].get("scan")
+            rec["mamba2"] = {"ssm_heads": MAMBA2_HEADS, "ms_per_step": pre_m2["ms_step"],
+                             "value": T / (pre_m2["ms_step"] * 1e-3), "unit": "tok/s",
+                             "mfma_frac_layer": fl2["total"] / (pre_m2["ms_step"] * 1e-3) / MFMA_BF16_PEAK,
+                             "algorithmic_gflop_per_step": fl2["total"] / 1e9,
+                             "stage_us": {k: v * 1e3 for k, v in pre_m2["stages"].items()},
+                             "scan_exps": T * dd.d_inner,
+                             "scan_exps_per_s": T * dd.d_inner / (t_scan2 * 1e-3) if t_scan2 else None}
         if t_in:
             ach = fl["inproj"] / (t_in * 1e-3)
             tr = measured_traffic("gemm_bf16_lds", pre["workload"])

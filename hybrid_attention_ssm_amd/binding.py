@@ -30,7 +30,8 @@ _i32 = ctypes.c_int32
 class HHDims(ctypes.Structure):
     _fields_ = [("d_model", _i32), ("n_heads", _i32), ("n_kv_heads", _i32), ("head_dim", _i32),
                 ("d_inner", _i32), ("d_state", _i32), ("d_conv", _i32), ("n_meta", _i32),
-                ("dtype", _i32), ("rms_eps", ctypes.c_float), ("rope_base", ctypes.c_float)]
+                ("dtype", _i32), ("rms_eps", ctypes.c_float), ("rope_base", ctypes.c_float),
+                ("ssm_heads", _i32)]
 
 
 class HHWeights(ctypes.Structure):
@@ -147,7 +148,8 @@ def storage_dtype(dims: LayerDims) -> torch.dtype:
 def hh_dims(dims: LayerDims) -> HHDims:
     return HHDims(dims.d_model, dims.n_heads, dims.n_kv_heads, dims.head_dim, dims.d_inner,
                   dims.d_state, dims.d_conv, dims.n_meta,
-                  HH_BF16 if dims.dtype == "bf16" else HH_F32, dims.eps, dims.rope_base)
+                  HH_BF16 if dims.dtype == "bf16" else HH_F32, dims.eps, dims.rope_base,
+                  dims.ssm_heads)
 
 
 def hh_version() -> str:

@@ -703,7 +703,8 @@ __device__ __forceinline__ float quad_sum(float v) {
 // .. +3.  Every load is independent and issued before any arithmetic; one
 // quad per thread at full occupancy keeps the most loads in flight (two or
 // four quads per thread measured slower: 15.5 -> 16.7 / 20.2 us).
-template <class T, int K>
+// SC: Mamba2 heads (Delta per head, one scalar A per head: one exp2 per lane)
+template <class T, int K, bool SC>
 __global__ void __launch_bounds__(256) decode_ssm_step(DecodeSsmArgs a) {
   constexpr int NS = 16;
   typedef float f32v4 __attribute__((ext_vector_type(4)));
@@ -721,11 +722,13 @@ __global__ void __launch_bounds__(256) decode_ssm_step(DecodeSsmArgs a) {
 #pragma unroll
   for (int j = 0; j < K; ++j) wk[j] = a.conv_w[(size_t)c * K + j];
   const float cb = a.conv_b[c];
-  const float dt = a.dt[ci];
+  const int hd_ = SC ? c / (a.D / a.S) : 0;   // Mamba2 head of channel c
+  const float dt = SC ? a.dt[(size_t)b * a.S + hd_] : a.dt[ci];
   const float zv = to_f32(reinterpret_cast<const T *>(a.z)[ci]);
   const float4 Bq = *reinterpret_cast<const float4 *>(a.bc + (size_t)b * 2 * NS + 4 * q);
   const float4 Cq = *reinterpret_cast<const float4 *>(a.bc + (size_t)b * 2 * NS + NS + 4 * q);
-  const float4 Aq = *reinterpret_cast<const float4 *>(a.A + (size_t)c * NS + 4 * q);
+  const float4 Aq = SC ? make_float4(a.A[hd_], 0.0f, 0.0f, 0.0f)
+                       : *reinterpret_cast<const float4 *>(a.A + (size_t)c * NS + 4 * q);
   // The state is read and written once per step, a step's worth of other
   // traffic apart: stream it (nt) rather than let it displace the weights
   // from the last-level cache.
@@ -737,10 +740,18 @@ __global__ void __launch_bounds__(256) decode_ssm_step(DecodeSsmArgs a) {
   for (int j = 0; j < K; ++j) cv = fmaf(wk[j], win[j], cv);
   const float du = dt * silu_f(cv);
   const float d2 = dt * kLog2e;
-  h.x = fmaf(exp2_fast(d2 * Aq.x), h.x, du * Bq.x);
-  h.y = fmaf(exp2_fast(d2 * Aq.y), h.y, du * Bq.y);
-  h.z = fmaf(exp2_fast(d2 * Aq.z), h.z, du * Bq.z);
-  h.w = fmaf(exp2_fast(d2 * Aq.w), h.w, du * Bq.w);
+  if constexpr (SC) {
+    const float decay = exp2_fast(d2 * Aq.x);
+    h.x = fmaf(decay, h.x, du * Bq.x);
+    h.y = fmaf(decay, h.y, du * Bq.y);
+    h.z = fmaf(decay, h.z, du * Bq.z);
+    h.w = fmaf(decay, h.w, du * Bq.w);
+  } else {
+    h.x = fmaf(exp2_fast(d2 * Aq.x), h.x, du * Bq.x);
+    h.y = fmaf(exp2_fast(d2 * Aq.y), h.y, du * Bq.y);
+    h.z = fmaf(exp2_fast(d2 * Aq.z), h.z, du * Bq.z);
+    h.w = fmaf(exp2_fast(d2 * Aq.w), h.w, du * Bq.w);
+  }
   float y = Cq.x * h.x;
   y = fmaf(Cq.y, h.y, y);
   y = fmaf(Cq.z, h.z, y);
@@ -759,10 +770,15 @@ template <class T>
 hipError_t launch_decode_ssm(const DecodeSsmArgs &a, hipStream_t s) {
   const long n = (long)a.B * a.D * 4;
   const dim3 grid((unsigned)((n + 255) / 256));
+  const bool sc = a.S > 0;
   switch (a.k) {
-    case 2: hipLaunchKernelGGL((decode_ssm_step<T, 2>), grid, dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((decode_ssm_step<T, 3>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_ssm_step<T, 4>), grid, dim3(256), 0, s, a); break;
+#define HH_SSM_CASE(KK) \
+    case KK: \
+      if (sc) hipLaunchKernelGGL((decode_ssm_step<T, KK, true>), grid, dim3(256), 0, s, a); \
+      else hipLaunchKernelGGL((decode_ssm_step<T, KK, false>), grid, dim3(256), 0, s, a); \
+      break;
+    HH_SSM_CASE(2) HH_SSM_CASE(3) HH_SSM_CASE(4)
+#undef HH_SSM_CASE
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

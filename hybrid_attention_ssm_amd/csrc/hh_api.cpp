@@ -74,6 +74,7 @@ size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Shape {
   int d, H, G, hd, D, N, k, m, Wa, KV, n_in, dtype;
+  int S, dtw;   // Mamba2 SSM heads (0: Mamba) and the dt block's width (S or D)
   size_t es;
   float eps, rope_base;
 };
@@ -104,11 +105,16 @@ hh_status check_dims(const hh_dims *dm, int kv_producer, Shape &s) {
     return fail(HH_ERR_INVALID_ARG, "rms_eps must be in [0, 1]");
   if (!(dm->rope_base == 0.0f || (dm->rope_base > 1.0f && dm->rope_base < 1e30f)))
     return fail(HH_ERR_INVALID_ARG, "rope_base must be 0 (no rotary embedding) or a finite base > 1");
+  if (dm->ssm_heads < 0 || (dm->ssm_heads > 0 && (dm->d_inner % dm->ssm_heads || dm->ssm_heads % 4)))
+    return fail(HH_ERR_INVALID_ARG, "ssm_heads %d must be 0 or divide d_inner %d and be a multiple of 4",
+                dm->ssm_heads, dm->d_inner);
   s.d = dm->d_model; s.H = dm->n_heads; s.G = dm->n_kv_heads; s.hd = dm->head_dim;
   s.D = dm->d_inner; s.N = dm->d_state; s.k = dm->d_conv; s.m = dm->n_meta;
+  s.S = dm->ssm_heads;
+  s.dtw = s.S ? s.S : s.D;
   s.Wa = s.H * s.hd;
   s.KV = kv_producer ? s.G * s.hd : 0;
-  s.n_in = s.Wa + 2 * s.KV + 3 * s.D + 2 * s.N;
+  s.n_in = s.Wa + 2 * s.KV + 2 * s.D + s.dtw + 2 * s.N;
   s.dtype = dm->dtype;
   s.es = dm->dtype == HH_BF16 ? 2 : 4;
   s.eps = dm->rms_eps;
@@ -157,7 +163,7 @@ PrefillLayout prefill_layout(const Shape &s, int B, int n) {
   }
   take(HH_WS_XS, T * s.D * 4);
   take(HH_WS_Z, T * s.D * s.es);
-  take(HH_WS_DELTA, T * s.D * 4);
+  take(HH_WS_DELTA, T * s.dtw * 4);
   take(HH_WS_BC, T * 2 * s.N * 4);
   take(HH_WS_O, T * s.Wa * s.es);
   take(HH_WS_Y, T * s.D * s.es);
@@ -184,7 +190,7 @@ DecodeLayout decode_layout(const Shape &s, int B, int max_real) {
   take(L.q, (size_t)B * s.Wa * s.es);
   take(L.xs, (size_t)B * s.D * 4);
   take(L.z, (size_t)B * s.D * s.es);
-  take(L.dt, (size_t)B * s.D * 4);
+  take(L.dt, (size_t)B * s.dtw * 4);
   take(L.bc, (size_t)B * 2 * s.N * 4);
   take(L.o, (size_t)B * s.Wa * s.es);
   take(L.y, (size_t)B * s.D * s.es);
@@ -227,7 +233,7 @@ hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, i
 
   hh::InProjOut e{};
   e.mode = hh::EPI_PREFILL;
-  e.Wa = s.Wa; e.KV = s.KV; e.D = s.D; e.N = s.N; e.hd = s.hd; e.n_rows_per_seq = n;
+  e.Wa = s.Wa; e.KV = s.KV; e.D = s.D; e.Ddt = s.dtw; e.N = s.N; e.hd = s.hd; e.n_rows_per_seq = n;
   e.q = at(ws, L.off[HH_WS_Q]);
   e.k_full = kfull; e.v_full = vfull;
   if (prod && kv && kv->cache_k) {
@@ -261,7 +267,7 @@ hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, i
   sa.h_out = state ? state->h : nullptr;
   sa.tail_out = state ? state->conv : nullptr;
   sa.carry = reinterpret_cast<float *>(at(ws, L.off[HH_WS_SCAN]));
-  sa.B = B; sa.n = n; sa.D = s.D; sa.N = s.N; sa.k = s.k; sa.chunk = L.chunk;
+  sa.B = B; sa.n = n; sa.D = s.D; sa.N = s.N; sa.k = s.k; sa.S = s.S; sa.chunk = L.chunk;
   {
     Stage sg(st, "scan");
     err = hh::launch_scan<T>(sa, st);
@@ -297,7 +303,7 @@ hh_status meta_prefix_t(const Shape &s, const hh_weights *w, const void *R, void
                         float *h0, float *tail, void *ws, const PrefillLayout &L, hipStream_t st) {
   hh::InProjOut e{};
   e.mode = hh::EPI_META;
-  e.Wa = s.Wa; e.KV = s.KV; e.D = s.D; e.N = s.N; e.hd = s.hd; e.n_rows_per_seq = s.m;
+  e.Wa = s.Wa; e.KV = s.KV; e.D = s.D; e.Ddt = s.dtw; e.N = s.N; e.hd = s.hd; e.n_rows_per_seq = s.m;
   e.q = at(ws, L.off[HH_WS_Q]);
   e.k_full = mk; e.v_full = mv;
   e.xs = reinterpret_cast<float *>(at(ws, L.off[HH_WS_XS])); e.z = at(ws, L.off[HH_WS_Z]);
@@ -313,7 +319,7 @@ hh_status meta_prefix_t(const Shape &s, const hh_weights *w, const void *R, void
   sa.h0 = nullptr; sa.tail0 = nullptr; sa.y = nullptr;
   sa.h_out = h0; sa.tail_out = tail;
   sa.carry = reinterpret_cast<float *>(at(ws, L.off[HH_WS_SCAN]));
-  sa.B = 1; sa.n = s.m; sa.D = s.D; sa.N = s.N; sa.k = s.k; sa.chunk = L.chunk;
+  sa.B = 1; sa.n = s.m; sa.D = s.D; sa.N = s.N; sa.k = s.k; sa.S = s.S; sa.chunk = L.chunk;
   hipError_t err = hh::launch_scan<T>(sa, st);
   return err == hipSuccess ? HH_OK : hip_fail(err, "meta scan");
 }
@@ -325,7 +331,7 @@ hh_status decode_t(const Shape &s, const hh_weights *w, const void *x, int B, co
   const bool prod = w->kv_producer != 0;
   hh::InProjOut e{};
   e.mode = hh::EPI_DECODE;
-  e.Wa = s.Wa; e.KV = s.KV; e.D = s.D; e.N = s.N; e.hd = s.hd; e.n_rows_per_seq = 1;
+  e.Wa = s.Wa; e.KV = s.KV; e.D = s.D; e.Ddt = s.dtw; e.N = s.N; e.hd = s.hd; e.n_rows_per_seq = 1;
   e.q = at(ws, L.q);
   e.cache_k = kv->cache_k; e.cache_v = kv->cache_v; e.cap = kv->cap; e.is_ring = kv->is_ring;
   e.len = kv->len;
@@ -350,7 +356,7 @@ hh_status decode_t(const Shape &s, const hh_weights *w, const void *x, int B, co
   sa.xs = e.xs; sa.z = e.z; sa.dt = e.dt; sa.bc = e.bc;
   sa.A = w->A; sa.conv_w = w->conv_w; sa.conv_b = w->conv_b;
   sa.h = state->h; sa.conv = state->conv; sa.y = at(ws, L.y);
-  sa.B = B; sa.D = s.D; sa.N = s.N; sa.k = s.k;
+  sa.B = B; sa.D = s.D; sa.N = s.N; sa.k = s.k; sa.S = s.S;
   hipError_t err;
   bool o_ready = false;
   {

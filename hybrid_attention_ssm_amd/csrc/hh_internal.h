@@ -62,12 +62,14 @@ __device__ __forceinline__ float softplus_f(float v) {
 
 // ---- the in-projection column map ------------------------------------------
 // Columns of P = X W_in^T: Q [0, Wa) | K [Wa, Wa+KV) | V [Wa+KV, Wa+2KV) |
-// xs (D) | z (D) | dt (D) | B (N) | C (N); KV = 0 for a consumer layer.
+// xs (D) | z (D) | dt (Ddt: D, or one per Mamba2 head) | B (N) | C (N);
+// KV = 0 for a consumer layer.
 enum EpiMode : int { EPI_PREFILL = 0, EPI_DECODE = 1, EPI_META = 2 };
 
 struct InProjOut {
   int mode;
   int Wa, KV, D, N, hd, n_rows_per_seq;  // n_rows_per_seq: seqlen (prefill) or m (meta)
+  int Ddt;                    // dt block width: D, or the Mamba2 head count
   void *q;                    // [rows, Wa]
   void *k_full, *v_full;      // prefill: [B, G, n, hd]; meta: [G, m, hd]
   void *cache_k, *cache_v;    // prefill/decode cache [B, G, cap, hd] (may be null)
@@ -75,7 +77,7 @@ struct InProjOut {
   const int32_t *len;         // decode: position of the new token per row
   float *xs;                  // [rows, D] fp32 (SSM input features)
   void *z;                    // [rows, D]
-  float *dt;                  // [rows, D] softplus(dt + bias)
+  float *dt;                  // [rows, Ddt] softplus(dt + bias)
   float *bc;                  // [rows, 2N] B then C
   const float *dt_bias;       // [D]
   // Rotary embedding of Q and K (rope_base 0: none).  Position of a row:
@@ -221,7 +223,7 @@ __device__ __forceinline__ ColInfo<W> inproj_col(const InProjOut &e, int col) {
   col -= D;
   if (col < D) { ci.seg = 4; ci.c = col; return ci; }
   col -= D;
-  if (col < D) {
+  if (col < e.Ddt) {
     ci.seg = 5; ci.c = col;
 #pragma unroll
     for (int q = 0; q < W / 4; ++q) {
@@ -230,7 +232,7 @@ __device__ __forceinline__ ColInfo<W> inproj_col(const InProjOut &e, int col) {
     }
     return ci;
   }
-  ci.seg = 6; ci.c = col - D;
+  ci.seg = 6; ci.c = col - e.Ddt;
   return ci;
 }
 
@@ -350,7 +352,7 @@ __device__ __forceinline__ void inproj_storeW(const InProjOut &e, int row, const
       float sp[W];
 #pragma unroll
       for (int i = 0; i < W; ++i) sp[i] = softplus_f(v[i] + ci.bias[i]);
-      storeW_T<float, W>(e.dt + (size_t)row * D + ci.c, sp);
+      storeW_T<float, W>(e.dt + (size_t)row * e.Ddt + ci.c, sp);
       return;
     }
     default: storeW_T<float, W>(e.bc + (size_t)row * 2 * e.N + ci.c, v); return;
@@ -410,9 +412,9 @@ template <class T> hipError_t launch_attention(const AttnArgs &a, hipStream_t s)
 struct ScanArgs {
   const float *xs;         // [B*n, D] fp32
   const void *z;           // [B*n, D] (null: no gate, no Y)
-  const float *dt;         // [B*n, D]
+  const float *dt;         // [B*n, D], or [B*n, S] for Mamba2 heads
   const float *bc;         // [B*n, 2N]
-  const float *A;          // [D, N]
+  const float *A;          // [D, N], or [S] for Mamba2 heads
   const float *conv_w;     // [D, k]
   const float *conv_b;     // [D]
   const float *h0;         // [D, N] initial state (null: zero)
@@ -423,6 +425,7 @@ struct ScanArgs {
   float *carry;            // workspace for chunk carries
   int B, n, D, N, k;
   int chunk;               // time steps per chunk
+  int S;                   // Mamba2 heads (per-head Delta, scalar A); 0: Mamba
 };
 template <class T> hipError_t launch_scan(const ScanArgs &a, hipStream_t s);
 size_t scan_carry_bytes(int B, int n, int D, int N, int *chunk_out);
@@ -479,12 +482,13 @@ size_t decode_attn_part_bytes(int B, int H, int G, int hd, int m, int max_real,
 struct DecodeSsmArgs {
   const float *xs;         // [B, D] fp32
   const void *z;           // [B, D]
-  const float *dt, *bc;    // [B, D], [B, 2N]
-  const float *A, *conv_w, *conv_b;
+  const float *dt, *bc;    // [B, D] (Mamba2: [B, S]), [B, 2N]
+  const float *A, *conv_w, *conv_b;   // A [D, N] (Mamba2: [S])
   float *h;                // [B, D, N] in/out
   float *conv;             // [B, k-1, D] fp32 in/out
   void *y;                 // [B, D]
   int B, D, N, k;
+  int S;                   // Mamba2 heads; 0: Mamba
 };
 template <class T> hipError_t launch_decode_ssm(const DecodeSsmArgs &a, hipStream_t s);
 

@@ -20,6 +20,10 @@
 //   pass 3 (all chunks): rescan each chunk from its true incoming state and
 //          write Y; the last chunk writes the final state and conv history.
 // With one chunk only pass 3 runs.
+//
+// Mamba2 heads (a.S > 0, template flag SC): the P = D / S channels of a head
+// share Delta_t and one scalar A, so the decay exp(Delta A) is one exp2 per
+// (step, channel) for all N states instead of N.
 #include "hh_internal.h"
 
 namespace hh {
@@ -30,14 +34,25 @@ constexpr int KC = 4;       // conv taps held (shorter kernels are zero-padded)
 constexpr int TB = 8;       // time steps loaded per batch
 
 struct ChanParams {
-  float A2[NS];             // A * log2(e)
+  float A2[NS];             // A * log2(e) (Mamba2: A2[0] is the head's)
   float w[KC];              // conv taps, w[KC-1] multiplies the current row
   float bias;
+  int dcol, dstride;        // Delta of this channel: column and row stride
 };
 
+template <bool SC>
 __device__ __forceinline__ void load_params(const ScanArgs &a, int c, ChanParams &p) {
+  if constexpr (SC) {
+    const int h = c / (a.D / a.S);
+    p.A2[0] = a.A[h] * kLog2e;
+    p.dcol = h;
+    p.dstride = a.S;
+  } else {
 #pragma unroll
-  for (int s = 0; s < NS; ++s) p.A2[s] = a.A[(size_t)c * NS + s] * kLog2e;
+    for (int s = 0; s < NS; ++s) p.A2[s] = a.A[(size_t)c * NS + s] * kLog2e;
+    p.dcol = c;
+    p.dstride = a.D;
+  }
 #pragma unroll
   for (int j = 0; j < KC; ++j) {
     const int src = j - (KC - a.k);          // zero-pad taps in front
@@ -63,7 +78,7 @@ __device__ __forceinline__ void load_history(const ScanArgs &a, int b, int c, in
 
 // One time step of the channel recurrence.  bc points at B_t then C_t (the
 // same for every channel, so the loads are uniform).
-template <int MODE>
+template <int MODE, bool SC>
 __device__ __forceinline__ float scan_step(const ChanParams &p, float h[NS], float hist[KC - 1],
                                            float x, float dt, const float bv[NS],
                                            const float cv[NS], float &dsum) {
@@ -73,9 +88,10 @@ __device__ __forceinline__ float scan_step(const ChanParams &p, float h[NS], flo
   hist[0] = x;
   const float du = dt * silu_f(conv);
   float acc = 0.0f;
+  const float decay1 = SC ? exp2_fast(dt * p.A2[0]) : 0.0f;   // Mamba2: one per step
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const float decay = exp2_fast(dt * p.A2[s]);
+    const float decay = SC ? decay1 : exp2_fast(dt * p.A2[s]);
     h[s] = fmaf(decay, h[s], du * bv[s]);
     if (MODE == 1) acc = fmaf(cv[s], h[s], acc);
   }
@@ -90,7 +106,7 @@ __device__ __forceinline__ float scan_step(const ChanParams &p, float h[NS], flo
 // TB steps at a time.
 constexpr int SUB = 64;
 
-template <class T, int MODE>
+template <class T, int MODE, bool SC>
 __device__ __forceinline__ void scan_range(const ScanArgs &a, int b, int c, bool active, int t0,
                                            int t1, const ChanParams &p, float h[NS],
                                            float hist[KC - 1], float &dsum, float *sbc) {
@@ -128,7 +144,7 @@ __device__ __forceinline__ void scan_range(const ScanArgs &a, int b, int c, bool
       for (int i = 0; i < TB; ++i) {
         const size_t idx = (row0 + s0 + tb + i) * D + c;
         xo[i] = xs[idx];
-        dvo[i] = a.dt[idx];
+        dvo[i] = a.dt[(row0 + s0 + tb + i) * p.dstride + p.dcol];
         if (MODE == 1) zo[i] = zp[idx];
       }
     };
@@ -150,7 +166,7 @@ __device__ __forceinline__ void scan_range(const ScanArgs &a, int b, int c, bool
             cv[4 * q] = u.x; cv[4 * q + 1] = u.y; cv[4 * q + 2] = u.z; cv[4 * q + 3] = u.w;
           }
         }
-        const float acc = scan_step<MODE>(p, h, hist, xv[i], dv[i], bv, cv, dsum);
+        const float acc = scan_step<MODE, SC>(p, h, hist, xv[i], dv[i], bv, cv, dsum);
         if (MODE == 1 && y && active)
           y[(row0 + s0 + t + i) * D + c] = from_f32<T>(acc * silu_f(to_f32(zv[i])));
       }
@@ -170,7 +186,8 @@ __device__ __forceinline__ void scan_range(const ScanArgs &a, int b, int c, bool
           cv[4 * q] = u.x; cv[4 * q + 1] = u.y; cv[4 * q + 2] = u.z; cv[4 * q + 3] = u.w;
         }
       }
-      const float acc = scan_step<MODE>(p, h, hist, xs[idx], a.dt[idx], bv, cv, dsum);
+      const float acc = scan_step<MODE, SC>(p, h, hist, xs[idx],
+                                            a.dt[(row0 + s0 + t) * p.dstride + p.dcol], bv, cv, dsum);
       if (MODE == 1 && y && active) y[idx] = from_f32<T>(acc * silu_f(to_f32(z[idx])));
     }
   }
@@ -179,7 +196,7 @@ __device__ __forceinline__ void scan_range(const ScanArgs &a, int b, int c, bool
 }  // namespace
 
 // pass 1: summaries of chunks 0..C-2.  grid (C-1, ceil(D/64), B), 64 threads
-template <class T>
+template <class T, bool SC>
 __global__ void __launch_bounds__(64) scan_pass1(ScanArgs a) {
   const int ck = blockIdx.x, b = blockIdx.z;
   // lanes past the last channel compute a copy of it (every lane takes part
@@ -188,7 +205,7 @@ __global__ void __launch_bounds__(64) scan_pass1(ScanArgs a) {
   const int c = min(blockIdx.y * 64 + (int)threadIdx.x, a.D - 1);
   const int nc = (a.n + a.chunk - 1) / a.chunk;
   ChanParams p;
-  load_params(a, c, p);
+  load_params<SC>(a, c, p);
   const int t0 = ck * a.chunk, t1 = min(a.n, t0 + a.chunk);
   float hist[KC - 1];
   load_history<T>(a, b, c, t0, hist);
@@ -197,7 +214,7 @@ __global__ void __launch_bounds__(64) scan_pass1(ScanArgs a) {
   for (int s = 0; s < NS; ++s) h[s] = 0.0f;
   float dsum = 0.0f;
   __shared__ float4 sbc[SUB * 2 * NS / 4];
-  scan_range<T, 0>(a, b, c, active, t0, t1, p, h, hist, dsum, reinterpret_cast<float *>(sbc));
+  scan_range<T, 0, SC>(a, b, c, active, t0, t1, p, h, hist, dsum, reinterpret_cast<float *>(sbc));
   // carry layout: [B][nc][NS][D] states, then [B][nc][D] delta sums
   if (!active) return;
   float *hs = a.carry + ((size_t)b * nc + ck) * NS * a.D;
@@ -217,7 +234,7 @@ __global__ void __launch_bounds__(256) scan_pass2(ScanArgs a) {
   if (idx >= NS * a.D) return;
   const int s = idx / a.D, c = idx - s * a.D;
   const int nc = (a.n + a.chunk - 1) / a.chunk;
-  const float A2 = a.A[(size_t)c * NS + s] * kLog2e;
+  const float A2 = (a.S ? a.A[c / (a.D / a.S)] : a.A[(size_t)c * NS + s]) * kLog2e;
   float H = a.h0 ? a.h0[(size_t)c * NS + s] : 0.0f;
   const float *ds = a.carry + (size_t)a.B * nc * NS * a.D + (size_t)b * nc * a.D + c;
   float *hs = a.carry + ((size_t)b * nc * NS + s) * a.D + c;
@@ -242,7 +259,7 @@ __global__ void __launch_bounds__(256) scan_pass2(ScanArgs a) {
 }
 
 // pass 3: outputs of every chunk.  grid (C, ceil(D/64), B)
-template <class T>
+template <class T, bool SC>
 __global__ void __launch_bounds__(64) scan_pass3(ScanArgs a) {
   const int ck = blockIdx.x, b = blockIdx.z;
   // lanes past the last channel compute a copy of it (every lane takes part
@@ -251,7 +268,7 @@ __global__ void __launch_bounds__(64) scan_pass3(ScanArgs a) {
   const int c = min(blockIdx.y * 64 + (int)threadIdx.x, a.D - 1);
   const int nc = (a.n + a.chunk - 1) / a.chunk;
   ChanParams p;
-  load_params(a, c, p);
+  load_params<SC>(a, c, p);
   const int t0 = ck * a.chunk, t1 = min(a.n, t0 + a.chunk);
   float hist[KC - 1];
   load_history<T>(a, b, c, t0, hist);
@@ -266,7 +283,7 @@ __global__ void __launch_bounds__(64) scan_pass3(ScanArgs a) {
   }
   float dsum = 0.0f;
   __shared__ float4 sbc[SUB * 2 * NS / 4];
-  scan_range<T, 1>(a, b, c, active, t0, t1, p, h, hist, dsum, reinterpret_cast<float *>(sbc));
+  scan_range<T, 1, SC>(a, b, c, active, t0, t1, p, h, hist, dsum, reinterpret_cast<float *>(sbc));
   if (ck == nc - 1 && active) {
     if (a.h_out) {
       float *ho = a.h_out + ((size_t)b * a.D + c) * NS;
@@ -295,16 +312,21 @@ size_t scan_carry_bytes(int B, int n, int D, int N, int *chunk_out) {
   return (size_t)B * nc * (N + 1) * D * sizeof(float);
 }
 
-template <class T>
-hipError_t launch_scan(const ScanArgs &a, hipStream_t s) {
+template <class T, bool SC>
+static hipError_t launch_scan_t(const ScanArgs &a, hipStream_t s) {
   const int nc = (a.n + a.chunk - 1) / a.chunk;
   const int cw = (a.D + 63) / 64;
   if (nc > 1) {
-    hipLaunchKernelGGL(scan_pass1<T>, dim3(nc - 1, cw, a.B), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((scan_pass1<T, SC>), dim3(nc - 1, cw, a.B), dim3(64), 0, s, a);
     hipLaunchKernelGGL(scan_pass2, dim3((NS * a.D + 255) / 256, a.B), dim3(256), 0, s, a);
   }
-  hipLaunchKernelGGL(scan_pass3<T>, dim3(nc, cw, a.B), dim3(64), 0, s, a);
+  hipLaunchKernelGGL((scan_pass3<T, SC>), dim3(nc, cw, a.B), dim3(64), 0, s, a);
   return hipGetLastError();
+}
+
+template <class T>
+hipError_t launch_scan(const ScanArgs &a, hipStream_t s) {
+  return a.S ? launch_scan_t<T, true>(a, s) : launch_scan_t<T, false>(a, s);
 }
 
 template hipError_t launch_scan<float>(const ScanArgs &, hipStream_t);

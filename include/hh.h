@@ -78,20 +78,32 @@ typedef enum {
  * prefill K/V and the cache all hold rotated keys.  pos counts the rows of
  * [R; X]: meta token j is at position j, real position p at n_meta + p (a
  * decode token at real position len[b], or len[b] - 1 for a KV-sharing
- * consumer, likewise).  Must be 0 or a finite value > 1. */
+ * consumer, likewise).  Must be 0 or a finite value > 1.
+ *
+ * ssm_heads: the SSM heads' form (the authors' reply on Mamba vs Mamba2: the
+ * hybrid head works with either; shapes not given).  0 = Mamba (Eq. 2 as
+ * written: Delta per channel, A per channel and state).  S > 0 = Mamba2: the
+ * d_inner channels form S heads of P = d_inner / S consecutive channels, each
+ * head with one Delta_t (the dt block of w_in has S rows, dt_bias [S]) and
+ * one negative scalar A (A [S]); h_t[c,s] = exp(Delta_t[h] A[h]) h_{t-1}[c,s]
+ * + Delta_t[h] u_t[c] B_t[s] with h = c / P.  S must divide d_inner and be a
+ * multiple of 4. */
 typedef struct {
   int32_t d_model, n_heads, n_kv_heads, head_dim;
   int32_t d_inner, d_state, d_conv, n_meta;
   int32_t dtype;   /* hh_dtype */
   float rms_eps;   /* epsilon inside the RMS norm of both branches */
   float rope_base; /* rotary embedding base of Q and K; 0 = none */
+  int32_t ssm_heads; /* Mamba2 SSM heads S (see below); 0 = Mamba heads */
 } hh_dims;
 
 /* One layer's parameters (all device pointers, read only).
  *   w_in      [n_in, d_model] dtype, rows Q (H*hd) | K (G*hd) | V (G*hd) |
- *             xs (D) | z (D) | dt (D) | B (N) | C (N); the K and V rows are
- *             absent when kv_producer == 0 (n_in = H*hd + 3D + 2N).
+ *             xs (D) | z (D) | dt (D, or S for Mamba2 heads) | B (N) | C (N);
+ *             the K and V rows are absent when kv_producer == 0
+ *             (n_in = H*hd + 3D + 2N for Mamba heads).
  *   dt_bias   [D] fp32       A [D, N] fp32 (negative)
+ *             (Mamba2 heads: dt_bias [S], A [S])
  *   conv_w    [D, k] fp32 (tap k-1 multiplies the current row)   conv_b [D] fp32
  *   beta_attn [H*hd] fp32    beta_ssm [D] fp32
  *   w_out     [d_model, H*hd + D] dtype

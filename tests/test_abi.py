@@ -69,7 +69,8 @@ def test_workspace_sizes():
     (dict(head_dim=128), 2), (dict(d_state=8), 2), (dict(d_conv=5), 2), (dict(n_kv_heads=3), 1),
     (dict(d_model=60), 2), (dict(n_heads=0), 1), (dict(eps=-1.0), 1),
     (dict(rope_base=-10.0), 1), (dict(rope_base=0.5), 1), (dict(rope_base=float("nan")), 1),
-    (dict(rope_base=float("inf")), 1)])
+    (dict(rope_base=float("inf")), 1), (dict(ssm_heads=-1), 1), (dict(ssm_heads=6), 1),
+    (dict(ssm_heads=2), 1)])
 def test_bad_dims_rejected(change, status):
     assert _call_prefill(replace(TINY, **change)) == status
     assert hb.hh_last_error() != ""

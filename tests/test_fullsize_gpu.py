@@ -40,8 +40,13 @@ CFG1_SWA_8K_ROPE = replace(CFG1_SWA_8K, name=CFG1_SWA_8K.name + "_rope",
                            dims=replace(CFG1_SWA_8K.dims, rope_base=10000.0))
 
 
-@pytest.mark.parametrize("w", [CFG1_SWA_8K, CFG2_GLOBAL_8K, CFG4_SWA_32K, CFG1_SWA_8K_ROPE],
-                         ids=lambda w: w.name)
+# the 8k SWA workload with Mamba2 SSM heads (64 heads of 50 channels)
+CFG1_SWA_8K_MAMBA2 = replace(CFG1_SWA_8K, name=CFG1_SWA_8K.name + "_mamba2",
+                             dims=replace(CFG1_SWA_8K.dims, ssm_heads=64))
+
+
+@pytest.mark.parametrize("w", [CFG1_SWA_8K, CFG2_GLOBAL_8K, CFG4_SWA_32K, CFG1_SWA_8K_ROPE,
+                               CFG1_SWA_8K_MAMBA2], ids=lambda w: w.name)
 def test_prefill_full_size(w):
     dims = w.dims
     print(f"case {w.name} B={w.batch} n={w.seqlen}", flush=True)
