@@ -107,8 +107,11 @@ def _ragged_decode(dims, lens, window, gcap, seed):
 
 
 @pytest.mark.parametrize("dims", [TINY, SMALL_BF16, replace(SMALL_BF16, n_meta=70),
-                                  replace(SMALL_BF16, n_meta=0)],
-                         ids=["f32", "bf16-m128", "bf16-m70", "bf16-m0"])
+                                  replace(SMALL_BF16, n_meta=0),
+                                  replace(TINY, rope_base=10000.0), replace(SMALL_BF16, rope_base=10000.0),
+                                  replace(SMALL_BF16, ssm_heads=8, rope_base=500.0)],
+                         ids=["f32", "bf16-m128", "bf16-m70", "bf16-m0", "f32-rope", "bf16-rope",
+                              "bf16-mamba2-rope"])
 def test_ragged_lengths_decode(dims):
     """Sequences at positions 1..45 in one batch: a ring of 16 (some not yet
     full, some wrapped several times) and a linear cache of 64."""

@@ -40,13 +40,16 @@ CFG1_SWA_8K_ROPE = replace(CFG1_SWA_8K, name=CFG1_SWA_8K.name + "_rope",
                            dims=replace(CFG1_SWA_8K.dims, rope_base=10000.0))
 
 
-# the 8k SWA workload with Mamba2 SSM heads (64 heads of 50 channels)
+# the 8k SWA workload with Mamba2 SSM heads: 64 heads of 50 channels and
+# 100 heads of 32
 CFG1_SWA_8K_MAMBA2 = replace(CFG1_SWA_8K, name=CFG1_SWA_8K.name + "_mamba2",
                              dims=replace(CFG1_SWA_8K.dims, ssm_heads=64))
+CFG1_SWA_8K_MAMBA2_100 = replace(CFG1_SWA_8K, name=CFG1_SWA_8K.name + "_mamba2_100",
+                                 dims=replace(CFG1_SWA_8K.dims, ssm_heads=100))
 
 
 @pytest.mark.parametrize("w", [CFG1_SWA_8K, CFG2_GLOBAL_8K, CFG4_SWA_32K, CFG1_SWA_8K_ROPE,
-                               CFG1_SWA_8K_MAMBA2], ids=lambda w: w.name)
+                               CFG1_SWA_8K_MAMBA2, CFG1_SWA_8K_MAMBA2_100], ids=lambda w: w.name)
 def test_prefill_full_size(w):
     dims = w.dims
     print(f"case {w.name} B={w.batch} n={w.seqlen}", flush=True)

@@ -23,6 +23,23 @@ pytestmark = pytest.mark.gpu
 
 TINY_M2 = replace(TINY, ssm_heads=8)                   # 16 channels per head
 SMALL_M2 = replace(SMALL_BF16, ssm_heads=8)            # 64 channels per head
+SMALL_P32 = replace(SMALL_BF16, ssm_heads=16)          # 32 channels per head
+
+
+@pytest.mark.parametrize("B,n,window,is_global", [
+    (2, 300, 100, False), (1, 64, 16, False), (1, 37, 16, False),
+    (1, 200, 64, True),
+    (2, 1100, 64, False)])    # with the 256x256-tile in-projection
+def test_prefill_mamba2_32_channel_heads(B, n, window, is_global):
+    """bf16, 32 channels per head, sequences of one partial chunk to many."""
+    # a global cache of about the sequence length (the error metric is relative
+    # to the RMS over all slots, so unwritten ones would inflate it)
+    _check_prefill(SMALL_P32, B, n, window, is_global, seed=400 + n, cache_cap=128 if not is_global else 256)
+
+
+def test_mamba2_hymba_shapes_100_heads():
+    """The 1.5B layer widths with 100 heads of 32 channels."""
+    _check_prefill(replace(HYMBA_1P5B, ssm_heads=100), 1, 333, 64, False, seed=8)
 
 
 @pytest.mark.parametrize("dims,B,n,window,is_global,cap", [
@@ -68,7 +85,8 @@ def test_meta_prefix_with_mamba2_heads(dims):
 
 @pytest.mark.parametrize("dims,n0,steps,window,is_global,cap", [
     (TINY_M2, 10, 12, 8, False, 8), (TINY_M2, 20, 5, 16, True, 32),
-    (SMALL_M2, 60, 9, 64, False, 64), (SMALL_M2, 130, 4, 64, True, 160)])
+    (SMALL_M2, 60, 9, 64, False, 64), (SMALL_M2, 130, 4, 64, True, 160),
+    (SMALL_P32, 150, 6, 64, False, 64)])
 def test_decode_with_mamba2_heads(dims, n0, steps, window, is_global, cap):
     B = 2
     inp = prefill_inputs(PrefillWorkload("pd", n0 + steps, dims, B, n0 + steps, window, is_global))
