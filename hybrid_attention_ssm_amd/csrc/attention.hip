@@ -177,14 +177,22 @@ attn_prefill_bf16(AttnArgs a) {
     else need_mask = (kbase + BKV - 1 > q0) || (kbase + BKV > a.n) ||
                      (!a.is_global && kbase < q0 + BQ - 1 - a.window + 1);
     if (need_mask) {
+      // this lane's query sees keys klo..khi of the tile's source (meta or
+      // real); one unsigned range test per score, no per-score branches
+      int klo = 0, khi = a.m - 1;
+      if (!meta) {
+        khi = min(qpos, a.n - 1);
+        klo = a.is_global ? 0 : qpos - a.window + 1;
+      }
+      const bool none = khi < klo;     // only padding lanes past the last query
+      const unsigned span = none ? 0u : (unsigned)(khi - klo);
+      const int d0 = kbase + 4 * lh - klo;   // key - klo of the lane's first score
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kbase + blk * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-          bool ok;
-          if (meta) ok = key < a.m;
-          else ok = key < a.n && key <= qpos && (a.is_global || qpos - key < a.window);
+          const int off = blk * 32 + 8 * (r >> 2) + (r & 3);
+          const bool ok = none ? false : (unsigned)(d0 + off) <= span;
           s[blk][r] = ok ? s[blk][r] : -INFINITY;
         }
     }
