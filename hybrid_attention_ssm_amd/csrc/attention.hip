@@ -32,10 +32,16 @@ constexpr int TILE_CHUNKS = BKV * HD / 8;   // 16-byte chunks per K (or V) tile
 
 __device__ __forceinline__ int swz(int row, int c) { return row * 8 + (c ^ ((row >> 1) & 7)); }
 
-__device__ __forceinline__ float wave_max32(float v) {  // combine lane l and l^32
-  return fmaxf(v, __shfl_xor(v, 32));
+// combine lane l with lane l ^ 32 (v_permlane32_swap: the two half-waves
+// trade values in the VALU, no LDS round trip)
+__device__ __forceinline__ float other_half(float v, bool low) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  // r[0]: lanes 0-31 keep v, lanes 32-63 get v of lane l-32; r[1]: lanes 0-31
+  // get v of lane l+32, lanes 32-63 keep v
+  return __uint_as_float(low ? r[1] : r[0]);
 }
-__device__ __forceinline__ float wave_sum32(float v) { return v + __shfl_xor(v, 32); }
+__device__ __forceinline__ float wave_max32(float v, bool low) { return fmaxf(v, other_half(v, low)); }
+__device__ __forceinline__ float wave_sum32(float v, bool low) { return v + other_half(v, low); }
 
 }  // namespace
 
@@ -132,20 +138,14 @@ attn_prefill_bf16(AttnArgs a) {
                                                kbase * HD * 2, 0, 0);
   };
   // ds_read_b64_tr_b16 source offsets (bytes) inside a V tile for
-  // (dblk, ks, call) = index dblk*8 + ks*2 + call
+  // (dblk, ks, call): row 16ks + 8call + r0 and column 32dblk + c0 with
+  // r0 = 4lh + (l%16)/4 < 8 and c0 = 16((l/16)%2) + 4(l%4) < 32.  The swizzle
+  // term (col/8) ^ ((row/2)%8) is (4dblk + c0/8) ^ (4call + r0/2) =
+  // 4(dblk ^ call) + ((c0/8) ^ (r0/2)), so every offset is one per-lane base
+  // plus 2048ks + 1024call + 64(dblk ^ call), a constant the read encodes.
   const int tr_row0 = 4 * lh + ((lane & 15) >> 2);
   const int tr_col0 = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  int tr_off[16];
-#pragma unroll
-  for (int dblk = 0; dblk < 2; ++dblk)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int call = 0; call < 2; ++call) {
-        const int row = 16 * ks + 8 * call + tr_row0;
-        const int col = 32 * dblk + tr_col0;
-        tr_off[dblk * 8 + ks * 2 + call] = row * 128 + (((col >> 3) ^ ((row >> 1) & 7)) << 4) + (col & 7) * 2;
-      }
+  const int tr_base = tr_row0 * 128 + (((tr_col0 >> 3) ^ (tr_row0 >> 1)) << 4) + (tr_col0 & 7) * 2;
 
   const float sl2 = kLog2e * rsqrtf((float)HD);
   // Online softmax with a lazily updated maximum: probabilities are taken as
@@ -164,13 +164,15 @@ attn_prefill_bf16(AttnArgs a) {
     f32x16 s[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
+      bf16x8 kf[4];   // a 32-key block's four k-step fragments, read together
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        kf[kk] = __builtin_bit_cast(bf16x8, sK[swz(blk * 32 + lr, kk * 2 + lh)]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[blk][r] = 0.0f;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, sK[swz(blk * 32 + lr, kk * 2 + lh)]);
-        s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[blk], 0, 0, 0);
-      }
+      for (int kk = 0; kk < 4; ++kk)
+        s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s[blk], 0, 0, 0);
     }
     bool need_mask;
     if (meta) need_mask = kbase + BKV > a.m;
@@ -201,7 +203,7 @@ attn_prefill_bf16(AttnArgs a) {
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[blk][r]);
-    mx = wave_max32(mx) * sl2;
+    mx = wave_max32(mx, lh == 0) * sl2;
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = exp2_fast(m_run - (m_new == -INFINITY ? 0.0f : m_new));
@@ -211,33 +213,35 @@ attn_prefill_bf16(AttnArgs a) {
       m_run = m_new;
     }
     const float neg_m = m_run == -INFINITY ? 0.0f : -m_run;
-    float rs = 0.0f;
+    float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // four independent partial sums
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = exp2_fast(fmaf(s[blk][r], sl2, neg_m));
         s[blk][r] = p;
-        rs += p;
+        rs[r & 3] += p;
       }
-    l_run += wave_sum32(rs);
+    l_run += wave_sum32((rs[0] + rs[1]) + (rs[2] + rs[3]), lh == 0);
     typedef short v4i16 __attribute__((ext_vector_type(4)));
-    const char *vbase = reinterpret_cast<const char *>(sV);
+    const char *vbase = reinterpret_cast<const char *>(sV) + tr_base;
+    bf16x8 pb[4];   // P^T in bf16, all four k-steps, before the V reads
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[ks][e] = (bf16)s[ks >> 1][8 * (ks & 1) + e];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 pb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = (bf16)s[ks >> 1][8 * (ks & 1) + e];
 #pragma unroll
       for (int dblk = 0; dblk < 2; ++dblk) {
         const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16 *)(vbase + tr_off[dblk * 8 + ks * 2]));
+            (__attribute__((address_space(3))) v4i16 *)(vbase + 2048 * ks + 64 * dblk));
         const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16 *)(vbase + tr_off[dblk * 8 + ks * 2 + 1]));
+            (__attribute__((address_space(3))) v4i16 *)(vbase + 2048 * ks + 1024 + 64 * (dblk ^ 1)));
         typedef short v8i16 __attribute__((ext_vector_type(8)));
         const v8i16 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         const bf16x8 vf = __builtin_bit_cast(bf16x8, both);
-        o[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[dblk], 0, 0, 0);
+        o[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[ks], o[dblk], 0, 0, 0);
       }
     }
   };
