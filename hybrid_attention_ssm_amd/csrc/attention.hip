@@ -30,7 +30,19 @@ constexpr int BQ = 32;      // queries per workgroup
 constexpr int BKV = 64;     // keys per tile
 constexpr int TILE_CHUNKS = BKV * HD / 8;   // 16-byte chunks per K (or V) tile
 
-__device__ __forceinline__ int swz(int row, int c) { return row * 8 + (c ^ ((row >> 1) & 7)); }
+// 16-byte chunk c of K/V tile row `row` sits at slot c ^ slot_xor(row).  The
+// LDS serves 256 bytes (64 banks) per cycle.  K fragment reads take 16 rows
+// per cycle, two rows per 256 bytes, so the eight even rows and the eight odd
+// rows need distinct slots: slot_xor is a permutation of (row/2) % 8.  The
+// transposing V reads take 4 consecutive rows x 32 bytes per 16 lanes, so the
+// two rows of a 4-row group that share a 256-byte half (r, r + 2) must differ
+// in the slot's bit 2, which the permutation (j%2)*4 + j/2 of j = (row/2) % 8
+// also gives.  Both read patterns are then free of bank conflicts.
+__device__ __forceinline__ int slot_xor(int row) {
+  const int j = (row >> 1) & 7;
+  return ((j & 1) << 2) | (j >> 1);
+}
+__device__ __forceinline__ int swz(int row, int c) { return row * 8 + (c ^ slot_xor(row)); }
 
 // combine lane l with lane l ^ 32 (v_permlane32_swap: the two half-waves
 // trade values in the VALU, no LDS round trip)
@@ -115,7 +127,7 @@ attn_prefill_bf16(AttnArgs a) {
   for (int j = 0; j < KI; ++j) {
     part[j] = (wave * KI + j) & 7;
     const int u = part[j] * 64 + lane;
-    const int row = u >> 3, c = (u & 7) ^ ((row >> 1) & 7);
+    const int row = u >> 3, c = (u & 7) ^ slot_xor(row);
     voff[j] = row * HD * 2 + c * 16;
   }
   auto issue = [&](int t, uint4 *dK, uint4 *dV) {
@@ -139,13 +151,20 @@ attn_prefill_bf16(AttnArgs a) {
   };
   // ds_read_b64_tr_b16 source offsets (bytes) inside a V tile for
   // (dblk, ks, call): row 16ks + 8call + r0 and column 32dblk + c0 with
-  // r0 = 4lh + (l%16)/4 < 8 and c0 = 16((l/16)%2) + 4(l%4) < 32.  The swizzle
-  // term (col/8) ^ ((row/2)%8) is (4dblk + c0/8) ^ (4call + r0/2) =
-  // 4(dblk ^ call) + ((c0/8) ^ (r0/2)), so every offset is one per-lane base
-  // plus 2048ks + 1024call + 64(dblk ^ call), a constant the read encodes.
+  // r0 = 4lh + (l%16)/4 < 8 and c0 = 16((l/16)%2) + 4(l%4) < 32.  slot_xor
+  // depends on (row/2) % 8 only, which 16ks leaves alone, so each offset is
+  // one of four per-lane bases (call, dblk) plus 2048ks, a constant the read
+  // encodes.
   const int tr_row0 = 4 * lh + ((lane & 15) >> 2);
   const int tr_col0 = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int tr_base = tr_row0 * 128 + (((tr_col0 >> 3) ^ (tr_row0 >> 1)) << 4) + (tr_col0 & 7) * 2;
+  int tr_base[2][2];
+#pragma unroll
+  for (int call = 0; call < 2; ++call)
+#pragma unroll
+    for (int dblk = 0; dblk < 2; ++dblk) {
+      const int row = 8 * call + tr_row0, col = 32 * dblk + tr_col0;
+      tr_base[call][dblk] = row * 128 + (((col >> 3) ^ slot_xor(row)) << 4) + (col & 7) * 2;
+    }
 
   const float sl2 = kLog2e * rsqrtf((float)HD);
   // Online softmax with a lazily updated maximum: probabilities are taken as
@@ -224,7 +243,7 @@ attn_prefill_bf16(AttnArgs a) {
       }
     l_run += wave_sum32((rs[0] + rs[1]) + (rs[2] + rs[3]), lh == 0);
     typedef short v4i16 __attribute__((ext_vector_type(4)));
-    const char *vbase = reinterpret_cast<const char *>(sV) + tr_base;
+    const char *vbase = reinterpret_cast<const char *>(sV);
     bf16x8 pb[4];   // P^T in bf16, all four k-steps, before the V reads
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
@@ -235,9 +254,9 @@ attn_prefill_bf16(AttnArgs a) {
 #pragma unroll
       for (int dblk = 0; dblk < 2; ++dblk) {
         const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16 *)(vbase + 2048 * ks + 64 * dblk));
+            (__attribute__((address_space(3))) v4i16 *)(vbase + tr_base[0][dblk] + 2048 * ks));
         const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16 *)(vbase + 2048 * ks + 1024 + 64 * (dblk ^ 1)));
+            (__attribute__((address_space(3))) v4i16 *)(vbase + tr_base[1][dblk] + 2048 * ks));
         typedef short v8i16 __attribute__((ext_vector_type(8)));
         const v8i16 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         const bf16x8 vf = __builtin_bit_cast(bf16x8, both);

@@ -608,7 +608,7 @@ __global__ void __launch_bounds__(64) decode_attn_combine(DecodeAttnArgs a) {
 // (5.8 rounds), global-layer attention 222.6 -> 220.1 us.
 constexpr int kDecodeTargetWG = 640;
 constexpr int kDecodeWGPerCU = 3;
-static int device_cus() {
+int device_cus() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)

@@ -73,10 +73,15 @@ struct LdsCfg {
   static constexpr int TM = WM / 32, TN = WN / 32;
   static constexpr int A_UNITS = BM * KCH, B_UNITS = BN * KCH;   // 16-byte units
   static constexpr int STAGE = A_UNITS + B_UNITS;
-  static constexpr int A_INS = A_UNITS / 64 / NWAVES;        // load instrs per wave
-  static constexpr int B_INS = B_UNITS / 64 / NWAVES;
+  // a stage is A_Q + B_Q load instructions of 64 x 16 bytes, dealt round the
+  // waves; when they do not divide evenly, the last waves repeat the first
+  // instructions (the same bytes into the same slots), so every wave issues
+  // the same count and waits for the same vmcnt
+  static constexpr int A_Q = A_UNITS / 64, B_Q = B_UNITS / 64;
+  static constexpr int A_INS = (A_Q + NWAVES - 1) / NWAVES;   // load instrs per wave
+  static constexpr int B_INS = (B_Q + NWAVES - 1) / NWAVES;
   static_assert(BK == 32 || BK == 64, "k-tile");
-  static_assert(A_INS * 64 * NWAVES == A_UNITS && B_INS * 64 * NWAVES == B_UNITS, "tile");
+  static_assert(A_Q * 64 == A_UNITS && B_Q * 64 == B_UNITS, "tile rows");
   // chunk c of row `row` sits at slot c ^ f(row): the 16 (32) rows one
   // fragment read touches with the same c land on distinct 16-byte bank groups
   __device__ static __forceinline__ int swz(int row, int c) {
@@ -105,15 +110,17 @@ gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int
   const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(B + (size_t)n0 * K), (short)0, (N - n0) * K * 2, 0x00020000);
   int voffA[Cfg::A_INS], voffB[Cfg::B_INS];
+  auto qA = [&](int j) { return (wave * Cfg::A_INS + j) % Cfg::A_Q; };   // instruction of the stage
+  auto qB = [&](int j) { return (wave * Cfg::B_INS + j) % Cfg::B_Q; };
 #pragma unroll
   for (int j = 0; j < Cfg::A_INS; ++j) {   // LDS unit u holds chunk of swz(row, kc) == u
-    const int u = (wave * Cfg::A_INS + j) * 64 + lane;
+    const int u = qA(j) * 64 + lane;
     const int row = u / Cfg::KCH, kc = Cfg::swz(row, u % Cfg::KCH) - row * Cfg::KCH;
     voffA[j] = (row * K + kc * 8) * 2;
   }
 #pragma unroll
   for (int j = 0; j < Cfg::B_INS; ++j) {
-    const int u = (wave * Cfg::B_INS + j) * 64 + lane;
+    const int u = qB(j) * 64 + lane;
     const int row = u / Cfg::KCH, kc = Cfg::swz(row, u % Cfg::KCH) - row * Cfg::KCH;
     voffB[j] = ((b_row(epi, n0 + row) - n0) * K + kc * 8) * 2;
   }
@@ -124,11 +131,11 @@ gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int
 #pragma unroll
     for (int j = 0; j < Cfg::A_INS; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsA, (lds_void *)(base + (wave * Cfg::A_INS + j) * 64), 16, voffA[j], soff, 0, 0);
+          rsA, (lds_void *)(base + qA(j) * 64), 16, voffA[j], soff, 0, 0);
 #pragma unroll
     for (int j = 0; j < Cfg::B_INS; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsB, (lds_void *)(base + Cfg::A_UNITS + (wave * Cfg::B_INS + j) * 64), 16, voffB[j],
+          rsB, (lds_void *)(base + Cfg::A_UNITS + qB(j) * 64), 16, voffB[j],
           soff, 0, 0);
   };
 
@@ -199,50 +206,56 @@ gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int
   wait_vmcnt<0>();
   __syncthreads();
 
-  constexpr int SROW = Cfg::WN + 8;
-  constexpr int LPR = Cfg::WN / 8;   // lanes per row; each stores two groups of 4 columns
+  // the wave's WN columns are staged CW at a time (all of them when WN <= 64)
+  constexpr int CW = Cfg::WN % 64 == 0 ? 64 : 32;
+  static_assert(Cfg::WN % CW == 0 && (CW == Cfg::WN || CW == 32), "epilogue chunks");
+  constexpr int SROW = CW + 8;
+  constexpr int LPR = CW / 8;   // lanes per row; each stores two groups of 4 columns
   constexpr int RPI = 64 / LPR;
   static_assert(Cfg::NWAVES * 32 * SROW * 4 <= (int)sizeof(smem), "epilogue strip fits");
   float *strip = reinterpret_cast<float *>(smem) + wave * 32 * SROW;
-  // a lane stores columns c0..c0+3 and WN/2+c0..+3 of every row it visits, so
+  // a lane stores columns c0..c0+3 and CW/2+c0..+3 of every row it visits, so
   // each store instruction writes one contiguous run per row; the routing of
-  // both groups is resolved once
-  const int c0 = (lane % LPR) * 4, c1 = Cfg::WN / 2 + c0;
-  const int g0 = n0 + wn * Cfg::WN + c0, g1 = n0 + wn * Cfg::WN + c1;
-  const bool ok0 = g0 < N, ok1 = g1 < N;
-  const typename Epi::template Col<4> ci0 = epi.template col_info<4>(ok0 ? g0 : 0);
-  const typename Epi::template Col<4> ci1 = epi.template col_info<4>(ok1 ? g1 : 0);
+  // both groups is resolved once per chunk
+  const int c0 = (lane % LPR) * 4, c1 = CW / 2 + c0;
 #pragma unroll
-  for (int i = 0; i < Cfg::TM; ++i) {
+  for (int ch = 0; ch < Cfg::WN / CW; ++ch) {
+    const int g0 = n0 + wn * Cfg::WN + ch * CW + c0, g1 = n0 + wn * Cfg::WN + ch * CW + c1;
+    const bool ok0 = g0 < N, ok1 = g1 < N;
+    const typename Epi::template Col<4> ci0 = epi.template col_info<4>(ok0 ? g0 : 0);
+    const typename Epi::template Col<4> ci1 = epi.template col_info<4>(ok1 ? g1 : 0);
 #pragma unroll
-    for (int j = 0; j < Cfg::TN; ++j)
+    for (int i = 0; i < Cfg::TM; ++i) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        strip[(8 * (r >> 2) + 4 * lh + (r & 3)) * SROW + j * 32 + lr] = acc[i][j][r];
-    // the strip is this wave's own: LDS keeps one wave's accesses in order,
-    // so only the compiler must not move the reads above the writes
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
+      for (int jj = 0; jj < CW / 32; ++jj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          strip[(8 * (r >> 2) + 4 * lh + (r & 3)) * SROW + jj * 32 + lr] = acc[i][ch * (CW / 32) + jj][r];
+      // the strip is this wave's own: LDS keeps one wave's accesses in order,
+      // so only the compiler must not move the reads above the writes
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll 1
-    for (int it = 0; it < 32 / RPI; ++it) {
-      const int rr = it * RPI + lane / LPR;
-      const float4 a = *reinterpret_cast<const float4 *>(strip + rr * SROW + c0);
-      const float4 b = *reinterpret_cast<const float4 *>(strip + rr * SROW + c1);
-      const float va[4] = {a.x, a.y, a.z, a.w}, vb[4] = {b.x, b.y, b.z, b.w};
-      const int row = m0 + wm * Cfg::WM + i * 32 + rr;
-      if (row < M) {
-        if constexpr (HasPairStore<Epi>::value) {
-          if (ok0 && ok1) {
-            epi.template store_pair<4>(row, ci0, va, ci1, vb);
-            continue;
+      for (int it = 0; it < 32 / RPI; ++it) {
+        const int rr = it * RPI + lane / LPR;
+        const float4 a = *reinterpret_cast<const float4 *>(strip + rr * SROW + c0);
+        const float4 b = *reinterpret_cast<const float4 *>(strip + rr * SROW + c1);
+        const float va[4] = {a.x, a.y, a.z, a.w}, vb[4] = {b.x, b.y, b.z, b.w};
+        const int row = m0 + wm * Cfg::WM + i * 32 + rr;
+        if (row < M) {
+          if constexpr (HasPairStore<Epi>::value) {
+            if (ok0 && ok1) {
+              epi.template store_pair<4>(row, ci0, va, ci1, vb);
+              continue;
+            }
           }
+          if (ok0) epi.template store<4>(row, ci0, va);
+          if (ok1) epi.template store<4>(row, ci1, vb);
         }
-        if (ok0) epi.template store<4>(row, ci0, va);
-        if (ok1) epi.template store<4>(row, ci1, vb);
       }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
     }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
   }
 #endif
 }
@@ -425,6 +438,10 @@ static hipError_t run_lds(const bf16 *A, int M, int K, const bf16 *B, int N, con
 // 256x256 tile, 8 waves of 128x64 (two per SIMD, so one wave's LDS waits and
 // barriers hide behind the other's MFMAs), 3 LDS stages (96 KB)
 using CfgLds = LdsCfg<256, 256, 128, 64, 3>;
+// 256x224 tile, 8 waves of 32x224: for outputs whose 256x256 tiles leave part
+// of the chip idle in their last round (8192 x 1600: 224 tiles on 256 CUs,
+// with 12% padding), 224-wide tiles give every CU one tile of 7/8 the area
+using CfgWide = LdsCfg<256, 224, 32, 224, 3>;
 // Few rows (decode, meta prefix): the weights dominate the traffic and each
 // workgroup streams a slab of 64 weight rows.  When those slabs alone leave
 // the chip short of workgroups (the output projection: 25 slabs) the K range
@@ -472,10 +489,24 @@ static hipError_t run_skinny(const bf16 *A, int M, int K, const bf16 *B, int N, 
   return run_skinny_cfg<CfgSkinny>(A, M, K, B, N, epi, part ? skinny_splits(M, K, N) : 1, part, s);
 }
 
+// rounds of one-tile-per-CU times the tile's area: the many-row kernel's time
+// up to its per-flop efficiency
+template <class Cfg>
+static long tile_cost(int M, int N, int cus) {
+  const long tiles = (long)((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
+  return (tiles + cus - 1) / cus * (long)Cfg::BM * Cfg::BN;
+}
+
 template <class Epi>
 static hipError_t run_bf16_auto(const bf16 *A, int M, int K, const bf16 *B, int N, const Epi &epi,
                                 float *part, hipStream_t s) {
-  if (M >= 1024) return run_lds<CfgLds>(A, M, K, B, N, epi, s);
+  if (M >= 1024) {
+    const int cus = device_cus();
+    // the wide tile reads more LDS per flop: only where it saves a tenth
+    if (10 * tile_cost<CfgWide>(M, N, cus) < 9 * tile_cost<CfgLds>(M, N, cus))
+      return run_lds<CfgWide>(A, M, K, B, N, epi, s);
+    return run_lds<CfgLds>(A, M, K, B, N, epi, s);
+  }
   return run_skinny(A, M, K, B, N, epi, part, s);
 }
 

@@ -399,6 +399,8 @@ template <class T>
 hipError_t launch_mlp_gate_up(const T *x, int M, int K, const T *w, int Ncols, T *h,
                               float *part, hipStream_t s);
 size_t skinny_part_bytes(int M, int K, int N);
+// compute units of the current device (256 if the query fails)
+int device_cus();
 
 struct AttnArgs {
   const void *q;           // [B*n, H*hd]
