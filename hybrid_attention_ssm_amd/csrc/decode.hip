@@ -12,6 +12,8 @@
 //
 // SSM (paper §2.1 Eq. (2)): one recurrence step per channel from the stored
 // state and conv history, updated in place.
+#include <atomic>
+
 #include "hh_internal.h"
 
 namespace hh {
@@ -609,10 +611,18 @@ __global__ void __launch_bounds__(64) decode_attn_combine(DecodeAttnArgs a) {
 constexpr int kDecodeTargetWG = 640;
 constexpr int kDecodeWGPerCU = 3;
 int device_cus() {
+  // queried once per device; concurrent first calls store the same value
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cached[kMaxDev];
   int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < kMaxDev) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
     return 256;
+  if (dev >= 0 && dev < kMaxDev) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 size_t decode_attn_part_bytes(int B, int H, int G, int hd, int m, int max_real, int *split_out,

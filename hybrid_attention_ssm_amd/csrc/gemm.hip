@@ -235,9 +235,14 @@ gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int
       // so only the compiler must not move the reads above the writes
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
+      // with 64 LDS banks a float4 read serves 16 lanes per cycle: when they
+      // are two rows of 8 lanes (CW = 64), take rows r and r + 4 (4 SROW
+      // floats apart, 128 bytes mod 256) rather than r and r + 1
+      const int q = lane / LPR;
+      const int qrow = (LPR == 8 && RPI == 8) ? ((q & 1) << 2) | (q >> 1) : q;
 #pragma unroll 1
       for (int it = 0; it < 32 / RPI; ++it) {
-        const int rr = it * RPI + lane / LPR;
+        const int rr = it * RPI + qrow;
         const float4 a = *reinterpret_cast<const float4 *>(strip + rr * SROW + c0);
         const float4 b = *reinterpret_cast<const float4 *>(strip + rr * SROW + c1);
         const float va[4] = {a.x, a.y, a.z, a.w}, vb[4] = {b.x, b.y, b.z, b.w};
