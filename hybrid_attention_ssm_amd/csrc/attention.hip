@@ -28,7 +28,6 @@ namespace {
 constexpr int HD = 64;      // bf16 path head dim
 constexpr int BQ = 32;      // queries per workgroup
 constexpr int BKV = 64;     // keys per tile
-constexpr int TILE_CHUNKS = BKV * HD / 8;   // 16-byte chunks per K (or V) tile
 
 // 16-byte chunk c of K/V tile row `row` sits at slot c ^ slot_xor(row).  The
 // LDS serves 256 bytes (64 banks) per cycle.  K fragment reads take 16 rows
