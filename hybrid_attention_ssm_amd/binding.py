@@ -17,7 +17,10 @@ import torch
 
 from .configs import LayerDims
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhymba_hh.so")
+# HH_LIB_PATH selects another build of the same library (the host-sanitizer
+# build of the ABI check); there is no other implementation to fall back to
+LIB_PATH = os.environ.get("HH_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                         "libhymba_hh.so")
 
 HH_F32, HH_BF16 = 0, 1
 HH_WS = ["Q", "K", "V", "XS", "Z", "DELTA", "BC", "O", "Y", "F", "SCAN", "GEMM"]

@@ -6,8 +6,8 @@
 // keys and to the cached positions max(0, p-W+1)..p (global: 0..p).  Position
 // q lives in slot q % cap of a ring cache or slot q of a linear one.  The key
 // range is split across workgroups (each keeps a running max, sum and
-// weighted V sum per head in the log2 domain) and a second kernel merges the
-// splits.  One workgroup serves every query head of its KV head, so each
+// weighted V sum per head in the log2 domain) and the decode norm merges the
+// splits on its way (a single split writes O directly).  One workgroup serves every query head of its KV head, so each
 // cached K/V row is read once per step.
 //
 // SSM (paper §2.1 Eq. (2)): one recurrence step per channel from the stored
@@ -164,7 +164,8 @@ __global__ void __launch_bounds__(DTHREADS) decode_attn_split(DecodeAttnArgs a) 
 //   ds_read_b64_tr_b16 (lane j of a 16-lane group gets element j%4 of the
 //   loads of lanes 4k + j/4).
 // The 4 waves' (max, sum, O) are merged through LDS into one partial per
-// (sequence, head, split); decode_attn_combine merges the splits.
+// (sequence, head, split); the decode norm (norm_fuse_parts) merges the
+// splits.
 constexpr int DB = 32;        // keys per block
 
 template <int HPG>
@@ -581,25 +582,6 @@ __global__ void __launch_bounds__(NW * 64) decode_attn_dma(DecodeAttnArgs a) {
   attn_dma_body<HPG, NW>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
-// grid (B*H); hd threads
-template <class T>
-__global__ void __launch_bounds__(64) decode_attn_combine(DecodeAttnArgs a) {
-  const int bh = blockIdx.x, d = threadIdx.x;
-  if (d >= a.hd) return;
-  const int stride = a.hd + 2;
-  const float *pp = a.part + (size_t)bh * a.nsplit * stride;
-  float M = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, pp[(size_t)s * stride]);
-  float L = 0.0f, acc = 0.0f;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float ms = pp[(size_t)s * stride];
-    const float sc = (ms == -INFINITY) ? 0.0f : exp2_fast(ms - M);
-    L += pp[(size_t)s * stride + 1] * sc;
-    acc += pp[(size_t)s * stride + 2 + d] * sc;
-  }
-  reinterpret_cast<T *>(a.o)[(size_t)bh * a.hd + d] = from_f32<T>(acc / L);
-}
-
 // Keys per split: a multiple of the 32-key block, at most DSPLIT, and small
 // enough that the grid has about kDecodeTargetWG workgroups (a short sliding
 // window over few heads would otherwise leave most of the chip idle).  From
@@ -646,8 +628,7 @@ size_t decode_attn_part_bytes(int B, int H, int G, int hd, int m, int max_real, 
 }
 
 template <class T>
-hipError_t launch_decode_attention(const DecodeAttnArgs &a, hipStream_t s, bool defer_combine,
-                                   bool *o_ready) {
+hipError_t launch_decode_attention(const DecodeAttnArgs &a, hipStream_t s, bool *o_ready) {
   const int hpg = a.H / a.G;
   dim3 grid(a.nsplit, a.G, a.B);
   // the DMA kernel writes O itself when there is a single split; the others
@@ -689,13 +670,11 @@ hipError_t launch_decode_attention(const DecodeAttnArgs &a, hipStream_t s, bool 
       default: return hipErrorInvalidValue;
     }
   }
-  if (!direct && !defer_combine)
-    hipLaunchKernelGGL(decode_attn_combine<T>, dim3(a.B * a.H), dim3(64), 0, s, a);
-  if (o_ready) *o_ready = direct || !defer_combine;
+  if (o_ready) *o_ready = direct;
   return hipGetLastError();
 }
-template hipError_t launch_decode_attention<float>(const DecodeAttnArgs &, hipStream_t, bool, bool *);
-template hipError_t launch_decode_attention<bf16>(const DecodeAttnArgs &, hipStream_t, bool, bool *);
+template hipError_t launch_decode_attention<float>(const DecodeAttnArgs &, hipStream_t, bool *);
+template hipError_t launch_decode_attention<bf16>(const DecodeAttnArgs &, hipStream_t, bool *);
 
 // ---------------------------------------------------------------------------
 // one SSM step: four lanes per (sequence, channel), four states each, so the

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -46,25 +47,49 @@ struct Timing {
 };
 thread_local Timing g_timing;
 
-// Brackets one stage's launches with events when timing is enabled.
+// Test aid: with HH_FAULT_INJECT set to a stage's name, that stage reports a
+// failed launch without launching anything (a host-side stand-in for a launch
+// error: the error path runs, no kernel is enqueued, nothing faults).
+thread_local const char *g_injected_stage = nullptr;
+bool fault_injected(const char *stage) {
+  const char *v = std::getenv("HH_FAULT_INJECT");
+  return v && std::strcmp(v, stage) == 0;
+}
+
+// Brackets one stage's launches with events when timing is enabled; run()
+// performs the launches unless a fault is injected for this stage.
 struct Stage {
   hipStream_t st;
+  const char *name;
   TimingRec rec{nullptr, nullptr, nullptr};
-  Stage(hipStream_t s, const char *name) : st(s) {
+  template <class F>
+  hipError_t run(F &&launch) {
+    if (fault_injected(name)) {
+      g_injected_stage = name;
+      return hipErrorLaunchFailure;
+    }
+    return launch();
+  }
+  Stage(hipStream_t s, const char *nm) : st(s), name(nm) {
     if (!g_timing.on) return;
     rec.stage = name;
     rec.start = g_timing.get();
     rec.stop = g_timing.get();
-    if (rec.start) hipEventRecord(rec.start, st);
+    if (rec.start) (void)hipEventRecord(rec.start, st);
   }
   ~Stage() {
     if (!rec.stage || !rec.start || !rec.stop) return;
-    hipEventRecord(rec.stop, st);
+    (void)hipEventRecord(rec.stop, st);
     g_timing.recs.push_back(rec);
   }
 };
 
 hh_status hip_fail(hipError_t e, const char *where) {
+  if (g_injected_stage) {
+    const char *stage = g_injected_stage;
+    g_injected_stage = nullptr;
+    return fail(HH_ERR_HIP, "%s: launch failure injected at stage '%s' (HH_FAULT_INJECT)", where, stage);
+  }
   return fail(HH_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
 }
 
@@ -101,6 +126,17 @@ hh_status check_dims(const hh_dims *dm, int kv_producer, Shape &s) {
   if (dm->dtype == HH_BF16 && (dm->d_model % 64 || (dm->n_heads * dm->head_dim + dm->d_inner) % 64))
     return fail(HH_ERR_UNSUPPORTED, "bf16 path needs d_model and n_heads*head_dim + d_inner "
                                     "to be multiples of 64");
+  // the row kernels hold a row in at most 2048 vector chunks per workgroup
+  // (the decode norm's split merge, the block's pre-norms): 16384 values in
+  // bf16, 8192 in fp32
+  {
+    const long widest = std::max<long>(std::max<long>(dm->d_model, (long)dm->n_heads * dm->head_dim),
+                                       dm->d_inner);
+    const long limit = dm->dtype == HH_BF16 ? 16384 : 8192;
+    if (widest > limit)
+      return fail(HH_ERR_UNSUPPORTED, "d_model, n_heads*head_dim and d_inner must be at most %ld for this "
+                  "dtype (widest is %ld)", limit, widest);
+  }
   if (!(dm->rms_eps >= 0.0f) || dm->rms_eps > 1.0f)
     return fail(HH_ERR_INVALID_ARG, "rms_eps must be in [0, 1]");
   if (!(dm->rope_base == 0.0f || (dm->rope_base > 1.0f && dm->rope_base < 1e30f)))
@@ -216,8 +252,10 @@ hh_status run_inproj(const Shape &s, const hh_weights *w, const void *x, int M,
                      const hh::InProjOut &e, float *part, hipStream_t st) {
   Stage sg(st, e.mode == hh::EPI_DECODE ? "decode_inproj"
               : e.mode == hh::EPI_META ? "meta_inproj" : "inproj");
-  hipError_t err = hh::launch_inproj<T>(static_cast<const T *>(x), M, s.d,
-                                        static_cast<const T *>(w->w_in), s.n_in, e, part, st);
+  hipError_t err = sg.run([&] {
+    return hh::launch_inproj<T>(static_cast<const T *>(x), M, s.d, static_cast<const T *>(w->w_in), s.n_in, e,
+                                part, st);
+  });
   return err == hipSuccess ? HH_OK : hip_fail(err, "input projection");
 }
 
@@ -255,7 +293,7 @@ hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, i
   hipError_t err;
   {
     Stage sg(st, "attention");
-    err = hh::launch_attention<T>(aa, st);
+    err = sg.run([&] { return hh::launch_attention<T>(aa, st); });
   }
   if (err != hipSuccess) return hip_fail(err, "attention");
 
@@ -270,7 +308,7 @@ hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, i
   sa.B = B; sa.n = n; sa.D = s.D; sa.N = s.N; sa.k = s.k; sa.S = s.S; sa.chunk = L.chunk;
   {
     Stage sg(st, "scan");
-    err = hh::launch_scan<T>(sa, st);
+    err = sg.run([&] { return hh::launch_scan<T>(sa, st); });
   }
   if (err != hipSuccess) return hip_fail(err, "selective scan");
 
@@ -283,15 +321,17 @@ hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, i
   }
   {
     Stage sg(st, "norm");
-    err = hh::launch_norm_fuse<T>(na, st);
+    err = sg.run([&] { return hh::launch_norm_fuse<T>(na, st); });
   }
   if (err != hipSuccess) return hip_fail(err, "norm/average");
 
   {
     Stage sg(st, "outproj");
-    err = hh::launch_outproj<T>(static_cast<const T *>(na.f), rows, s.Wa + s.D,
-                                static_cast<const T *>(w->w_out), s.d, static_cast<T *>(out),
-                                static_cast<const T *>(resid), part_ptr(ws, L.off[HH_WS_GEMM]), st);
+    err = sg.run([&] {
+      return hh::launch_outproj<T>(static_cast<const T *>(na.f), rows, s.Wa + s.D,
+                                   static_cast<const T *>(w->w_out), s.d, static_cast<T *>(out),
+                                   static_cast<const T *>(resid), part_ptr(ws, L.off[HH_WS_GEMM]), st);
+    });
   }
   if (err != hipSuccess) return hip_fail(err, "output projection");
 
@@ -320,7 +360,8 @@ hh_status meta_prefix_t(const Shape &s, const hh_weights *w, const void *R, void
   sa.h_out = h0; sa.tail_out = tail;
   sa.carry = reinterpret_cast<float *>(at(ws, L.off[HH_WS_SCAN]));
   sa.B = 1; sa.n = s.m; sa.D = s.D; sa.N = s.N; sa.k = s.k; sa.S = s.S; sa.chunk = L.chunk;
-  hipError_t err = hh::launch_scan<T>(sa, st);
+  Stage sg(st, "meta_scan");
+  hipError_t err = sg.run([&] { return hh::launch_scan<T>(sa, st); });
   return err == hipSuccess ? HH_OK : hip_fail(err, "meta scan");
 }
 
@@ -361,12 +402,12 @@ hh_status decode_t(const Shape &s, const hh_weights *w, const void *x, int B, co
   bool o_ready = false;
   {
     Stage sg(st, is_global ? "decode_attention_global" : "decode_attention_swa");
-    err = hh::launch_decode_attention<T>(da, st, /*defer_combine=*/true, &o_ready);
+    err = sg.run([&] { return hh::launch_decode_attention<T>(da, st, &o_ready); });
   }
   if (err != hipSuccess) return hip_fail(err, "decode attention");
   {
     Stage sg(st, "decode_ssm");
-    err = hh::launch_decode_ssm<T>(sa, st);
+    err = sg.run([&] { return hh::launch_decode_ssm<T>(sa, st); });
   }
   if (err != hipSuccess) return hip_fail(err, "decode SSM step");
 
@@ -382,15 +423,17 @@ hh_status decode_t(const Shape &s, const hh_weights *w, const void *x, int B, co
   }
   {
     Stage sg(st, "decode_norm");
-    err = hh::launch_norm_fuse<T>(na, st);
+    err = sg.run([&] { return hh::launch_norm_fuse<T>(na, st); });
   }
   if (err != hipSuccess) return hip_fail(err, "decode norm/average");
 
   {
     Stage sg(st, "decode_outproj");
-    err = hh::launch_outproj<T>(static_cast<const T *>(na.f), B, s.Wa + s.D,
-                                static_cast<const T *>(w->w_out), s.d, static_cast<T *>(out),
-                                static_cast<const T *>(resid), part_ptr(ws, L.gemm), st);
+    err = sg.run([&] {
+      return hh::launch_outproj<T>(static_cast<const T *>(na.f), B, s.Wa + s.D,
+                                   static_cast<const T *>(w->w_out), s.d, static_cast<T *>(out),
+                                   static_cast<const T *>(resid), part_ptr(ws, L.gemm), st);
+    });
   }
   if (err != hipSuccess) return hip_fail(err, "decode output projection");
   return HH_OK;
@@ -432,6 +475,10 @@ hh_status check_prefill_call(const hh_dims *dims, const hh_weights *w, const voi
       if (kv->is_ring && is_global) return fail(HH_ERR_INVALID_ARG, "a global layer needs a linear cache");
       if (kv->is_ring && window > kv->cap)
         return fail(HH_ERR_INVALID_ARG, "ring cache cap %d below window %d", kv->cap, window);
+      // a linear cache must hold every prompt position: the prompt's length
+      // becomes len, and decode appends at slot len
+      if (!kv->is_ring && kv->cap < seqlen)
+        return fail(HH_ERR_INVALID_ARG, "linear cache cap %d below seqlen %d", kv->cap, seqlen);
     }
   }
   return HH_OK;
@@ -512,19 +559,23 @@ hh_status block_mlp_t(const Shape &s, const hh_block_weights *w, int rows, void 
   hipError_t err;
   {
     Stage sg(st, "block_norm2");
-    err = hh::launch_rmsnorm<T>(x1, w->norm2, n2, rows, s.d, s.eps, st);
+    err = sg.run([&] { return hh::launch_rmsnorm<T>(x1, w->norm2, n2, rows, s.d, s.eps, st); });
   }
   if (err != hipSuccess) return hip_fail(err, "block pre-norm 2");
   {
     Stage sg(st, "mlp_gate_up");
-    err = hh::launch_mlp_gate_up<T>(n2, rows, s.d, static_cast<const T *>(w->w_gate_up),
-                                    2 * w->d_ff, h, part, st);
+    err = sg.run([&] {
+      return hh::launch_mlp_gate_up<T>(n2, rows, s.d, static_cast<const T *>(w->w_gate_up), 2 * w->d_ff, h,
+                                       part, st);
+    });
   }
   if (err != hipSuccess) return hip_fail(err, "MLP gate/up projection");
   {
     Stage sg(st, "mlp_down");
-    err = hh::launch_outproj<T>(h, rows, w->d_ff, static_cast<const T *>(w->w_down), s.d,
-                                static_cast<T *>(out), x1, part, st);
+    err = sg.run([&] {
+      return hh::launch_outproj<T>(h, rows, w->d_ff, static_cast<const T *>(w->w_down), s.d,
+                                   static_cast<T *>(out), x1, part, st);
+    });
   }
   return err == hipSuccess ? HH_OK : hip_fail(err, "MLP down projection");
 }
@@ -533,8 +584,10 @@ template <class T>
 hh_status block_norm1_t(const Shape &s, const hh_block_weights *w, const void *x, int rows, void *dst,
                         hipStream_t st) {
   Stage sg(st, "block_norm1");
-  hipError_t err = hh::launch_rmsnorm<T>(static_cast<const T *>(x), w->norm1, static_cast<T *>(dst), rows,
-                                         s.d, s.eps, st);
+  hipError_t err = sg.run([&] {
+    return hh::launch_rmsnorm<T>(static_cast<const T *>(x), w->norm1, static_cast<T *>(dst), rows, s.d, s.eps,
+                                 st);
+  });
   return err == hipSuccess ? HH_OK : hip_fail(err, "block pre-norm 1");
 }
 

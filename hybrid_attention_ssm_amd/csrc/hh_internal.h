@@ -472,12 +472,11 @@ struct DecodeAttnArgs {
 };
 // Per-split partials sit at part[((b*H + h)*nsplit + s)*(hd + 2)]: the running
 // maximum m of the base-2 scaled scores, l = sum 2^(score - m), then
-// a[hd] = sum 2^(score - m) v.  With defer_combine the merge of several splits
-// is left to the caller (the decode norm does it); *o_ready says whether o
-// holds the finished output.
+// a[hd] = sum 2^(score - m) v.  The merge of several splits is left to the
+// caller (the decode norm does it); *o_ready says whether o holds the
+// finished output (one split, written directly).
 template <class T>
-hipError_t launch_decode_attention(const DecodeAttnArgs &a, hipStream_t s, bool defer_combine,
-                                   bool *o_ready);
+hipError_t launch_decode_attention(const DecodeAttnArgs &a, hipStream_t s, bool *o_ready);
 size_t decode_attn_part_bytes(int B, int H, int G, int hd, int m, int max_real,
                               int *split_out, int *nsplit_out);
 

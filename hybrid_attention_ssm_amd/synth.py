@@ -14,6 +14,12 @@ draws in this fixed order):
   6. conv_w [D, k]             ~ N(0, 1/k);  conv_b = 0
   7. W_out  [d, H*hd + D]      ~ N(0, 1/(H*hd + D))
   8. beta_attn = beta_ssm = 1
+With `varied` (the parity tests' recipe, so that the per-channel weights are
+exercised; the benchmark workloads keep 6 and 8 as above), the layer draws
+after step 7:
+ 12. conv_b    [D]             ~ 0.1 N(0, 1)
+ 13. beta_attn [H*hd]          ~ U[0.5, 2]
+ 14. beta_ssm  [D]             ~ U[0.5, 2]
 A block (pre-norm, layer, residual, pre-norm, MLP, residual) draws its layer
 (3-8), then:
   9. g1, g2 [d]                ~ 1 + 0.1 N(0, 1)    (RMSNorm gains, fp32)
@@ -28,7 +34,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .configs import DecodeWorkload, LayerDims, PrefillWorkload
+from .configs import DecodeWorkload, LayerDims, PrefillWorkload, StackWorkload
 
 
 def round_bf16(a) -> np.ndarray:
@@ -51,8 +57,9 @@ def _normal(rng, shape, std=1.0) -> np.ndarray:
     return out
 
 
-def layer_weights(rng, dims: LayerDims, kv_producer: bool = True) -> dict:
-    """Draw one layer's parameters (steps 3-8 of the recipe)."""
+def layer_weights(rng, dims: LayerDims, kv_producer: bool = True, varied: bool = False) -> dict:
+    """Draw one layer's parameters (steps 3-8 of the recipe; with `varied`,
+    steps 12-14 replace the constant conv bias and betas)."""
     d, D, N, k = dims.d_model, dims.d_inner, dims.d_state, dims.d_conv
     Wa, kv = dims.attn_width, dims.n_kv_heads * dims.head_dim
     w_in = _store(dims, _normal(rng, (dims.n_in(True), d), (1.0 / d) ** 0.5))
@@ -66,15 +73,20 @@ def layer_weights(rng, dims: LayerDims, kv_producer: bool = True) -> dict:
     conv_w = _store(dims, _normal(rng, (D, k), (1.0 / k) ** 0.5))
     conv_b = np.zeros(D, np.float32)
     w_out = _store(dims, _normal(rng, (d, Wa + D), (1.0 / (Wa + D)) ** 0.5))
+    beta_attn, beta_ssm = np.ones(Wa, np.float32), np.ones(D, np.float32)
+    if varied:
+        conv_b = _normal(rng, (D,), 0.1)
+        beta_attn = rng.uniform(0.5, 2.0, size=Wa).astype(np.float32)
+        beta_ssm = rng.uniform(0.5, 2.0, size=D).astype(np.float32)
     return dict(w_in=w_in, dt_bias=dt_bias, A=A, conv_w=conv_w, conv_b=conv_b,
-                beta_attn=np.ones(Wa, np.float32), beta_ssm=np.ones(D, np.float32),
-                w_out=w_out, kv_producer=bool(kv_producer))
+                beta_attn=beta_attn, beta_ssm=beta_ssm, w_out=w_out, kv_producer=bool(kv_producer))
 
 
-def block_weights(rng, dims: LayerDims, d_ff: int, kv_producer: bool = True) -> dict:
+def block_weights(rng, dims: LayerDims, d_ff: int, kv_producer: bool = True,
+                  varied: bool = False) -> dict:
     """Draw one block's parameters: its layer, then steps 9-11 of the recipe."""
     d = dims.d_model
-    mixer = layer_weights(rng, dims, kv_producer)
+    mixer = layer_weights(rng, dims, kv_producer, varied)
     g1 = (1.0 + 0.1 * _normal(rng, (d,))).astype(np.float32)
     g2 = (1.0 + 0.1 * _normal(rng, (d,))).astype(np.float32)
     w_gu = _store(dims, _normal(rng, (2 * d_ff, d), (1.0 / d) ** 0.5))
@@ -82,26 +94,28 @@ def block_weights(rng, dims: LayerDims, d_ff: int, kv_producer: bool = True) -> 
     return dict(mixer=mixer, norm1=g1, norm2=g2, w_gate_up=w_gu, w_down=w_down, d_ff=int(d_ff))
 
 
-def block_inputs(w: PrefillWorkload, d_ff: int, kv_producer: bool = True, seed=None) -> dict:
+def block_inputs(w: PrefillWorkload, d_ff: int, kv_producer: bool = True, seed=None,
+                 varied: bool = False) -> dict:
     """x, meta tokens R and one block's weights for a prefill workload."""
     dims = w.dims
     rng = np.random.default_rng(w.seed if seed is None else seed)
     x = _store(dims, _normal(rng, (w.batch, w.seqlen, dims.d_model)))
     R = _store(dims, _normal(rng, (dims.n_meta, dims.d_model)))
-    return dict(x=x, R=R, weights=block_weights(rng, dims, d_ff, kv_producer))
+    return dict(x=x, R=R, weights=block_weights(rng, dims, d_ff, kv_producer, varied))
 
 
-def prefill_inputs(w: PrefillWorkload, kv_producer: bool = True, seed=None) -> dict:
+def prefill_inputs(w: PrefillWorkload, kv_producer: bool = True, seed=None,
+                   varied: bool = False) -> dict:
     """x, meta tokens R and the layer weights for a prefill workload."""
     dims = w.dims
     rng = np.random.default_rng(w.seed if seed is None else seed)
     x = _store(dims, _normal(rng, (w.batch, w.seqlen, dims.d_model)))
     R = _store(dims, _normal(rng, (dims.n_meta, dims.d_model)))
-    weights = layer_weights(rng, dims, kv_producer)
+    weights = layer_weights(rng, dims, kv_producer, varied)
     return dict(x=x, R=R, weights=weights)
 
 
-def decode_inputs(w: DecodeWorkload, seed=None) -> dict:
+def decode_inputs(w: DecodeWorkload, seed=None, varied: bool = False) -> dict:
     """Weights, caches, SSM states and new tokens for a decode workload.
 
     Draw order: per layer (in layer order) its weights; then per cache (sorted
@@ -115,7 +129,7 @@ def decode_inputs(w: DecodeWorkload, seed=None) -> dict:
     B, D, N, k = w.batch, dims.d_inner, dims.d_state, dims.d_conv
     layers = []
     for spec in w.layers:
-        layers.append(dict(spec=spec, weights=layer_weights(rng, dims, spec.kv_producer)))
+        layers.append(dict(spec=spec, weights=layer_weights(rng, dims, spec.kv_producer, varied)))
     caches = {}
     for name in sorted({s.cache for s in w.layers}):
         is_ring = name != "global"
@@ -131,3 +145,38 @@ def decode_inputs(w: DecodeWorkload, seed=None) -> dict:
         lay["conv"] = _store(dims, _normal(rng, (B, k - 1, D)))
         lay["x_t"] = _store(dims, _normal(rng, (B, dims.d_model)))
     return dict(layers=layers, caches=caches)
+
+
+def stack_inputs(w: StackWorkload, steps: int, varied: bool = False, seed=None) -> dict:
+    """Weights, caches, SSM states and stack inputs for decode steps through a
+    stack of blocks (w.layer_plan()).
+
+    Draw order: per block (in order) its weights (block recipe); then per cache
+    (in order of first use) meta K, meta V, cache K, cache V; then per block h
+    [B, D, N] (fp32) and its conv history [B, k-1, D]; then the stack input of
+    each step x [steps, B, d]; all N(0, 1).  Every sequence holds `context`
+    real positions before the first step.
+    """
+    dims = w.dims
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    G, m, hd = dims.n_kv_heads, dims.n_meta, dims.head_dim
+    B, D, N, k = w.batch, dims.d_inner, dims.d_state, dims.d_conv
+    plan = w.layer_plan()
+    blocks = [dict(is_global=g, kv_producer=p, cache=c,
+                   weights=block_weights(rng, dims, w.d_ff, p, varied)) for g, p, c in plan]
+    caches = {}
+    for g, _, name in plan:
+        if name in caches:
+            continue
+        cap = w.global_cap if g else w.window
+        caches[name] = dict(
+            meta_k=_store(dims, _normal(rng, (G, m, hd))),
+            meta_v=_store(dims, _normal(rng, (G, m, hd))),
+            k=_store(dims, _normal(rng, (B, G, cap, hd))),
+            v=_store(dims, _normal(rng, (B, G, cap, hd))),
+            len=np.full(B, w.context, np.int32), cap=cap, is_ring=not g)
+    for blk in blocks:
+        blk["h"] = _normal(rng, (B, D, N))
+        blk["conv"] = _store(dims, _normal(rng, (B, k - 1, D)))
+    x = _store(dims, _normal(rng, (steps, B, dims.d_model)))
+    return dict(blocks=blocks, caches=caches, x=x)

@@ -10,7 +10,10 @@
  * are validated on the host BEFORE anything is enqueued, so on an error no
  * buffer has been touched; hh_last_error() then holds a message (per thread).
  * HH_ERR_HIP reports a failed kernel launch; output buffers may then be
- * partially written.
+ * partially written, except when the first stage of a call fails (nothing has
+ * been enqueued yet).  For tests, the environment variable HH_FAULT_INJECT set
+ * to a stage name (e.g. "inproj", "scan", "decode_inproj", "decode_norm")
+ * makes that stage report a failed launch on the host without launching.
  *
  * What the layer computes (the method of "Hymba: A Hybrid-head Architecture
  * for Small Language Models", arXiv 2411.13676, and the authors' OpenReview
@@ -44,7 +47,9 @@
  * Supported shapes: head_dim 32 or 64 (bf16: 64); n_heads a multiple of
  * n_kv_heads with at most 8 query heads per KV head; d_state 16; d_conv 2..4;
  * d_model, n_heads*head_dim + d_inner and d_inner multiples of 8 (bf16: d_model
- * and n_heads*head_dim + d_inner multiples of 64).
+ * and n_heads*head_dim + d_inner multiples of 64); d_model, n_heads*head_dim
+ * and d_inner at most 16384 (bf16) or 8192 (fp32).  Every one of these limits
+ * is checked before any launch (HH_ERR_UNSUPPORTED).
  */
 #ifndef HH_H
 #define HH_H
@@ -144,9 +149,14 @@ typedef struct {
  *                   it to seqlen (NULL skips).  Decode: a producer appends at
  *                   position len[b] and then increments len[b]; a consumer
  *                   attends up to position len[b]-1 (the token its producer
- *                   appended this step) and writes nothing.  A producer's
- *                   decode on a linear cache with len[b] >= cap writes no slot
- *                   and leaves len[b] unchanged for that sequence.
+ *                   appended this step) and writes nothing.
+ *                   Prefill into a linear cache needs cap >= seqlen
+ *                   (HH_ERR_INVALID_ARG otherwise).  Decoding a sequence whose
+ *                   linear cache is full (len[b] >= cap) is a caller error:
+ *                   len lives on the device, so it is not checked before the
+ *                   launch; the kernels then write no slot and leave len[b]
+ *                   unchanged (the sequence's output for that step does not
+ *                   include the new token).
  *   cap, is_ring    slots per sequence and head; ring caches need window <= cap. */
 typedef struct {
   void *full_k, *full_v;

@@ -155,3 +155,70 @@ def test_block_validation():
     d = hb.hh_dims(TINY)
     need = hb.lib().hh_block_prefill_workspace_size(ctypes.byref(d), 96, 1, 64, 1)
     assert _call_block_prefill(TINY, _block_weights(), ws_bytes=need - 1) == 3
+
+
+def test_linear_cache_shorter_than_prompt_rejected():
+    """A producer's prefill into a linear cache must fit every prompt
+    position (its length becomes len, where decode appends)."""
+    kv = hb.HHKV(None, None, FAKE, FAKE, FAKE, 32, 0)           # linear, cap 32
+    assert _call_prefill(TINY, n=64, kv=kv) == 1
+    assert "linear cache" in hb.hh_last_error()
+    kv = hb.HHKV(None, None, FAKE, FAKE, FAKE, 64, 0)           # cap == seqlen: accepted
+    assert _call_prefill(TINY, n=64, kv=kv, ws_bytes=1) == 3    # (fails later, on the workspace)
+
+
+@pytest.mark.parametrize("dims,status", [
+    (replace(TINY, d_inner=8200), 2),                              # fp32 rows above 8192
+    (replace(TINY, d_model=8200), 2),
+    (replace(HYMBA_1P5B, d_inner=16448), 2),                       # bf16 rows above 16384
+    (replace(TINY, d_inner=8192), 3)])                             # at the limit: accepted
+def test_row_width_limits_checked_before_launch(dims, status):
+    """The row kernels' width limits (decode norm merge, block pre-norms) are
+    validated up front, so no call can fail after it has started updating
+    the caller's state."""
+    assert _call_prefill(dims, ws_bytes=1) == status
+    if status == 2:
+        assert "at most" in hb.hh_last_error()
+    d = hb.hh_dims(dims)
+    w = _weights()
+    meta = hb.HHMeta(FAKE, FAKE, FAKE, FAKE)
+    st = hb.HHSsmState(FAKE, FAKE)
+    kv = hb.HHKV(None, None, FAKE, FAKE, FAKE, 16, 1)
+    r = hb.lib().hh_decode_step(ctypes.byref(d), ctypes.byref(w), FAKE, 4, ctypes.byref(meta),
+                                16, 0, ctypes.byref(kv), ctypes.byref(st), FAKE, FAKE, 1, None)
+    assert r == status
+
+
+def _call_decode(dims, B=4, ws_bytes=1 << 40):
+    d = hb.hh_dims(dims)
+    w = _weights()
+    meta = hb.HHMeta(FAKE, FAKE, FAKE, FAKE)
+    st = hb.HHSsmState(FAKE, FAKE)
+    kv = hb.HHKV(None, None, FAKE, FAKE, FAKE, 16, 1)
+    return hb.lib().hh_decode_step(ctypes.byref(d), ctypes.byref(w), FAKE, B, ctypes.byref(meta),
+                                   16, 0, ctypes.byref(kv), ctypes.byref(st), FAKE, FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("entry,stage", [("prefill", "inproj"), ("decode", "decode_inproj"),
+                                         ("meta_prefix", "meta_inproj"), ("block_prefill", "block_norm1")])
+def test_injected_launch_failure_surfaces_as_hip_error(entry, stage, monkeypatch):
+    """HH_FAULT_INJECT=<stage> makes that stage's launch fail on the host,
+    before anything is enqueued: the call returns HH_ERR_HIP naming the stage
+    (here the first stage of each entry point, so no HIP call is made and the
+    fake device pointers are never touched)."""
+    monkeypatch.setenv("HH_FAULT_INJECT", stage)
+    if entry == "prefill":
+        r = _call_prefill(TINY)
+    elif entry == "decode":
+        r = _call_decode(TINY)
+    elif entry == "meta_prefix":
+        d, w = hb.hh_dims(TINY), _weights()
+        r = hb.lib().hh_meta_prefix(ctypes.byref(d), ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    FAKE, 1 << 40, None)
+    else:
+        r = _call_block_prefill(TINY, _block_weights())
+    assert r == 4, r
+    msg = hb.hh_last_error()
+    assert "injected" in msg and stage in msg, msg
+    # validation still comes first: a bad argument is reported as such
+    assert _call_prefill(TINY, n=0) == 1

@@ -85,7 +85,7 @@ def _assert_block(got_out, want_out, x, tol, label, dtype):
 ])
 def test_block_prefill_matches_oracle(dims, d_ff, B, n, window, is_global):
     print(f"case block {dims.dtype} d_ff={d_ff} B={B} n={n} W={window} global={is_global}", flush=True)
-    inp = block_inputs(PrefillWorkload("blk", 50, dims, B, n, window, is_global), d_ff)
+    inp = block_inputs(PrefillWorkload("blk", 50, dims, B, n, window, is_global), d_ff, varied=True)
     want = ref.block_prefill(dims.as_dict(), inp["weights"], inp["R"], inp["x"], window, is_global)
     stored = ref.block_prefill(dims.as_dict(), inp["weights"], inp["R"], inp["x"], window, is_global,
                                store=_store(dims))
@@ -110,7 +110,8 @@ def test_block_decode_matches_longer_prefill(dims, d_ff, n0, steps, window, is_g
     print(f"case block decode {dims.dtype} n0={n0} steps={steps} W={window} global={is_global} "
           f"cap={cap}", flush=True)
     B = 2
-    inp = block_inputs(PrefillWorkload("bd", n0 + steps, dims, B, n0 + steps, window, is_global), d_ff)
+    inp = block_inputs(PrefillWorkload("bd", n0 + steps, dims, B, n0 + steps, window, is_global), d_ff,
+                       varied=True)
     x = inp["x"]
     want = ref.block_prefill(dims.as_dict(), inp["weights"], inp["R"], x, window, is_global)
     stored = ref.block_prefill(dims.as_dict(), inp["weights"], inp["R"], x, window, is_global,
@@ -140,7 +141,8 @@ def test_block_full_width_prefill_and_decode():
     dims, d_ff = HYMBA_1P5B, MLP_HIDDEN_1P5B
     n, window, steps = 1024, 1024, 2
     print(f"case block full width n={n} d_ff={d_ff}", flush=True)
-    inp = block_inputs(PrefillWorkload("bfw", n + steps, dims, 1, n + steps, window, False), d_ff, seed=7)
+    inp = block_inputs(PrefillWorkload("bfw", n + steps, dims, 1, n + steps, window, False), d_ff, seed=7,
+                       varied=True)
     x = inp["x"]
     want = ref.block_prefill(dims.as_dict(), inp["weights"], inp["R"], x, window, False,
                              cache=dict(k=np.zeros((1, dims.n_kv_heads, window, dims.head_dim)),

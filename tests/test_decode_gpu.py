@@ -17,7 +17,8 @@ from hybrid_attention_ssm_amd import binding as hb
 from hybrid_attention_ssm_amd.configs import TINY, LayerDims, PrefillWorkload
 from hybrid_attention_ssm_amd.synth import prefill_inputs
 from oracle import hymba_ref as ref
-from tests.harness import TOL, np_of, rel_err, run_prefill
+from tests.harness import (TOL, assert_written, check_guards, guarded, np_of, poisoned_workspace,
+                           rel_err, run_prefill)
 
 pytestmark = pytest.mark.gpu
 
@@ -33,19 +34,24 @@ def _decode_steps(dims, got, x_new, window, is_global, cap, consumer=None):
     layer = got["layer"]
     kv = hb.make_kv(None, None, got["cache_k"], got["cache_v"], got["len"], cap, not is_global)
     meta = hb.make_meta(got["meta"]["k"], got["meta"]["v"], None, None)
+    ws = poisoned_workspace(hb.hh_decode_workspace_size(dims, B, cap, True))
     for s in range(k):
         xt = hb.to_device(x_new[:, s], sd)
-        out = torch.empty(B, d, dtype=sd, device="cuda")
-        hb.hh_decode_step(layer, xt, meta, window, is_global, kv, got["h"], got["conv"], out)
+        out = guarded((B, d), sd)
+        hb.hh_decode_step(layer, xt, meta, window, is_global, kv, got["h"], got["conv"], out, ws=ws)
         if consumer is not None:
             cl, ch, cc, cx = consumer
-            cout = torch.empty(B, d, dtype=sd, device="cuda")
-            hb.hh_decode_step(cl, hb.to_device(cx[:, s], sd), meta, window, is_global, kv, ch, cc, cout)
+            cout = guarded((B, d), sd)
+            hb.hh_decode_step(cl, hb.to_device(cx[:, s], sd), meta, window, is_global, kv, ch, cc, cout,
+                              ws=ws)
             torch.cuda.synchronize()
+            assert_written("consumer decode out", cout)
             outs.append((np_of(out), np_of(cout)))
         else:
             torch.cuda.synchronize()
             outs.append(np_of(out))
+        assert_written("decode out", out)
+    check_guards()
     return outs
 
 
@@ -57,7 +63,8 @@ def _decode_steps(dims, got, x_new, window, is_global, cap, consumer=None):
 ])
 def test_prefill_then_decode_matches_longer_prefill(dims, n0, steps, window, is_global, cap):
     B = 2
-    inp = prefill_inputs(PrefillWorkload("pd", n0 + steps, dims, B, n0 + steps, window, is_global))
+    inp = prefill_inputs(PrefillWorkload("pd", n0 + steps, dims, B, n0 + steps, window, is_global),
+                         varied=True)
     x = inp["x"]
     print(f"case {dims.dtype} n0={n0} steps={steps} W={window} global={is_global} cap={cap}", flush=True)
     z = np.zeros((B, dims.n_kv_heads, cap, dims.head_dim))
@@ -83,8 +90,8 @@ def test_consumer_decode_reads_producer_cache(dims):
     B, n0, steps, window = 2, 30, 6, 16
     cap = window
     wp = PrefillWorkload("p", 41, dims, B, n0 + steps, window, False)
-    ip = prefill_inputs(wp)
-    ic = prefill_inputs(replace(wp, seed=42), kv_producer=False)
+    ip = prefill_inputs(wp, varied=True)
+    ic = prefill_inputs(replace(wp, seed=42), kv_producer=False, varied=True)
     mp = ref.meta_prefix(dims.as_dict(), ip["weights"], ip["R"])
     mc = ref.meta_prefix(dims.as_dict(), ic["weights"], ip["R"])
     z = np.zeros((B, dims.n_kv_heads, cap, dims.head_dim))

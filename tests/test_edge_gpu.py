@@ -31,7 +31,7 @@ SMALL_BF16 = LayerDims(d_model=256, n_heads=8, n_kv_heads=2, head_dim=64, d_inne
 @pytest.mark.parametrize("is_global", [False, True], ids=["swa", "global"])
 def test_no_meta_tokens_prefill(dims, is_global):
     B, n, W = 2, 77, 20
-    inp = prefill_inputs(PrefillWorkload("nometa", 51, dims, B, n, W, is_global))
+    inp = prefill_inputs(PrefillWorkload("nometa", 51, dims, B, n, W, is_global), varied=True)
     assert inp["R"].shape[0] == 0
     cap = n if is_global else W
     want = ref.prefill(dims.as_dict(), inp["weights"], inp["R"], inp["x"], W, is_global,
@@ -56,7 +56,7 @@ def _ragged_decode(dims, lens, window, gcap, seed):
     w = DecodeWorkload("ragged", seed, dims, batch=B, context=0, window=window, global_cap=gcap,
                        layers=(DecodeLayer(False, True, "swa"), DecodeLayer(False, False, "swa"),
                                DecodeLayer(True, True, "global")))
-    inp = decode_inputs(w)
+    inp = decode_inputs(w, varied=True)
     for c in inp["caches"].values():
         c["len"] = np.array(lens, np.int32)
     sd = hb.storage_dtype(dims)
@@ -118,3 +118,62 @@ def test_ragged_lengths_decode(dims):
     lens = [1, 2, 15, 16, 17, 33, 45]
     print(f"ragged decode {dims.dtype} m={dims.n_meta}", flush=True)
     _ragged_decode(dims, lens, window=16, gcap=64, seed=61)
+
+
+@pytest.mark.parametrize("dims", [
+    # fp32 rows wider than 512 four-wide chunks and bf16 rows wider than 512
+    # eight-wide chunks, with at least 2048 rows: the norm kernel that keeps
+    # no row in registers
+    LayerDims(d_model=64, n_heads=2, n_kv_heads=1, head_dim=32, d_inner=2560, d_state=16, d_conv=4,
+              n_meta=4, dtype="f32"),
+    LayerDims(d_model=128, n_heads=2, n_kv_heads=1, head_dim=64, d_inner=4160, d_state=16, d_conv=4,
+              n_meta=4, dtype="bf16")], ids=["f32-D2560", "bf16-D4160"])
+def test_wide_ssm_branch_many_rows(dims):
+    n, W = 2048, 16
+    print(f"case wide SSM {dims.dtype} D={dims.d_inner} n={n}", flush=True)
+    inp = prefill_inputs(PrefillWorkload("wide", 52, dims, 1, n, W, False), varied=True)
+    want = ref.prefill(dims.as_dict(), inp["weights"], inp["R"], inp["x"], W, False)
+    got = run_prefill(dims, inp["weights"], inp["R"], inp["x"], W, False)
+    tol = TOL[dims.dtype]
+    e_out, e_h = rel_err(np_of(got["out"]), want["out"]), rel_err(np_of(got["h"]), want["h"])
+    print(f"  err out={e_out:.2e} h={e_h:.2e}", flush=True)
+    assert e_out <= tol and e_h <= tol
+
+
+def test_injected_launch_failure_leaves_state_untouched(monkeypatch):
+    """A launch failure of a decode step's first stage (injected on the host
+    with HH_FAULT_INJECT) returns HH_ERR_HIP before anything is enqueued: the
+    cache, its lengths, the SSM state and the output keep every bit.  An
+    injected failure at a later stage is reported the same way."""
+    dims = SMALL_BF16
+    w = DecodeWorkload("inject", 62, dims, batch=3, context=0, window=16, global_cap=64,
+                       layers=(DecodeLayer(False, True, "swa"),))
+    inp = decode_inputs(w, varied=True)
+    c = inp["caches"]["swa"]
+    c["len"] = np.array([3, 20, 40], np.int32)
+    sd = hb.storage_dtype(dims)
+    kk, vv = hb.to_device(c["k"], sd), hb.to_device(c["v"], sd)
+    ln = hb.to_device(c["len"], torch.int32)
+    mk, mv = hb.to_device(c["meta_k"], sd), hb.to_device(c["meta_v"], sd)
+    kv = hb.make_kv(None, None, kk, vv, ln, c["cap"], True)
+    meta = hb.make_meta(mk, mv, None, None)
+    lay = inp["layers"][0]
+    layer = hb.upload_weights(dims, lay["weights"])
+    h = hb.to_device(lay["h"], torch.float32)
+    cv = hb.to_device(lay["conv"], torch.float32)
+    out = torch.full((3, dims.d_model), 7.0, dtype=sd, device="cuda")
+    before = [t.clone() for t in (kk, vv, ln, h, cv, out)]
+    xt = hb.to_device(lay["x_t"], sd)
+    monkeypatch.setenv("HH_FAULT_INJECT", "decode_inproj")
+    with pytest.raises(hb.HHError) as ei:
+        hb.hh_decode_step(layer, xt, meta, w.window, False, kv, h, cv, out)
+    assert ei.value.status == 4 and "injected" in str(ei.value)
+    torch.cuda.synchronize()
+    for a, b in zip((kk, vv, ln, h, cv, out), before):
+        assert torch.equal(a, b)
+    monkeypatch.setenv("HH_FAULT_INJECT", "decode_norm")
+    with pytest.raises(hb.HHError) as ei:
+        hb.hh_decode_step(layer, xt, meta, w.window, False, kv, h, cv, out)
+    assert ei.value.status == 4 and "decode_norm" in str(ei.value)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("HH_FAULT_INJECT")

@@ -61,8 +61,8 @@ def test_mamba2_hymba_shapes():
 def test_consumer_prefill_with_mamba2_heads(dims):
     B, n, window = 2, 90, 20
     wp = PrefillWorkload("p", 71, dims, B, n, window, False)
-    ip = prefill_inputs(wp)
-    ic = prefill_inputs(replace(wp, seed=72), kv_producer=False)
+    ip = prefill_inputs(wp, varied=True)
+    ic = prefill_inputs(replace(wp, seed=72), kv_producer=False, varied=True)
     pr = ref.prefill(dims.as_dict(), ip["weights"], ip["R"], ip["x"], window, False)
     cr = ref.prefill(dims.as_dict(), ic["weights"], ip["R"], ic["x"], window, False,
                      shared_kv=(pr["K_all"], pr["V_all"]))
@@ -75,7 +75,7 @@ def test_consumer_prefill_with_mamba2_heads(dims):
 
 @pytest.mark.parametrize("dims", [TINY_M2, SMALL_M2])
 def test_meta_prefix_with_mamba2_heads(dims):
-    inp = prefill_inputs(PrefillWorkload("m", 13, dims, 1, 8, 4, False))
+    inp = prefill_inputs(PrefillWorkload("m", 13, dims, 1, 8, 4, False), varied=True)
     _, meta = run_meta_prefix(dims, inp["weights"], inp["R"])
     want = ref.meta_prefix(dims.as_dict(), inp["weights"], inp["R"])
     tol = TOL[dims.dtype]
@@ -89,7 +89,7 @@ def test_meta_prefix_with_mamba2_heads(dims):
     (SMALL_P32, 150, 6, 64, False, 64)])
 def test_decode_with_mamba2_heads(dims, n0, steps, window, is_global, cap):
     B = 2
-    inp = prefill_inputs(PrefillWorkload("pd", n0 + steps, dims, B, n0 + steps, window, is_global))
+    inp = prefill_inputs(PrefillWorkload("pd", n0 + steps, dims, B, n0 + steps, window, is_global), varied=True)
     x = inp["x"]
     print(f"case {dims.dtype} S={dims.ssm_heads} n0={n0} steps={steps} global={is_global}", flush=True)
     z = np.zeros((B, dims.n_kv_heads, cap, dims.head_dim))

@@ -116,6 +116,39 @@ BLOCK_MUTANTS = {
 }
 
 
+def _block_store_err():
+    from tests.test_oracle_pins import _block, block_by_library
+    from hybrid_attention_ssm_amd.configs import TINY
+    from hybrid_attention_ssm_amd.synth import round_bf16
+    x, R, bw = _block(TINY, 13, seed=37)
+    got = ref.block_prefill(TINY.as_dict(), bw, R, x, 6, False, store=round_bf16)
+    want = block_by_library(TINY, bw, R, x[0], 6, False, store=round_bf16)
+    return float(np.abs(got["out"][0] - want["out"]).max())
+
+
+STORE_MUTANTS = {
+    # the MLP's hidden units handed on unrounded
+    "MLP hidden not stored": ("mlp", lambda v, w_gu, w_down, store=None: _orig_mlp(v, w_gu, w_down)),
+    # the rounding applied to the hidden units twice over a wider type: the
+    # gate rounded before the product instead of the product
+    "MLP gate stored instead of the product": (
+        "mlp", lambda v, w_gu, w_down, store=None: (
+            np.asarray(store(ref.silu((np.asarray(v) @ w_gu.T)[..., 0::2])), dtype=np.float64)
+            * (np.asarray(v) @ w_gu.T)[..., 1::2]) @ w_down.T),
+}
+
+
+def test_unmutated_block_store_agrees():
+    assert _block_store_err() < 1e-9
+
+
+@pytest.mark.parametrize("name", sorted(STORE_MUTANTS))
+def test_block_store_pin_catches_mutant(name, monkeypatch):
+    attr, fn = STORE_MUTANTS[name]
+    monkeypatch.setattr(ref, attr, fn)
+    assert _block_store_err() > 1e-4, f"mutant '{name}' not caught"
+
+
 def test_unmutated_block_agrees():
     assert _block_err() < 1e-9
 

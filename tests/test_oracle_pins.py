@@ -416,18 +416,22 @@ def _block(dims: LayerDims, n, seed, d_ff=20, kv_producer=True, batch=1):
     return x, R, block_weights(rng, dims, d_ff, kv_producer)
 
 
-def block_by_library(dims: LayerDims, bw, R, xb, window, is_global):
+def block_by_library(dims: LayerDims, bw, R, xb, window, is_global, store=None):
     """x1 = x + layer(rms_norm(x; g1)); out = x1 + down(silu(gate) * up) of
     rms_norm(x1; g2), with torch's rms_norm, linear and silu; the gate/up rows
-    are taken from the even/odd rows of the stored matrix."""
+    are taken from the even/odd rows of the stored matrix.  store (optional):
+    the rounding a 16-bit path applies to what it hands from one kernel to the
+    next: the layer's inputs, the residual x1, the MLP's input and its hidden
+    units."""
     t = lambda a: torch.as_tensor(np.asarray(a, dtype=np.float64))
+    st = (lambda v: t(store(np.asarray(v, dtype=np.float32)))) if store else t
     d = dims.d_model
-    n1 = lambda v: TF.rms_norm(t(v), (d,), weight=t(bw["norm1"]), eps=dims.eps).numpy()
+    n1 = lambda v: st(TF.rms_norm(t(v), (d,), weight=t(bw["norm1"]), eps=dims.eps)).numpy()
     layer = layer_by_library(dims, bw["mixer"], n1(R), n1(xb), window, is_global)
-    x1 = t(xb) + t(layer["out"])
-    n2 = TF.rms_norm(x1, (d,), weight=t(bw["norm2"]), eps=dims.eps)
+    x1 = st(t(xb) + t(layer["out"]))
+    n2 = st(TF.rms_norm(x1, (d,), weight=t(bw["norm2"]), eps=dims.eps))
     w = t(bw["w_gate_up"])
-    hidden = TF.silu(TF.linear(n2, w[0::2])) * TF.linear(n2, w[1::2])
+    hidden = st(TF.silu(TF.linear(n2, w[0::2])) * TF.linear(n2, w[1::2]))
     return dict(out=(x1 + TF.linear(hidden, t(bw["w_down"]))).numpy(), x1=x1.numpy(), h=layer["h"])
 
 
@@ -439,6 +443,53 @@ def test_block_matches_library_composition(dims, n, window, is_global):
     np.testing.assert_allclose(got["out"][0], want["out"], rtol=1e-10, atol=1e-10)
     np.testing.assert_allclose(got["x1"][0], want["x1"], rtol=1e-10, atol=1e-10)
     np.testing.assert_allclose(got["h"][0], want["h"], rtol=1e-10, atol=1e-12)
+
+
+def _round_bf16(v):
+    from hybrid_attention_ssm_amd.synth import round_bf16
+    return round_bf16(v)
+
+
+@pytest.mark.parametrize("dims,n,window,is_global", [(TINY, 21, 8, False), (GQA, 17, 5, True)])
+def test_block_with_stored_operands_matches_library_composition(dims, n, window, is_global):
+    """The oracle's `store` hook: rounding at the layer inputs, the residual
+    after the layer, the MLP input and the MLP hidden units, against the torch
+    composition that rounds at the same four points."""
+    x, R, bw = _block(dims, n, seed=35)
+    got = ref.block_prefill(dims.as_dict(), bw, R, x, window, is_global, store=_round_bf16)
+    want = block_by_library(dims, bw, R, x[0], window, is_global, store=_round_bf16)
+    np.testing.assert_allclose(got["out"][0], want["out"], rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(got["x1"][0], want["x1"], rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(got["h"][0], want["h"], rtol=1e-10, atol=1e-12)
+    # the rounding is really applied: x1 holds bf16 values, and the result
+    # differs from the unrounded block by far more than the fp64 noise
+    assert np.array_equal(_round_bf16(got["x1"]).astype(np.float64), got["x1"])
+    exact = ref.block_prefill(dims.as_dict(), bw, R, x, window, is_global)
+    assert np.abs(exact["out"] - got["out"]).max() > 1e-4
+
+
+def test_block_decode_with_stored_operands_equals_longer_prefill():
+    """store applies per row, so prefill(n0) + decode steps with rounding at
+    the same points equals prefill(n0 + k) with it."""
+    dims = GQA
+    n0, steps, cap = 6, 4, 6
+    x, R, bw = _block(dims, n0 + steps, seed=36, batch=2)
+    B = x.shape[0]
+    zeros = np.zeros((B, dims.n_kv_heads, cap, dims.head_dim))
+    cache0 = dict(k=zeros, v=zeros, is_ring=True)
+    st = _round_bf16
+    full = ref.block_prefill(dims.as_dict(), bw, R, x, cap, False, cache=cache0, store=st)
+    pre = ref.block_prefill(dims.as_dict(), bw, R, x[:, :n0], cap, False, cache=cache0, store=st)
+    mp = ref.block_meta_prefix(dims.as_dict(), bw, R, store=st)
+    cache = dict(k=pre["cache_k"], v=pre["cache_v"], len=np.full(B, n0), is_ring=True)
+    h, conv = pre["h"], pre["conv_tail"]
+    for s_ in range(steps):
+        r = ref.block_decode_step(dims.as_dict(), bw, x[:, n0 + s_], mp["k"], mp["v"], cap,
+                                  False, cache, h, conv, store=st)
+        np.testing.assert_allclose(r["out"], full["out"][:, n0 + s_], rtol=1e-10, atol=1e-11)
+        cache = dict(k=r["cache_k"], v=r["cache_v"], len=r["len"], is_ring=True)
+        h, conv = r["h"], r["conv"]
+    np.testing.assert_allclose(h, full["h"], rtol=1e-10, atol=1e-12)
 
 
 def test_rms_norm_closed_form():

@@ -26,9 +26,12 @@ SMALL_BF16_G5 = LayerDims(d_model=320, n_heads=10, n_kv_heads=2, head_dim=64, d_
                           d_state=16, d_conv=4, n_meta=100, dtype="bf16")
 
 
-def _check_prefill(dims, B, n, window, is_global, seed, kv_producer=True, cache_cap=None):
+def _check_prefill(dims, B, n, window, is_global, seed, kv_producer=True, cache_cap=None,
+                   varied=True):
+    """varied: per-channel betas and a conv bias drawn (the recipe's steps
+    12-14); False keeps the workload recipe (betas 1, conv bias 0)."""
     w = PrefillWorkload("t", seed, dims, B, n, window, is_global)
-    inp = prefill_inputs(w)
+    inp = prefill_inputs(w, varied=varied)
     tol = TOL[dims.dtype]
     print(f"case dims={dims.dtype} d={dims.d_model} H={dims.n_heads} G={dims.n_kv_heads} "
           f"B={B} n={n} W={window} global={is_global} seed={seed}", flush=True)
@@ -56,7 +59,16 @@ def _check_prefill(dims, B, n, window, is_global, seed, kv_producer=True, cache_
 
 def test_cfg0_tiny_f32_swa():
     w = CFG0_TINY
-    _check_prefill(w.dims, w.batch, w.seqlen, w.window, w.is_global, w.seed, cache_cap=w.window)
+    _check_prefill(w.dims, w.batch, w.seqlen, w.window, w.is_global, w.seed, cache_cap=w.window,
+                   varied=False)
+
+
+def test_cfg0_tiny_f32_swa_varied_betas_and_conv_bias():
+    """The tiny workload with per-channel betas (Eq. 3's learnable scaling)
+    and a nonzero conv bias."""
+    w = CFG0_TINY
+    _check_prefill(w.dims, w.batch, w.seqlen, w.window, w.is_global, w.seed, cache_cap=w.window,
+                   varied=True)
 
 
 @pytest.mark.parametrize("B,n,window,is_global", [
@@ -89,8 +101,8 @@ def test_consumer_layer_reads_producer_kv(dims):
     """A KV-sharing consumer attends over its producer's K/V (and meta K/V)."""
     B, n, window = 2, 90, 20
     wp = PrefillWorkload("p", 31, dims, B, n, window, False)
-    inp_p = prefill_inputs(wp)
-    inp_c = prefill_inputs(replace(wp, seed=32), kv_producer=False)
+    inp_p = prefill_inputs(wp, varied=True)
+    inp_c = prefill_inputs(replace(wp, seed=32), kv_producer=False, varied=True)
     prod_ref = ref.prefill(dims.as_dict(), inp_p["weights"], inp_p["R"], inp_p["x"], window, False)
     x_c = inp_c["x"]
     cons_ref = ref.prefill(dims.as_dict(), inp_c["weights"], inp_p["R"], x_c, window, False,
@@ -106,7 +118,7 @@ def test_consumer_layer_reads_producer_kv(dims):
 
 def test_meta_prefix_matches_oracle():
     for dims, seed in ((TINY, 3), (SMALL_BF16, 4)):
-        inp = prefill_inputs(PrefillWorkload("m", seed, dims, 1, 8, 4, False))
+        inp = prefill_inputs(PrefillWorkload("m", seed, dims, 1, 8, 4, False), varied=True)
         from tests.harness import run_meta_prefix
         _, meta = run_meta_prefix(dims, inp["weights"], inp["R"])
         want = ref.meta_prefix(dims.as_dict(), inp["weights"], inp["R"])
@@ -120,7 +132,7 @@ def test_meta_prefix_matches_oracle():
 def test_deterministic_rerun():
     """Same inputs twice: bit-identical outputs (no races between workgroups)."""
     dims = SMALL_BF16
-    inp = prefill_inputs(PrefillWorkload("d", 9, dims, 1, 257, 64, False))
+    inp = prefill_inputs(PrefillWorkload("d", 9, dims, 1, 257, 64, False), varied=True)
     a = run_prefill(dims, inp["weights"], inp["R"], inp["x"], 64, False)
     b = run_prefill(dims, inp["weights"], inp["R"], inp["x"], 64, False)
     assert torch.equal(a["out"], b["out"]) and torch.equal(a["h"], b["h"])

@@ -59,8 +59,8 @@ def test_rope_changes_the_output():
 def test_consumer_prefill_with_rope(dims):
     B, n, window = 2, 90, 20
     wp = PrefillWorkload("p", 51, dims, B, n, window, False)
-    ip = prefill_inputs(wp)
-    ic = prefill_inputs(replace(wp, seed=52), kv_producer=False)
+    ip = prefill_inputs(wp, varied=True)
+    ic = prefill_inputs(replace(wp, seed=52), kv_producer=False, varied=True)
     pr = ref.prefill(dims.as_dict(), ip["weights"], ip["R"], ip["x"], window, False)
     cr = ref.prefill(dims.as_dict(), ic["weights"], ip["R"], ic["x"], window, False,
                      shared_kv=(pr["K_all"], pr["V_all"]))
@@ -74,7 +74,7 @@ def test_consumer_prefill_with_rope(dims):
 
 @pytest.mark.parametrize("dims", [TINY_R, SMALL_BF16_R])
 def test_meta_prefix_with_rope(dims):
-    inp = prefill_inputs(PrefillWorkload("m", 9, dims, 1, 8, 4, False))
+    inp = prefill_inputs(PrefillWorkload("m", 9, dims, 1, 8, 4, False), varied=True)
     _, meta = run_meta_prefix(dims, inp["weights"], inp["R"])
     want = ref.meta_prefix(dims.as_dict(), inp["weights"], inp["R"])
     tol = TOL[dims.dtype]
@@ -87,7 +87,7 @@ def test_meta_prefix_with_rope(dims):
     (SMALL_BF16_R, 60, 9, 64, False, 64), (SMALL_BF16_R, 130, 4, 64, True, 160)])
 def test_decode_with_rope(dims, n0, steps, window, is_global, cap):
     B = 2
-    inp = prefill_inputs(PrefillWorkload("pd", n0 + steps, dims, B, n0 + steps, window, is_global))
+    inp = prefill_inputs(PrefillWorkload("pd", n0 + steps, dims, B, n0 + steps, window, is_global), varied=True)
     x = inp["x"]
     print(f"case {dims.dtype} n0={n0} steps={steps} W={window} global={is_global}", flush=True)
     z = np.zeros((B, dims.n_kv_heads, cap, dims.head_dim))
@@ -108,8 +108,8 @@ def test_consumer_decode_with_rope(dims):
     B, n0, steps, window = 2, 30, 6, 16
     cap = window
     wp = PrefillWorkload("p", 61, dims, B, n0 + steps, window, False)
-    ip = prefill_inputs(wp)
-    ic = prefill_inputs(replace(wp, seed=62), kv_producer=False)
+    ip = prefill_inputs(wp, varied=True)
+    ic = prefill_inputs(replace(wp, seed=62), kv_producer=False, varied=True)
     mp = ref.meta_prefix(dims.as_dict(), ip["weights"], ip["R"])
     z = np.zeros((B, dims.n_kv_heads, cap, dims.head_dim))
     pre_p = ref.prefill(dims.as_dict(), ip["weights"], ip["R"], ip["x"][:, :n0], window, False,
