@@ -1,21 +1,27 @@
 """GPU parity of the block around the layer (pre-norms, residuals, SiLU-gated
 MLP) through the C ABI against the CPU oracle's block functions.
 
-Besides the output itself, the branch contribution out - x is compared with
-the oracle's, relative to its own RMS, so the residual stream cannot hide an
-error in the layer or the MLP.  That comparison allows, per element, for the
-two roundings of the residual stream to the storage type (x1 and out, each
-within half an ulp: 2^-9 of the value in bf16, 2^-24 in fp32).
+The bf16 path feeds its matrix units bf16 operands: the layer's input (the
+pre-norm output), the residual stream and the MLP's input and hidden units
+are stored in bf16 between kernels.  Storing them moves the block's result by
+itself, in exact arithmetic, by about 2% of the output's RMS at these random
+weights (the SSM state is the sensitive part: its largest element error from
+the input rounding alone reaches ~9% of its RMS); the oracle's `store` map
+(pinned on the CPU) computes that effect.
 
-The bf16 path also feeds its matrix units bf16 operands: the layer's input
-(the pre-norm output) and the MLP's input and hidden units are rounded to
-bf16 between kernels.  The SSM state is sensitive to that input rounding at
-the bar's scale (its largest element error reaches ~9% of its RMS), so the
-layer's state, conv history and K/V are compared with the oracle evaluated on
-the same stored values (its `store` map, bf16 rounding from the input
-recipe).  The block output is compared with the exact oracle: rounding the
-oracle's residual stream at the same points would, where the two sides differ
-by a fraction of an ulp, round them apart rather than together.
+* The block output is compared with the exact oracle, to the layer's bar
+  plus that storage effect, measured by the oracle on the same inputs (the
+  distance of the exact oracle from the stored-value oracle).  Comparing the
+  output with the stored-value oracle itself is no tighter: where the two
+  sides' residual streams differ by a fraction of an ulp they round apart.
+  The branch contribution out - x is compared the same way relative to its
+  own RMS, beyond the residual stream's two roundings (x1 and out, half an
+  ulp each: 2^-9 of the value in bf16, 2^-24 in fp32), so the residual stream
+  cannot hide an error in the layer or the MLP.
+* The layer's state, conv history and K/V are compared with the stored-value
+  oracle at the layer's bar.
+fp32 blocks store in fp32: there the oracles coincide and every bar is the
+fp32 one.
 """
 from dataclasses import replace
 
@@ -67,14 +73,26 @@ def _store(dims):
     return round_bf16 if dims.dtype == "bf16" else (lambda v: v)
 
 
-def _assert_block(got_out, want_out, x, tol, label, dtype):
-    e = rel_err(got_out, want_out)
+def _assert_block(got_out, want_exact, want_stored, x, tol, label, dtype):
+    """The output against the exact oracle.  The bar is tol (the layer's bar)
+    plus the distance of the exact oracle from the oracle on stored values
+    (`store`), i.e. what storing the block's intermediates in the path's type
+    moves the output by itself, computed by the oracle on these inputs; the
+    branch contribution out - x gets the same treatment beyond the residual
+    stream's two roundings (x1 and out, half an ulp each).  fp32: store is
+    the identity, so the bar is tol."""
     half_ulp = 2.0 ** -9 if dtype == "bf16" else 2.0 ** -24
-    branch = want_out - x
-    excess = np.abs(got_out - want_out) - 2.0 * half_ulp * np.abs(want_out)
-    e_branch = float(np.maximum(excess, 0.0).max()) / float(np.sqrt(np.mean(branch * branch)))
-    print(f"  {label}: err out={e:.2e} branches={e_branch:.2e} (beyond storage rounding)", flush=True)
-    assert e <= tol and e_branch <= tol
+    branch = want_exact - x
+    rms_b = float(np.sqrt(np.mean(branch * branch)))
+    e = rel_err(got_out, want_exact)
+    e_store = rel_err(want_stored, want_exact)
+    excess = np.abs(got_out - want_exact) - 2.0 * half_ulp * np.abs(want_exact)
+    e_branch = float(np.maximum(excess, 0.0).max()) / rms_b
+    e_store_branch = float(np.abs(want_stored - want_exact).max()) / rms_b
+    print(f"  {label}: err out={e:.2e} (bar {tol:.0e} + storage effect {e_store:.2e}); branches "
+          f"{e_branch:.2e} beyond the residual's rounding (bar {tol:.0e} + {e_store_branch:.2e}); "
+          f"vs stored-value oracle {rel_err(got_out, want_stored):.2e}", flush=True)
+    assert e <= tol + e_store and e_branch <= tol + e_store_branch
 
 
 @pytest.mark.parametrize("dims,d_ff,B,n,window,is_global", [
@@ -91,7 +109,8 @@ def test_block_prefill_matches_oracle(dims, d_ff, B, n, window, is_global):
                                store=_store(dims))
     got = _run_block_prefill(dims, inp, window, is_global)
     tol = TOL[dims.dtype]
-    _assert_block(np_of(got["out"]), want["out"], inp["x"].astype(np.float64), tol, "prefill", dims.dtype)
+    _assert_block(np_of(got["out"]), want["out"], stored["out"], inp["x"].astype(np.float64), tol, "prefill",
+                  dims.dtype)
     e_h = rel_err(np_of(got["h"]), stored["h"])
     print(f"  state err (stored-operand oracle) {e_h:.2e}, exact oracle {rel_err(np_of(got['h']), want['h']):.2e}",
           flush=True)
@@ -128,8 +147,8 @@ def test_block_decode_matches_longer_prefill(dims, d_ff, n0, steps, window, is_g
         out = torch.empty(B, dims.d_model, dtype=sd, device="cuda")
         hb.hh_block_decode_step(blk, xt, meta, window, is_global, kv, got["h"], got["conv"], out)
         torch.cuda.synchronize()
-        _assert_block(np_of(out), want["out"][:, n0 + s], x[:, n0 + s].astype(np.float64), tol,
-                      f"step {s}", dims.dtype)
+        _assert_block(np_of(out), want["out"][:, n0 + s], stored["out"][:, n0 + s],
+                      x[:, n0 + s].astype(np.float64), tol, f"step {s}", dims.dtype)
     assert rel_err(np_of(got["h"]), stored["h"]) <= tol
     assert (got["len"].cpu().numpy() == n0 + steps).all()
 
@@ -144,14 +163,15 @@ def test_block_full_width_prefill_and_decode():
     inp = block_inputs(PrefillWorkload("bfw", n + steps, dims, 1, n + steps, window, False), d_ff, seed=7,
                        varied=True)
     x = inp["x"]
-    want = ref.block_prefill(dims.as_dict(), inp["weights"], inp["R"], x, window, False,
-                             cache=dict(k=np.zeros((1, dims.n_kv_heads, window, dims.head_dim)),
-                                        v=np.zeros((1, dims.n_kv_heads, window, dims.head_dim)),
-                                        is_ring=True))
+    cache = dict(k=np.zeros((1, dims.n_kv_heads, window, dims.head_dim)),
+                 v=np.zeros((1, dims.n_kv_heads, window, dims.head_dim)), is_ring=True)
+    want = ref.block_prefill(dims.as_dict(), inp["weights"], inp["R"], x, window, False, cache=cache)
+    stored = ref.block_prefill(dims.as_dict(), inp["weights"], inp["R"], x, window, False, cache=cache,
+                               store=_store(dims))
     got = _run_block_prefill(dims, dict(inp, x=x[:, :n]), window, False, cache_cap=window)
     tol = TOL[dims.dtype]
-    _assert_block(np_of(got["out"]), want["out"][:, :n], x[:, :n].astype(np.float64), tol, "prefill",
-                  dims.dtype)
+    _assert_block(np_of(got["out"]), want["out"][:, :n], stored["out"][:, :n], x[:, :n].astype(np.float64),
+                  tol, "prefill", dims.dtype)
     sd = hb.storage_dtype(dims)
     kv = hb.make_kv(None, None, got["cache_k"], got["cache_v"], got["len"], window, True)
     meta = hb.make_meta(got["meta"]["k"], got["meta"]["v"], None, None)
@@ -160,5 +180,5 @@ def test_block_full_width_prefill_and_decode():
         out = torch.empty(1, dims.d_model, dtype=sd, device="cuda")
         hb.hh_block_decode_step(got["block"], xt, meta, window, False, kv, got["h"], got["conv"], out)
         torch.cuda.synchronize()
-        _assert_block(np_of(out), want["out"][:, n + s], x[:, n + s].astype(np.float64), tol, f"step {s}",
-                      dims.dtype)
+        _assert_block(np_of(out), want["out"][:, n + s], stored["out"][:, n + s], x[:, n + s].astype(np.float64),
+                      tol, f"step {s}", dims.dtype)

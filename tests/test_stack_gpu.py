@@ -5,17 +5,20 @@ producing for itself; meta K/V per cache; each block's own SSM state).
 
 Six blocks with full attention in blocks 0, 3 and 5: block 1 produces into a
 ring that block 2 reads, block 4 produces alone.  Batch 4, caches holding 20
-positions (the 16-slot rings have wrapped), three steps.  The oracle chains
-block_decode_step through the same plan; compared after every step are the
-stack output, and after the last step every block's SSM state and conv
-history and every cache's slots and lengths.
+positions (the 16-slot rings have wrapped), three steps.
 
-fp32 blocks are compared with the exact oracle chain (bar 1e-4).  The bf16
-path stores every activation it hands between kernels (within a block and
-from block to block) in bf16, so the oracle chain applies the same rounding
-(the oracle's `store` map, plus the rounding of each block's output before
-the next block reads it); the stack output is also compared with the exact,
-unrounded chain.  Bar 3e-2 for both.
+* Stack output: the oracle chains block_decode_step through the same plan
+  on its own values; compared after every step with the GPU's output.  fp32:
+  bar 1e-4.  bf16: the path stores every activation it hands between kernels
+  (inside a block and from block to block) in bf16, which moves the result by
+  itself; the bar is the layer's 3e-2 plus that effect, measured as the
+  distance between the exact chain and the same chain on stored values (the
+  oracle's `store` map plus the rounding of each block's output).
+* Every block's SSM state and conv history and every cache's slots and
+  lengths after the last step: against the oracle chain fed, block by block
+  and step by step, the inputs the GPU's blocks received (on stored values
+  for bf16), so each block's state is checked on its own inputs, at the
+  layer's bar; slots no step wrote keep their bits.
 """
 from dataclasses import replace
 
@@ -38,8 +41,11 @@ TINY_STACK = StackWorkload("stack6_tiny", 80, TINY, MLP_HIDDEN_TINY, batch=4, co
 SMALL_STACK = replace(TINY_STACK, name="stack6_small_bf16", seed=81, dims=SMALL_BF16, d_ff=256)
 
 
-def _oracle_chain(w, inp, store):
-    """Stack outputs per step and the final states/caches, oracle side."""
+def _oracle_chain(w, inp, store, forced=None):
+    """Stack outputs per step and the final states/caches, oracle side.
+    forced[s][i]: the input block i received at step s (teacher forcing);
+    None: each block reads the previous block's oracle output (rounded by
+    `store` when given)."""
     dims = w.dims
     caches = {n: dict(k=c["k"].astype(np.float64), v=c["v"].astype(np.float64), len=c["len"].copy(),
                       is_ring=c["is_ring"]) for n, c in inp["caches"].items()}
@@ -48,6 +54,8 @@ def _oracle_chain(w, inp, store):
     for s in range(STEPS):
         cur = inp["x"][s].astype(np.float64)
         for i, blk in enumerate(inp["blocks"]):
+            if forced is not None:
+                cur = forced[s][i]
             c = inp["caches"][blk["cache"]]
             kw = {} if store is None else dict(store=store)
             r = ref.block_decode_step(dims.as_dict(), blk["weights"], cur, c["meta_k"], c["meta_v"],
@@ -82,26 +90,32 @@ def test_decode_stack_matches_oracle_chain(w):
         blocks.append(dict(dev=hb.upload_block_weights(dims, blk["weights"]),
                            h=hb.to_device(blk["h"], torch.float32),
                            conv=hb.to_device(blk["conv"], torch.float32)))
-    outs = []
+    outs, inputs = [], []
     for s in range(STEPS):
         cur = hb.to_device(inp["x"][s], sd)
+        inputs.append([])
         for blk, b in zip(inp["blocks"], blocks):
             c = dev[blk["cache"]]
+            inputs[-1].append(cur)
             nxt = torch.empty(B, d, dtype=sd, device="cuda")
             hb.hh_block_decode_step(b["dev"], cur, c["meta"], w.window, blk["is_global"], c["kv"],
                                     b["h"], b["conv"], nxt)
             cur = nxt
         torch.cuda.synchronize()
         outs.append(np_of(cur))
+    forced = [[np_of(t) for t in step] for step in inputs]
 
     tol = TOL[dims.dtype]
     store = round_bf16 if dims.dtype == "bf16" else None
-    want_outs, want_states, want_caches = _oracle_chain(w, inp, store)
-    exact_outs = _oracle_chain(w, inp, None)[0] if store is not None else want_outs
+    exact_outs = _oracle_chain(w, inp, None)[0]
+    stored_outs = _oracle_chain(w, inp, store)[0] if store is not None else exact_outs
+    _, want_states, want_caches = _oracle_chain(w, inp, store, forced=forced)
     for s in range(STEPS):
-        e, e_exact = rel_err(outs[s], want_outs[s]), rel_err(outs[s], exact_outs[s])
-        print(f"  step {s}: out err {e:.2e} (exact chain {e_exact:.2e})", flush=True)
-        assert e <= tol and e_exact <= tol
+        e = rel_err(outs[s], exact_outs[s])
+        e_store = rel_err(stored_outs[s], exact_outs[s])
+        print(f"  step {s}: out err {e:.2e} (bar {tol:.0e} + storage effect {e_store:.2e}; "
+              f"vs stored-value chain {rel_err(outs[s], stored_outs[s]):.2e})", flush=True)
+        assert e <= tol + e_store
     for i, (blk, b) in enumerate(zip(inp["blocks"], blocks)):
         e_h = rel_err(np_of(b["h"]), want_states[i][0])
         e_c = rel_err(np_of(b["conv"]), want_states[i][1])
