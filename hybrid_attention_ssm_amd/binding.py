@@ -101,6 +101,9 @@ def lib() -> ctypes.CDLL:
         L.hh_decode_step.restype = ctypes.c_int
         L.hh_decode_step.argtypes = [P(HHDims), P(HHWeights), _vp, _i32, P(HHMeta), _i32, _i32,
                                      P(HHKV), P(HHSsmState), _vp, _vp, ctypes.c_size_t, _vp]
+        L.hh_decode_step_noalloc.restype = ctypes.c_int
+        L.hh_decode_step_noalloc.argtypes = [P(HHDims), P(HHWeights), _vp, _i32, P(HHMeta), _i32, _i32,
+                                             P(HHKV), P(HHSsmState), _vp, _vp]
         L.hh_block_meta_prefix_workspace_size.restype = ctypes.c_size_t
         L.hh_block_meta_prefix_workspace_size.argtypes = [P(HHDims), _i32]
         L.hh_block_prefill_workspace_size.restype = ctypes.c_size_t
@@ -336,6 +339,20 @@ def hh_decode_step(layer: DeviceLayer, x_t: torch.Tensor, meta: HHMeta, window: 
         ctypes.byref(d), ctypes.byref(layer.struct), _ptr(x_t), B, ctypes.byref(meta),
         int(window), int(bool(is_global)), ctypes.byref(kv), ctypes.byref(st), _ptr(out),
         _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def hh_decode_step_noalloc(layer: DeviceLayer, x_t: torch.Tensor, meta: HHMeta, window: int,
+                           is_global: bool, kv: HHKV, state_h: torch.Tensor, state_conv: torch.Tensor,
+                           out: torch.Tensor, stream=None) -> None:
+    """hh_decode_step_noalloc on device tensors (the library's static scratch,
+    no workspace); x_t [B, d] -> out [B, d]."""
+    B = x_t.shape[0]
+    d = hh_dims(layer.dims)
+    st = HHSsmState(_ptr(state_h), _ptr(state_conv))
+    _check("hh_decode_step_noalloc", lib().hh_decode_step_noalloc(
+        ctypes.byref(d), ctypes.byref(layer.struct), _ptr(x_t), B, ctypes.byref(meta),
+        int(window), int(bool(is_global)), ctypes.byref(kv), ctypes.byref(st), _ptr(out),
+        _stream(stream)))
 
 
 def to_device(a: np.ndarray, dtype: torch.dtype, device="cuda") -> torch.Tensor:

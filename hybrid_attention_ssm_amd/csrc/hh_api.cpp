@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -618,6 +619,38 @@ hh_status block_decode_t(const Shape &s, const hh_block_weights *w, const void *
   return block_mlp_t<T>(s, w, B, ws, BL, out, st);
 }
 
+// ---- scratch of the entry point that allocates nothing ---------------------
+// hh_decode_step_noalloc's workspace: a file-scope device array, one copy per
+// GPU the library runs on, held until the process ends.  In host code the
+// array's name is not a device address; its address on the current device
+// comes from hipGetSymbolAddress (once per device, kept in g_scratch) and is
+// the only way the host refers to it.  No kernel of the decode step reads a
+// scratch byte it has not written in the same call, so nothing is cleared.
+constexpr size_t kStaticScratchBytes = HH_STATIC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxScratchDevices] = {};
+
+hh_status static_scratch(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(HH_ERR_UNSUPPORTED, "device %d: the static scratch is tracked for devices 0..%d", dev,
+                kMaxScratchDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return HH_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -727,6 +760,24 @@ hh_status hh_decode_step(const hh_dims *dims, const hh_weights *w, const void *x
   DecodeLayout L = decode_layout(s, batch, max_real_keys(kv, window, is_global));
   if (!ws || ws_bytes < L.total)
     return fail(HH_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, L.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return s.dtype == HH_BF16
+             ? decode_t<hh::bf16>(s, w, x_t, batch, meta, window, is_global, kv, state, out, ws, L, st)
+             : decode_t<float>(s, w, x_t, batch, meta, window, is_global, kv, state, out, ws, L, st);
+}
+
+hh_status hh_decode_step_noalloc(const hh_dims *dims, const hh_weights *w, const void *x_t, int32_t batch,
+                                 const hh_meta *meta, int32_t window, int32_t is_global, hh_kv *kv,
+                                 hh_ssm_state *state, void *out, void *stream) {
+  Shape s;
+  hh_status r = check_decode_call(dims, w, x_t, batch, meta, window, is_global, kv, state, out, s);
+  if (r != HH_OK) return r;
+  DecodeLayout L = decode_layout(s, batch, max_real_keys(kv, window, is_global));
+  if (L.total > kStaticScratchBytes)
+    return fail(HH_ERR_WORKSPACE, "this step needs %zu bytes of scratch; the static scratch holds %zu "
+                "(use hh_decode_step with a workspace)", L.total, kStaticScratchBytes);
+  void *ws = nullptr;
+  if ((r = static_scratch(&ws)) != HH_OK) return r;
   hipStream_t st = static_cast<hipStream_t>(stream);
   return s.dtype == HH_BF16
              ? decode_t<hh::bf16>(s, w, x_t, batch, meta, window, is_global, kv, state, out, ws, L, st)

@@ -231,6 +231,24 @@ hh_status hh_decode_step(const hh_dims *dims, const hh_weights *w,
                          hh_ssm_state *state, void *out, void *ws,
                          size_t ws_bytes, void *stream);
 
+/* hh_decode_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same step with no workspace argument.  Its scratch is a static device
+ * array of HH_STATIC_SCRATCH_BYTES inside the library, one per GPU, held until
+ * the process ends; the call itself allocates nothing.  Arguments, results
+ * and errors as for hh_decode_step, plus HH_ERR_WORKSPACE (before anything
+ * is enqueued) when the step needs more scratch than that, i.e. more than
+ * hh_decode_workspace_size() reports (32 MiB covers batch 128 at 1.5B widths
+ * with caches of up to 32768 slots).  Every call on one GPU shares that GPU's
+ * scratch: calls that can overlap on one GPU (different streams or host
+ * threads without ordering between them) race and must be serialised by the
+ * caller. */
+#define HH_STATIC_SCRATCH_BYTES (32u << 20)
+hh_status hh_decode_step_noalloc(const hh_dims *dims, const hh_weights *w,
+                                 const void *x_t, int32_t batch, const hh_meta *meta,
+                                 int32_t window, int32_t is_global, hh_kv *kv,
+                                 hh_ssm_state *state, void *out, void *stream);
+
 /* ---- the block around the layer ---------------------------------------
  * One block (Hymba paper, Fig. 4 and the architecture table's MLP width):
  *   x1  = x + layer(g1 * rms(x))            (the layer above, meta rows g1 * rms(R))
