@@ -198,9 +198,11 @@ PrefillLayout prefill_layout(const Shape &s, int B, int n) {
     take(HH_WS_K, (size_t)B * s.G * n * s.hd * s.es);
     take(HH_WS_V, (size_t)B * s.G * n * s.hd * s.es);
   }
-  take(HH_WS_XS, T * s.D * 4);
-  take(HH_WS_Z, T * s.D * s.es);
-  take(HH_WS_DELTA, T * s.dtw * 4);
+  // the SSM features in the channel-block-major layout (whole 64-column blocks)
+  const size_t D64 = (s.D + 63) / 64 * 64, dt64 = (s.dtw + 63) / 64 * 64;
+  take(HH_WS_XS, T * D64 * 4);
+  take(HH_WS_Z, T * D64 * s.es);
+  take(HH_WS_DELTA, T * dt64 * 4);
   take(HH_WS_BC, T * 2 * s.N * 4);
   take(HH_WS_O, T * s.Wa * s.es);
   take(HH_WS_Y, T * s.D * s.es);
@@ -278,6 +280,7 @@ hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, i
   if (prod && kv && kv->cache_k) {
     e.cache_k = kv->cache_k; e.cache_v = kv->cache_v; e.cap = kv->cap; e.is_ring = kv->is_ring;
   }
+  e.ssm_rows = rows;
   e.xs = reinterpret_cast<float *>(at(ws, L.off[HH_WS_XS])); e.z = at(ws, L.off[HH_WS_Z]);
   e.dt = reinterpret_cast<float *>(at(ws, L.off[HH_WS_DELTA]));
   e.bc = reinterpret_cast<float *>(at(ws, L.off[HH_WS_BC]));
@@ -347,6 +350,7 @@ hh_status meta_prefix_t(const Shape &s, const hh_weights *w, const void *R, void
   e.Wa = s.Wa; e.KV = s.KV; e.D = s.D; e.Ddt = s.dtw; e.N = s.N; e.hd = s.hd; e.n_rows_per_seq = s.m;
   e.q = at(ws, L.off[HH_WS_Q]);
   e.k_full = mk; e.v_full = mv;
+  e.ssm_rows = s.m;
   e.xs = reinterpret_cast<float *>(at(ws, L.off[HH_WS_XS])); e.z = at(ws, L.off[HH_WS_Z]);
   e.dt = reinterpret_cast<float *>(at(ws, L.off[HH_WS_DELTA]));
   e.bc = reinterpret_cast<float *>(at(ws, L.off[HH_WS_BC]));

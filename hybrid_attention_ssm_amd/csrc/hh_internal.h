@@ -75,6 +75,11 @@ struct InProjOut {
   void *cache_k, *cache_v;    // prefill/decode cache [B, G, cap, hd] (may be null)
   int cap, is_ring;
   const int32_t *len;         // decode: position of the new token per row
+  // The SSM features: row-major [rows, width] when ssm_rows is 0 (decode),
+  // else channel-block-major (ssm_index: blocks of 64 columns, each holding
+  // all ssm_rows rows), so that a scan wave's 64 channels are one contiguous
+  // 256-byte run per row and its chunk one contiguous stream.
+  int ssm_rows;
   float *xs;                  // [rows, D] fp32 (SSM input features)
   void *z;                    // [rows, D]
   float *dt;                  // [rows, Ddt] softplus(dt + bias)
@@ -110,6 +115,17 @@ __device__ __forceinline__ int inproj_src_row(const InProjOut &e, int n) {
   if (n >= e.Wa + e.KV) return n;
   const int j = n % e.hd;
   return n - j + ((j & 1) ? e.hd / 2 : 0) + (j >> 1);
+}
+
+// Element (row, col) of an SSM feature array in the channel-block-major
+// layout: 64-column blocks, block-major, rows inside a block, the block's
+// 64 columns contiguous.  A buffer for `rows` rows and width w holds
+// rows * round_up(w, 64) elements.
+__host__ __device__ __forceinline__ size_t ssm_index(size_t row, int col, size_t rows) {
+  return ((size_t)(col >> 6) * rows + row) * 64 + (col & 63);
+}
+__device__ __forceinline__ size_t ssm_at(const InProjOut &e, int row, int col, int width) {
+  return e.ssm_rows ? ssm_index(row, col, e.ssm_rows) : (size_t)row * width + col;
 }
 
 // Store 8 consecutive columns col..col+7 of one row (col % 8 == 0).  Every
@@ -346,13 +362,15 @@ __device__ __forceinline__ void inproj_storeW(const InProjOut &e, int row, const
       put(ci.d, v, std::integral_constant<int, W>{});
       return;
     }
-    case 3: storeW_T<float, W>(e.xs + (size_t)row * D + ci.c, v); return;
-    case 4: storeW_T<T, W>(reinterpret_cast<T *>(e.z) + (size_t)row * D + ci.c, v); return;
+    // a group of W columns (W divides 64, col % W == 0) never crosses a
+    // 64-column block, so it stays one vector store in either layout
+    case 3: storeW_T<float, W>(e.xs + ssm_at(e, row, ci.c, D), v); return;
+    case 4: storeW_T<T, W>(reinterpret_cast<T *>(e.z) + ssm_at(e, row, ci.c, D), v); return;
     case 5: {
       float sp[W];
 #pragma unroll
       for (int i = 0; i < W; ++i) sp[i] = softplus_f(v[i] + ci.bias[i]);
-      storeW_T<float, W>(e.dt + (size_t)row * e.Ddt + ci.c, sp);
+      storeW_T<float, W>(e.dt + ssm_at(e, row, ci.c, e.Ddt), sp);
       return;
     }
     default: storeW_T<float, W>(e.bc + (size_t)row * 2 * e.N + ci.c, v); return;
@@ -412,6 +430,7 @@ struct AttnArgs {
 template <class T> hipError_t launch_attention(const AttnArgs &a, hipStream_t s);
 
 struct ScanArgs {
+  // xs, z and dt in the channel-block-major layout over B*n rows (ssm_index)
   const float *xs;         // [B*n, D] fp32
   const void *z;           // [B*n, D] (null: no gate, no Y)
   const float *dt;         // [B*n, D], or [B*n, S] for Mamba2 heads

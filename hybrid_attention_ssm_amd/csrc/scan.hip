@@ -8,8 +8,11 @@
 //   y_t = h_t . C_t,   Y_t = y_t * SiLU(z_t)
 //
 // One lane owns one channel and keeps its N = 16 states in registers; B_t and
-// C_t are the same for every channel, so each wavefront reads them as uniform
-// (scalar) loads while xs, Delta and z are read coalesced across 64 channels.
+// C_t are the same for every channel, so each wavefront reads them as
+// broadcasts from LDS, while xs, Delta and z arrive in the channel-block-major
+// layout (ssm_index): a wave's 64 channels are one contiguous 256-byte run per
+// time step, and consecutive steps are adjacent runs, so each wave streams its
+// chunk as one contiguous region.
 // exp(Delta A) is evaluated as 2^(Delta * A log2 e).
 //
 // Time is cut into chunks so that a single sequence fills the GPU:
@@ -37,7 +40,7 @@ struct ChanParams {
   float A2[NS];             // A * log2(e) (Mamba2: A2[0] is the head's)
   float w[KC];              // conv taps, w[KC-1] multiplies the current row
   float bias;
-  int dcol, dstride;        // Delta of this channel: column and row stride
+  int dcol;                 // Delta of this channel: its column
 };
 
 template <bool SC>
@@ -46,12 +49,10 @@ __device__ __forceinline__ void load_params(const ScanArgs &a, int c, ChanParams
     const int h = c / (a.D / a.S);
     p.A2[0] = a.A[h] * kLog2e;
     p.dcol = h;
-    p.dstride = a.S;
   } else {
 #pragma unroll
     for (int s = 0; s < NS; ++s) p.A2[s] = a.A[(size_t)c * NS + s] * kLog2e;
     p.dcol = c;
-    p.dstride = a.D;
   }
 #pragma unroll
   for (int j = 0; j < KC; ++j) {
@@ -66,11 +67,12 @@ template <class T>
 __device__ __forceinline__ void load_history(const ScanArgs &a, int b, int c, int t0, float hist[KC - 1]) {
   const float *xs = a.xs;
   const float *tail = a.tail0;
+  const size_t R = (size_t)a.B * a.n;
 #pragma unroll
   for (int j = 0; j < KC - 1; ++j) {
     const int pos = t0 - 1 - j;
     float v = 0.0f;
-    if (pos >= 0) v = xs[((size_t)b * a.n + pos) * a.D + c];
+    if (pos >= 0) v = xs[ssm_index((size_t)b * a.n + pos, c, R)];
     else if (tail && (a.k - 1) + pos >= 0) v = tail[(size_t)((a.k - 1) + pos) * a.D + c];
     hist[j] = v;
   }
@@ -110,14 +112,18 @@ template <class T, int MODE, bool SC>
 __device__ __forceinline__ void scan_range(const ScanArgs &a, int b, int c, bool active, int t0,
                                            int t1, const ChanParams &p, float h[NS],
                                            float hist[KC - 1], float &dsum, float *sbc) {
-  const float *xs = a.xs;
   const T *z = reinterpret_cast<const T *>(a.z);
   T *y = reinterpret_cast<T *>(a.y);
-  // without Y the gate is not needed: read (and ignore) xs instead, so the
-  // loads stay unconditional
-  const T *zp = y ? z : reinterpret_cast<const T *>(xs);
   const size_t D = a.D;
   const size_t row0 = (size_t)b * a.n;
+  const size_t R = (size_t)a.B * a.n;
+  // this lane's column of xs, Delta and z from the sequence's first row:
+  // step t is element t * 64 (channel-block-major layout)
+  const float *xs = a.xs + ssm_index(row0, c, R);
+  const float *dtp = a.dt + ssm_index(row0, p.dcol, R);
+  // without Y the gate is not needed: read (and ignore) xs instead, so the
+  // loads stay unconditional
+  const T *zp = y ? z + ssm_index(row0, c, R) : reinterpret_cast<const T *>(xs);
   const int lane = threadIdx.x;
   for (int s0 = t0; s0 < t1; s0 += SUB) {
     const int len = min(SUB, t1 - s0);
@@ -142,9 +148,9 @@ __device__ __forceinline__ void scan_range(const ScanArgs &a, int b, int c, bool
     auto load_batch = [&](int tb, float (&xo)[TB], float (&dvo)[TB], T (&zo)[TB]) {
 #pragma unroll
       for (int i = 0; i < TB; ++i) {
-        const size_t idx = (row0 + s0 + tb + i) * D + c;
+        const size_t idx = (size_t)(s0 + tb + i) * 64;
         xo[i] = xs[idx];
-        dvo[i] = a.dt[(row0 + s0 + tb + i) * p.dstride + p.dcol];
+        dvo[i] = dtp[idx];
         if (MODE == 1) zo[i] = zp[idx];
       }
     };
@@ -174,7 +180,7 @@ __device__ __forceinline__ void scan_range(const ScanArgs &a, int b, int c, bool
       for (int i = 0; i < TB; ++i) { xv[i] = xn[i]; dv[i] = dn[i]; zv[i] = zn[i]; }
     }
     for (; t < len; ++t) {
-      const size_t idx = (row0 + s0 + t) * D + c;
+      const size_t idx = (size_t)(s0 + t) * 64;
       const float4 *bc4 = reinterpret_cast<const float4 *>(sbc + t * 2 * NS);
       float bv[NS], cv[NS];
 #pragma unroll
@@ -186,9 +192,8 @@ __device__ __forceinline__ void scan_range(const ScanArgs &a, int b, int c, bool
           cv[4 * q] = u.x; cv[4 * q + 1] = u.y; cv[4 * q + 2] = u.z; cv[4 * q + 3] = u.w;
         }
       }
-      const float acc = scan_step<MODE, SC>(p, h, hist, xs[idx],
-                                            a.dt[(row0 + s0 + t) * p.dstride + p.dcol], bv, cv, dsum);
-      if (MODE == 1 && y && active) y[idx] = from_f32<T>(acc * silu_f(to_f32(z[idx])));
+      const float acc = scan_step<MODE, SC>(p, h, hist, xs[idx], dtp[idx], bv, cv, dsum);
+      if (MODE == 1 && y && active) y[(row0 + s0 + t) * D + c] = from_f32<T>(acc * silu_f(to_f32(zp[idx])));
     }
   }
 }
@@ -224,37 +229,69 @@ __global__ void __launch_bounds__(64) scan_pass1(ScanArgs a) {
   ds[((size_t)b * nc + ck) * a.D + c] = dsum;
 }
 
-// pass 2: chunk carries in order.  One lane per (channel, state) recurrence;
-// the loads of a group of chunks do not depend on the carry, so they are
-// issued together.  grid (ceil(N*D/256), B), 256 threads
+// pass 2: chunk carries.  Per (channel, state) the chunk summaries compose
+// as affine maps, H_k = exp(A S_k) H_{k-1} + h_k (S_k the chunk's sum of
+// Delta, h_k its end state from zero).  A group of G2 lanes shares one
+// (channel, state): lane j owns a run of consecutive chunks, loads all their
+// summaries at once and composes them from zero into one map; the G2 maps are
+// scanned across the group with lane shuffles (log2 G2 steps), which gives
+// each lane its run's entry state; the lane then walks its run again and
+// writes the state entering every following chunk.  grid (ceil(N*D*G2/256),
+// B), 256 threads.
+constexpr int P2_RUN = 24;   // chunks per lane at most
+
+template <int G2>
 __global__ void __launch_bounds__(256) scan_pass2(ScanArgs a) {
-  constexpr int U = 8;
   const int b = blockIdx.y;
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= NS * a.D) return;
+  const int gid = (blockIdx.x * 256 + (int)threadIdx.x) / G2;   // (state, channel) index
+  const int j = (int)threadIdx.x % G2;                           // lane in the group
+  const bool live = gid < NS * a.D;
+  const int idx = live ? gid : 0;
   const int s = idx / a.D, c = idx - s * a.D;
   const int nc = (a.n + a.chunk - 1) / a.chunk;
+  const int ncar = nc - 1;                       // carries to produce
+  const int run = (ncar + G2 - 1) / G2;          // <= P2_RUN (checked by the launcher)
+  const int k0 = min(j * run, ncar), k1 = min(k0 + run, ncar);
   const float A2 = (a.S ? a.A[c / (a.D / a.S)] : a.A[(size_t)c * NS + s]) * kLog2e;
-  float H = a.h0 ? a.h0[(size_t)c * NS + s] : 0.0f;
   const float *ds = a.carry + (size_t)a.B * nc * NS * a.D + (size_t)b * nc * a.D + c;
   float *hs = a.carry + ((size_t)b * nc * NS + s) * a.D + c;
   const size_t hstride = (size_t)NS * a.D;
-  for (int c0 = 0; c0 + 1 < nc; c0 += U) {
-    float Sv[U], hv[U];
+  float Sv[P2_RUN], hv[P2_RUN];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int ck = c0 + u;
-      const bool in = ck + 1 < nc;
-      Sv[u] = in ? ds[(size_t)ck * a.D] : 0.0f;
-      hv[u] = in ? hs[ck * hstride] : 0.0f;
-    }
+  for (int u = 0; u < P2_RUN; ++u) {
+    const bool in = live && k0 + u < k1;
+    Sv[u] = in ? ds[(size_t)(k0 + u) * a.D] : 0.0f;
+    hv[u] = in ? hs[(k0 + u) * hstride] : 0.0f;
+  }
+  // this lane's run as one map H -> P H + g
+  float P = 1.0f, g = 0.0f;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int ck = c0 + u;
-      if (ck + 1 >= nc) break;
-      H = fmaf(exp2_fast(A2 * Sv[u]), H, hv[u]);
-      hs[ck * hstride] = H;               // state entering chunk ck+1
+  for (int u = 0; u < P2_RUN; ++u) {
+    if (k0 + u >= k1) break;
+    const float d = exp2_fast(A2 * Sv[u]);
+    P *= d;
+    g = fmaf(d, g, hv[u]);
+  }
+  // inclusive scan of the maps over the group (lane j composes lanes 0..j,
+  // the earlier map applied first), then shift to exclusive
+#pragma unroll
+  for (int off = 1; off < G2; off <<= 1) {
+    const float Pp = __shfl_up(P, off, G2), gp = __shfl_up(g, off, G2);
+    if (j >= off) {
+      g = fmaf(P, gp, g);
+      P *= Pp;
     }
+  }
+  float Pe = __shfl_up(P, 1, G2), ge = __shfl_up(g, 1, G2);
+  if (j == 0) { Pe = 1.0f; ge = 0.0f; }
+  const float h0 = a.h0 ? a.h0[(size_t)c * NS + s] : 0.0f;
+  float H = fmaf(Pe, h0, ge);                     // state entering chunk k0
+  if (!live) return;
+#pragma unroll
+  for (int u = 0; u < P2_RUN; ++u) {
+    if (k0 + u >= k1) break;
+    H = fmaf(exp2_fast(A2 * Sv[u]), H, hv[u]);
+    hs[(k0 + u) * hstride] = H;                 // state entering chunk k0+u+1
   }
 }
 
@@ -303,7 +340,8 @@ size_t scan_carry_bytes(int B, int n, int D, int N, int *chunk_out) {
   const int cw = (D + 63) / 64;
   const long waves = (long)B * cw;
   int nc = (int)((4096 + waves - 1) / waves);
-  nc = std::max(1, std::min(nc, (n + 63) / 64));
+  // at most 64 * P2_RUN + 1 chunks, so pass 2's lane groups hold every carry
+  nc = std::max(1, std::min({nc, (n + 63) / 64, 1024}));
   int chunk = (n + nc - 1) / nc;
   chunk = (chunk + 7) / 8 * 8;
   if (chunk < 8) chunk = 8;
@@ -318,7 +356,14 @@ static hipError_t launch_scan_t(const ScanArgs &a, hipStream_t s) {
   const int cw = (a.D + 63) / 64;
   if (nc > 1) {
     hipLaunchKernelGGL((scan_pass1<T, SC>), dim3(nc - 1, cw, a.B), dim3(64), 0, s, a);
-    hipLaunchKernelGGL(scan_pass2, dim3((NS * a.D + 255) / 256, a.B), dim3(256), 0, s, a);
+    // lanes per (channel, state) group: the fewest whose runs hold every carry
+    const int ncar = nc - 1;
+    const int g2 = ncar <= 4 * P2_RUN ? 4 : ncar <= 16 * P2_RUN ? 16 : ncar <= 64 * P2_RUN ? 64 : 0;
+    if (!g2) return hipErrorInvalidValue;
+    const dim3 grid2((unsigned)(((long)NS * a.D * g2 + 255) / 256), a.B);
+    if (g2 == 4) hipLaunchKernelGGL(scan_pass2<4>, grid2, dim3(256), 0, s, a);
+    else if (g2 == 16) hipLaunchKernelGGL(scan_pass2<16>, grid2, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(scan_pass2<64>, grid2, dim3(256), 0, s, a);
   }
   hipLaunchKernelGGL((scan_pass3<T, SC>), dim3(nc, cw, a.B), dim3(64), 0, s, a);
   return hipGetLastError();

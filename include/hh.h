@@ -309,9 +309,9 @@ enum {
   HH_WS_Q = 0,   /* [B*n, H*hd] dtype */
   HH_WS_K,       /* [B, G, n, hd] dtype (used when full_k is NULL) */
   HH_WS_V,
-  HH_WS_XS,      /* [B*n, D] fp32 SSM input features */
-  HH_WS_Z,       /* [B*n, D] dtype */
-  HH_WS_DELTA,   /* [B*n, D] fp32, softplus applied */
+  HH_WS_XS,      /* SSM input features, fp32; these three regions hold  */
+  HH_WS_Z,       /* [B*n, D] (Delta: [B*n, D or S]) channel-block-major: */
+  HH_WS_DELTA,   /* element (r, c) at ((c/64)*B*n + r)*64 + c%64; Delta softplus'd */
   HH_WS_BC,      /* [B*n, 2N] fp32: B then C */
   HH_WS_O,       /* [B*n, H*hd] dtype attention output */
   HH_WS_Y,       /* [B*n, D] dtype gated SSM output */
