@@ -104,10 +104,11 @@ def decode_bytes(dims, B, layers, p, window, ring_cap, global_cap):
 
 
 # ---------------------------------------------------------------------------
-def bench_prefill(args, hb, torch, rope_base=0.0, ssm_heads=0):
+def bench_prefill(args, hb, torch, rope_base=0.0, ssm_heads=0, concurrent=False):
     """The 8k SWA prefill; rope_base > 0 times the same layer with Q and K
     turned by the rotary embedding (same inputs), ssm_heads > 0 with Mamba2
-    SSM heads (inputs drawn for that layout)."""
+    SSM heads (inputs drawn for that layout); concurrent runs the SSM branch
+    on the library's side stream (HH_CONCURRENT_BRANCHES=1)."""
     from dataclasses import replace
     from hybrid_attention_ssm_amd.configs import CFG1_SWA_8K
     from hybrid_attention_ssm_amd.synth import prefill_inputs
@@ -116,7 +117,10 @@ def bench_prefill(args, hb, torch, rope_base=0.0, ssm_heads=0):
     w = replace(w, dims=dims)
     B, n, W = w.batch, w.seqlen, w.window
     tag = ((f" (RoPE base {rope_base:g})" if rope_base else "") +
-           (f" (Mamba2 heads: {ssm_heads})" if ssm_heads else ""))
+           (f" (Mamba2 heads: {ssm_heads})" if ssm_heads else "") +
+           (" (branches on two streams)" if concurrent else ""))
+    prev_env = os.environ.get("HH_CONCURRENT_BRANCHES")
+    os.environ["HH_CONCURRENT_BRANCHES"] = "1" if concurrent else "0"
     log(f"[bench] prefill setup {w.name}{tag}")
     inp = prefill_inputs(w)
     sd = hb.storage_dtype(dims)
@@ -157,6 +161,10 @@ def bench_prefill(args, hb, torch, rope_base=0.0, ssm_heads=0):
     torch.cuda.synchronize()
     stages = hb.hh_timing_read()
     hb.hh_timing_enable(False)
+    if prev_env is None:
+        os.environ.pop("HH_CONCURRENT_BRANCHES", None)
+    else:
+        os.environ["HH_CONCURRENT_BRANCHES"] = prev_env
     fl = prefill_flops(dims, B, n, W, False)
     st_ms = {name: tot / cnt for name, (cnt, tot) in stages.items()}
     log(f"[bench] prefill{tag} {ms_step:.3f} ms/step; stages " +
@@ -400,6 +408,8 @@ def main():
                     help="skip the prefill line with the rotary embedding of Q and K")
     ap.add_argument("--no-mamba2", action="store_true",
                     help="skip the prefill line with Mamba2 SSM heads")
+    ap.add_argument("--no-branches", action="store_true",
+                    help="skip the prefill line with the SSM branch on a second stream")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192,
                     help="prefill tokens the CPU oracle runs (default: the whole 8k workload)")
     ap.add_argument("--cpu-sample-seqs", type=int, default=64,
@@ -437,6 +447,9 @@ def main():
         pre_rope = bench_prefill(args, hb, torch, rope_base=ROPE_BASE)
     if pre is not None and not args.no_mamba2:
         pre_m2 = bench_prefill(args, hb, torch, ssm_heads=MAMBA2_HEADS)
+    pre_br = None
+    if pre is not None and not args.no_branches:
+        pre_br = bench_prefill(args, hb, torch, concurrent=True)
     dec = bench_decode(args, hb, torch) if args.only in ("decode", "both") else None
     stack = None
     if args.only in ("decode", "both") and not args.no_stack:
@@ -495,6 +508,14 @@ def main():
                              "stage_us": {k: v * 1e3 for k, v in pre_m2["stages"].items()},
                              "scan_exps": T * dd.d_inner,
                              "scan_exps_per_s": T * dd.d_inner / (t_scan2 * 1e-3) if t_scan2 else None}
+        if pre_br is not None:
+            # the same workload with the SSM branch on the library's side stream (opt-in: measured
+            # slower than one stream); stage times overlap there, so only the step time is reported
+            rec["branches"] = {"mode": "HH_CONCURRENT_BRANCHES=1 (input projection in two row ranges, "
+                                       "scan summaries beside the second, rest of the scan beside the attention)",
+                               "ms_per_step": pre_br["ms_step"],
+                               "value": pre["B"] * pre["n"] / (pre_br["ms_step"] * 1e-3), "unit": "tok/s",
+                               "vs_one_stream": pre["ms_step"] / pre_br["ms_step"]}
         if t_in:
             ach = fl["inproj"] / (t_in * 1e-3)
             tr = measured_traffic("gemm_bf16_lds", pre["workload"])
@@ -514,6 +535,9 @@ def main():
              "value": B / (dec["ms_step"] * 1e-3), "unit": "tok/s", "ms_per_step": dec["ms_step"],
              "hbm_frac_step": dec["bytes"] / (dec["ms_step"] * 1e-3) / HBM_PEAK,
              "algorithmic_bytes_per_step": dec["bytes"],
+             # the same fraction over the 2.01 GB per step of the design notes' count (without
+             # the fp32 conv-history bytes)
+             "hbm_frac_step_2p01GB": 2.01e9 / (dec["ms_step"] * 1e-3) / HBM_PEAK,
              "stage_us": {k: v[1] / v[0] * 1e3 for k, v in st.items()}}
         if "decode_attention_global" in st:
             cnt, tot = st["decode_attention_global"]
@@ -542,7 +566,10 @@ def main():
         main_key = "prefill" if pre is not None else "decode"
         rec["cpu_baseline"] = {"value": cb[main_key]["value"], "unit": "tok/s", "cores": cb["cores"],
                                "kind": "oracle", "sample": cb[main_key]["sample"],
-                               "seconds": cb[main_key]["seconds"], "cpu": cb["cpu"]}
+                               "seconds": cb[main_key]["seconds"], "cpu": cb["cpu"],
+                               "threads": "cores = the BLAS thread count, used by the oracle's matrix "
+                                          "products (the projections); its per-query attention loop "
+                                          "and the sequential recurrence run on one thread"}
         if pre is not None and "decode" in cb:
             rec["cpu_baseline"]["decode"] = cb["decode"]
     print(json.dumps(rec), flush=True)

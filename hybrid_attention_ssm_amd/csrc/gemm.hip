@@ -336,12 +336,12 @@ struct InProjEpi {
   __device__ __forceinline__ Col<W> col_info(int col) const { return inproj_col<W, ROPE>(e, col); }
   template <int W>
   __device__ __forceinline__ void store(int row, const Col<W> &ci, const float v[W]) const {
-    inproj_storeW<T, W, ROPE>(e, row, ci, v);
+    inproj_storeW<T, W, ROPE>(e, e.row0 + row, ci, v);
   }
   template <int W>
   __device__ __forceinline__ void store_pair(int row, const Col<W> &ci0, const float va[W],
                                              const Col<W> &ci1, const float vb[W]) const {
-    inproj_store_pair<T, W, ROPE>(e, row, ci0, va, ci1, vb);
+    inproj_store_pair<T, W, ROPE>(e, e.row0 + row, ci0, va, ci1, vb);
   }
 };
 

@@ -10,6 +10,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "../../include/hh.h"
@@ -262,6 +263,66 @@ hh_status run_inproj(const Shape &s, const hh_weights *w, const void *x, int M,
   return err == hipSuccess ? HH_OK : hip_fail(err, "input projection");
 }
 
+// ---- the SSM branch beside the attention branch ---------------------------
+// A second stream per (host thread, device) with the default priority and
+// three ordering events, created on the first prefill that uses it and
+// destroyed when the thread ends.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t rows_a = nullptr, rows_b = nullptr, done = nullptr;
+  ~SideStream() {
+    if (rows_a) (void)hipEventDestroy(rows_a);
+    if (rows_b) (void)hipEventDestroy(rows_b);
+    if (done) (void)hipEventDestroy(done);
+    if (s) (void)hipStreamDestroy(s);
+  }
+};
+constexpr int kMaxSideDevices = 64;
+thread_local SideStream g_side[kMaxSideDevices];
+
+hh_status side_stream(SideStream **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxSideDevices)
+    return fail(HH_ERR_UNSUPPORTED, "device %d: side streams are kept for devices 0..%d", dev,
+                kMaxSideDevices - 1);
+  SideStream &ss = g_side[dev];
+  if (!ss.s) {
+    SideStream fresh;
+    if ((e = hipStreamCreateWithFlags(&fresh.s, hipStreamNonBlocking)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&fresh.rows_a, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&fresh.rows_b, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&fresh.done, hipEventDisableTiming)) != hipSuccess)
+      return hip_fail(e, "side stream set-up");
+    std::swap(ss.s, fresh.s);
+    std::swap(ss.rows_a, fresh.rows_a);
+    std::swap(ss.rows_b, fresh.rows_b);
+    std::swap(ss.done, fresh.done);
+  }
+  *out = &ss;
+  return HH_OK;
+}
+
+// The two branches run side by side only when HH_CONCURRENT_BRANCHES=1.  It
+// is off by default: measured on the 8k prefill, the scan's waves beside the
+// second half of the input projection slow that GEMM by about a quarter (the
+// two compete for LDS bandwidth and issue slots; raising the GEMM waves'
+// priority changed nothing), and beside the attention they slow it as much
+// as they gain, so the step takes 0.88 ms against 0.85 ms in one stream.
+bool concurrent_branches(const Shape &, long) {
+  const char *v = std::getenv("HH_CONCURRENT_BRANCHES");
+  return v && v[0] == '1';
+}
+
+// Prefill.  With the branches side by side (concurrent_branches), the input
+// projection runs in two row ranges on the caller's stream; the SSM branch's
+// chunk summaries (scan pass 1) of the first range start on the side stream as
+// soon as that range is projected and run beside the second range's
+// projection, whose matrix-core work leaves the vector ALUs mostly idle; the
+// rest of the scan runs beside the attention branch; the caller's stream
+// waits for it before the fusion.  Every kernel computes what it computes in
+// the single-stream order, so the results are the same bit for bit.
 template <class T>
 hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, int n,
                     const hh_meta *meta, int window, int is_global, void *out, hh_kv *kv,
@@ -286,20 +347,6 @@ hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, i
   e.bc = reinterpret_cast<float *>(at(ws, L.off[HH_WS_BC]));
   e.dt_bias = w->dt_bias;
   set_rope(e, s, 0);
-  hh_status r = run_inproj<T>(s, w, x, rows, e, part_ptr(ws, L.off[HH_WS_GEMM]), st);
-  if (r != HH_OK) return r;
-
-  hh::AttnArgs aa{};
-  aa.q = e.q; aa.k = kfull; aa.v = vfull; aa.mk = meta->k; aa.mv = meta->v;
-  aa.o = at(ws, L.off[HH_WS_O]);
-  aa.B = B; aa.n = n; aa.m = s.m; aa.H = s.H; aa.G = s.G; aa.hd = s.hd;
-  aa.window = window; aa.is_global = is_global;
-  hipError_t err;
-  {
-    Stage sg(st, "attention");
-    err = sg.run([&] { return hh::launch_attention<T>(aa, st); });
-  }
-  if (err != hipSuccess) return hip_fail(err, "attention");
 
   hh::ScanArgs sa{};
   sa.xs = e.xs; sa.z = e.z; sa.dt = e.dt; sa.bc = e.bc;
@@ -310,11 +357,83 @@ hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, i
   sa.tail_out = state ? state->conv : nullptr;
   sa.carry = reinterpret_cast<float *>(at(ws, L.off[HH_WS_SCAN]));
   sa.B = B; sa.n = n; sa.D = s.D; sa.N = s.N; sa.k = s.k; sa.S = s.S; sa.chunk = L.chunk;
-  {
-    Stage sg(st, "scan");
-    err = sg.run([&] { return hh::launch_scan<T>(sa, st); });
+
+  // the first row range: whole sequences when there are several, else the
+  // rows of the first half of the chunks that have summaries
+  SideStream *side = nullptr;
+  int rows_a = 0, ck_a = 0, b_a = 0;
+  const int nchunks = hh::scan_chunks(sa);
+  if (concurrent_branches(s, rows)) {
+    if (B >= 2) { b_a = B / 2; rows_a = b_a * n; }
+    else { ck_a = (nchunks - 1) / 2; rows_a = ck_a * L.chunk; }
+    if (rows_a > 0) {
+      hh_status r = side_stream(&side);
+      if (r != HH_OK) return r;
+    }
   }
-  if (err != hipSuccess) return hip_fail(err, "selective scan");
+  hipError_t err;
+  float *gemm_part = part_ptr(ws, L.off[HH_WS_GEMM]);
+  if (!side) {
+    hh_status r = run_inproj<T>(s, w, x, rows, e, gemm_part, st);
+    if (r != HH_OK) return r;
+  } else {
+    // the two row ranges (one GEMM each) on the caller's stream, an event after each
+    {
+      Stage sg(st, "inproj");
+      err = sg.run([&] {
+        hipError_t q = hh::launch_inproj<T>(static_cast<const T *>(x), rows_a, s.d,
+                                            static_cast<const T *>(w->w_in), s.n_in, e, gemm_part, st);
+        if (q == hipSuccess) q = hipEventRecord(side->rows_a, st);
+        hh::InProjOut eb = e;
+        eb.row0 = rows_a;
+        if (q == hipSuccess)
+          q = hh::launch_inproj<T>(static_cast<const T *>(x) + (size_t)rows_a * s.d, rows - rows_a, s.d,
+                                   static_cast<const T *>(w->w_in), s.n_in, eb, gemm_part, st);
+        if (q == hipSuccess) q = hipEventRecord(side->rows_b, st);
+        return q;
+      });
+    }
+    if (err != hipSuccess) return hip_fail(err, "input projection");
+    // the SSM branch on the side stream
+    {
+      Stage sg(side->s, "scan");
+      err = sg.run([&] {
+        hipError_t q = hipStreamWaitEvent(side->s, side->rows_a, 0);
+        if (q == hipSuccess)
+          q = B >= 2 ? hh::launch_scan_summaries<T>(sa, 0, nchunks, 0, b_a, side->s)
+                     : hh::launch_scan_summaries<T>(sa, 0, ck_a, 0, 1, side->s);
+        if (q == hipSuccess) q = hipStreamWaitEvent(side->s, side->rows_b, 0);
+        if (q == hipSuccess)
+          q = B >= 2 ? hh::launch_scan_summaries<T>(sa, 0, nchunks, b_a, B, side->s)
+                     : hh::launch_scan_summaries<T>(sa, ck_a, nchunks, 0, 1, side->s);
+        if (q == hipSuccess) q = hh::launch_scan_finish<T>(sa, side->s);
+        if (q == hipSuccess) q = hipEventRecord(side->done, side->s);
+        return q;
+      });
+    }
+    if (err != hipSuccess) return hip_fail(err, "selective scan");
+  }
+
+  hh::AttnArgs aa{};
+  aa.q = e.q; aa.k = kfull; aa.v = vfull; aa.mk = meta->k; aa.mv = meta->v;
+  aa.o = at(ws, L.off[HH_WS_O]);
+  aa.B = B; aa.n = n; aa.m = s.m; aa.H = s.H; aa.G = s.G; aa.hd = s.hd;
+  aa.window = window; aa.is_global = is_global;
+  {
+    Stage sg(st, "attention");
+    err = sg.run([&] { return hh::launch_attention<T>(aa, st); });
+  }
+  if (err != hipSuccess) return hip_fail(err, "attention");
+
+  if (!side) {
+    {
+      Stage sg(st, "scan");
+      err = sg.run([&] { return hh::launch_scan<T>(sa, st); });
+    }
+    if (err != hipSuccess) return hip_fail(err, "selective scan");
+  } else if ((err = hipStreamWaitEvent(st, side->done, 0)) != hipSuccess) {
+    return hip_fail(err, "joining the SSM branch");
+  }
 
   hh::NormArgs na{};
   na.o = aa.o; na.y = sa.y; na.beta_attn = w->beta_attn; na.beta_ssm = w->beta_ssm;
@@ -334,7 +453,7 @@ hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, i
     err = sg.run([&] {
       return hh::launch_outproj<T>(static_cast<const T *>(na.f), rows, s.Wa + s.D,
                                    static_cast<const T *>(w->w_out), s.d, static_cast<T *>(out),
-                                   static_cast<const T *>(resid), part_ptr(ws, L.off[HH_WS_GEMM]), st);
+                                   static_cast<const T *>(resid), gemm_part, st);
     });
   }
   if (err != hipSuccess) return hip_fail(err, "output projection");

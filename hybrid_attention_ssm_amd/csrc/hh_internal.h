@@ -68,6 +68,7 @@ enum EpiMode : int { EPI_PREFILL = 0, EPI_DECODE = 1, EPI_META = 2 };
 
 struct InProjOut {
   int mode;
+  int row0;                   // global row of the GEMM's first row (a launch over a row range)
   int Wa, KV, D, N, hd, n_rows_per_seq;  // n_rows_per_seq: seqlen (prefill) or m (meta)
   int Ddt;                    // dt block width: D, or the Mamba2 head count
   void *q;                    // [rows, Wa]
@@ -447,8 +448,17 @@ struct ScanArgs {
   int B, n, D, N, k;
   int chunk;               // time steps per chunk
   int S;                   // Mamba2 heads (per-head Delta, scalar A); 0: Mamba
+  int ck0, b0;             // pass 1: chunk and sequence of the grid's first workgroup
 };
 template <class T> hipError_t launch_scan(const ScanArgs &a, hipStream_t s);
+// The scan in two parts, for a caller that overlaps the first with other
+// work: launch_scan_summaries runs pass 1 over chunks [ck0, ck1) of sequences
+// [b0, b1) (the chunk summaries; chunks from nc - 1 on have none);
+// launch_scan_finish runs pass 2 and pass 3 once every summary is written.
+template <class T>
+hipError_t launch_scan_summaries(const ScanArgs &a, int ck0, int ck1, int b0, int b1, hipStream_t s);
+template <class T> hipError_t launch_scan_finish(const ScanArgs &a, hipStream_t s);
+int scan_chunks(const ScanArgs &a);
 size_t scan_carry_bytes(int B, int n, int D, int N, int *chunk_out);
 
 struct NormArgs {

@@ -203,7 +203,7 @@ __device__ __forceinline__ void scan_range(const ScanArgs &a, int b, int c, bool
 // pass 1: summaries of chunks 0..C-2.  grid (C-1, ceil(D/64), B), 64 threads
 template <class T, bool SC>
 __global__ void __launch_bounds__(64) scan_pass1(ScanArgs a) {
-  const int ck = blockIdx.x, b = blockIdx.z;
+  const int ck = a.ck0 + (int)blockIdx.x, b = a.b0 + (int)blockIdx.z;
   // lanes past the last channel compute a copy of it (every lane takes part
   // in staging B/C) and store nothing
   const bool active = blockIdx.y * 64 + (int)threadIdx.x < a.D;
@@ -350,12 +350,26 @@ size_t scan_carry_bytes(int B, int n, int D, int N, int *chunk_out) {
   return (size_t)B * nc * (N + 1) * D * sizeof(float);
 }
 
+int scan_chunks(const ScanArgs &a) { return (a.n + a.chunk - 1) / a.chunk; }
+
 template <class T, bool SC>
-static hipError_t launch_scan_t(const ScanArgs &a, hipStream_t s) {
-  const int nc = (a.n + a.chunk - 1) / a.chunk;
+static hipError_t launch_summaries_t(const ScanArgs &a0, int ck0, int ck1, int b0, int b1, hipStream_t s) {
+  const int nc = scan_chunks(a0);
+  ck1 = std::min(ck1, nc - 1);
+  if (ck0 >= ck1 || b0 >= b1) return hipSuccess;
+  ScanArgs a = a0;
+  a.ck0 = ck0;
+  a.b0 = b0;
+  const int cw = (a.D + 63) / 64;
+  hipLaunchKernelGGL((scan_pass1<T, SC>), dim3(ck1 - ck0, cw, b1 - b0), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+template <class T, bool SC>
+static hipError_t launch_finish_t(const ScanArgs &a, hipStream_t s) {
+  const int nc = scan_chunks(a);
   const int cw = (a.D + 63) / 64;
   if (nc > 1) {
-    hipLaunchKernelGGL((scan_pass1<T, SC>), dim3(nc - 1, cw, a.B), dim3(64), 0, s, a);
     // lanes per (channel, state) group: the fewest whose runs hold every carry
     const int ncar = nc - 1;
     const int g2 = ncar <= 4 * P2_RUN ? 4 : ncar <= 16 * P2_RUN ? 16 : ncar <= 64 * P2_RUN ? 64 : 0;
@@ -370,10 +384,26 @@ static hipError_t launch_scan_t(const ScanArgs &a, hipStream_t s) {
 }
 
 template <class T>
-hipError_t launch_scan(const ScanArgs &a, hipStream_t s) {
-  return a.S ? launch_scan_t<T, true>(a, s) : launch_scan_t<T, false>(a, s);
+hipError_t launch_scan_summaries(const ScanArgs &a, int ck0, int ck1, int b0, int b1, hipStream_t s) {
+  return a.S ? launch_summaries_t<T, true>(a, ck0, ck1, b0, b1, s)
+             : launch_summaries_t<T, false>(a, ck0, ck1, b0, b1, s);
 }
 
+template <class T>
+hipError_t launch_scan_finish(const ScanArgs &a, hipStream_t s) {
+  return a.S ? launch_finish_t<T, true>(a, s) : launch_finish_t<T, false>(a, s);
+}
+
+template <class T>
+hipError_t launch_scan(const ScanArgs &a, hipStream_t s) {
+  hipError_t e = launch_scan_summaries<T>(a, 0, scan_chunks(a), 0, a.B, s);
+  return e == hipSuccess ? launch_scan_finish<T>(a, s) : e;
+}
+
+template hipError_t launch_scan_summaries<float>(const ScanArgs &, int, int, int, int, hipStream_t);
+template hipError_t launch_scan_summaries<bf16>(const ScanArgs &, int, int, int, int, hipStream_t);
+template hipError_t launch_scan_finish<float>(const ScanArgs &, hipStream_t);
+template hipError_t launch_scan_finish<bf16>(const ScanArgs &, hipStream_t);
 template hipError_t launch_scan<float>(const ScanArgs &, hipStream_t);
 template hipError_t launch_scan<bf16>(const ScanArgs &, hipStream_t);
 
