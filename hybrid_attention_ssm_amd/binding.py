@@ -23,7 +23,7 @@ LIB_PATH = os.environ.get("HH_LIB_PATH") or os.path.join(os.path.dirname(os.path
                                                          "libhymba_hh.so")
 
 HH_F32, HH_BF16 = 0, 1
-HH_WS = ["Q", "K", "V", "XS", "Z", "DELTA", "BC", "O", "Y", "F", "SCAN", "GEMM"]
+HH_WS = ["Q", "K", "V", "XS", "Z", "DELTA", "BC", "O", "Y", "F", "SCAN", "GEMM", "SSQ"]
 STATUS = {0: "HH_OK", 1: "HH_ERR_INVALID_ARG", 2: "HH_ERR_UNSUPPORTED",
           3: "HH_ERR_WORKSPACE", 4: "HH_ERR_HIP"}
 _vp = ctypes.c_void_p

@@ -75,6 +75,8 @@ attn_prefill_bf16(AttnArgs a) {
   // DMA into another, so the compiler waits only for the tile being read
   __shared__ uint4 sK0[TILE_UNITS], sK1[TILE_UNITS], sK2[TILE_UNITS];
   __shared__ uint4 sV0[TILE_UNITS], sV1[TILE_UNITS], sV2[TILE_UNITS];
+  __shared__ float sq_part[NW][32];   // fused norm: each head's O^2 sums per query
+  __shared__ float sbeta[NW * HD];     // fused norm: the group's betas
   static_assert(ASTAGES == 3, "three stage arrays");
 
   const int nqt = (a.n + BQ - 1) / BQ;
@@ -267,6 +269,9 @@ attn_prefill_bf16(AttnArgs a) {
   const int tlast = n_tiles - 1;
   issue(0, sK0, sV0);
   issue(min(1, tlast), sK1, sV1);
+  // the group's betas, read by the epilogue (after a barrier)
+  if (a.beta)
+    for (int i = tid; i < NW * HD; i += NW * 64) sbeta[i] = a.beta[g * NW * HD + i];
   // tile t lives in stage t % 3; each step waits for its own tile, then (after
   // the barrier frees the stage read one step earlier) issues tile t + 2
 #define HH_ATTN_STEP(KC, VC, KN, VN)                                    \
@@ -284,6 +289,11 @@ attn_prefill_bf16(AttnArgs a) {
 #undef HH_ATTN_STEP
   wait_vmcnt<0>();   // the repeated last prefetches, before the workgroup ends
 
+  // lane (lr, lh) holds dims 32dblk + 8j + 4lh + e of query lr.  Under the
+  // fused norm the stored value is beta * O and the sum of the unscaled O^2
+  // over the group's heads goes to ssq (the row statistics of Eq. (3)).
+  float sq = 0.0f;
+  if (a.beta) __syncthreads();   // sbeta written
   if (qpos < a.n) {
     const float inv = 1.0f / l_run;
     bf16 *O = reinterpret_cast<bf16 *>(a.o) + ((size_t)b * a.n + qpos) * Wa + h * HD;
@@ -291,12 +301,35 @@ attn_prefill_bf16(AttnArgs a) {
     for (int dblk = 0; dblk < 2; ++dblk)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        const int d = dblk * 32 + 8 * j + 4 * lh;
+        float bt[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+        if (a.beta) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bt[e] = sbeta[wave * HD + d + e];
+        }
         bf16x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (bf16)(o[dblk][4 * j + e] * inv);
-        *reinterpret_cast<bf16x4 *>(O + dblk * 32 + 8 * j + 4 * lh) = w;
+        for (int e = 0; e < 4; ++e) {
+          const float v = o[dblk][4 * j + e] * inv;
+          sq = fmaf(v, v, sq);
+          w[e] = (bf16)(bt[e] * v);
+        }
+        *reinterpret_cast<bf16x4 *>(O + d) = w;
       }
   }
+  if (a.ssq) {
+    sq = wave_sum32(sq, lh == 0);   // both halves of the query's dims
+    if (lh == 0) sq_part[wave][lr] = sq;
+    __syncthreads();
+    if (wave == 0 && lh == 0 && qpos < a.n) {
+      float t = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) t += sq_part[w][lr];
+      a.ssq[((size_t)b * a.n + qpos) * a.G + g] = t;
+    }
+  }
+  if (a.set_len && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+    for (int i = tid; i < a.set_len_n; i += NW * 64) a.set_len[i] = a.set_len_value;
 #endif
 }
 

@@ -89,9 +89,16 @@ struct LdsCfg {
   }
 };
 
-template <class Cfg, class Epi>
+// FUSED (the output projection under the fused norm, see NormScale): A is
+// [M, ns.Wa] with K = ns.Wa + ns.D, its columns continued by ns.y [M, ns.D];
+// the k-tiles of the y part run first, then the accumulators are rescaled by
+// s_y / s_o, then the o part, then the accumulators are multiplied by s_o.
+// Rows of a lane's A fragments are lr (A layout); accumulator element r of
+// a 32x32 block belongs to row 8(r/4) + 4lh + r%4 (C layout).
+template <class Cfg, class Epi, bool FUSED = false>
 __global__ void __launch_bounds__(Cfg::NT)
-gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int N, int K, Epi epi) {
+gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int N, int K, Epi epi,
+              NormScale ns) {
   // the body uses LDS-DMA builtins that exist only for the device target; the
   // host pass needs just the launch stub
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -105,18 +112,24 @@ gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int
   const int lr = lane & 31, lh = lane >> 5;
 
   // buffers based at the tile's first row; rows past M (N) read as zero
+  const int lda = FUSED ? ns.Wa : K;
   const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(A + (size_t)m0 * K), (short)0, (M - m0) * K * 2, 0x00020000);
+      (void *)(A + (size_t)m0 * lda), (short)0, (M - m0) * lda * 2, 0x00020000);
+  __amdgpu_buffer_rsrc_t rsY = rsA;
+  if constexpr (FUSED)
+    rsY = __builtin_amdgcn_make_buffer_rsrc((void *)(static_cast<const bf16 *>(ns.y) + (size_t)m0 * ns.D),
+                                            (short)0, (M - m0) * ns.D * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(B + (size_t)n0 * K), (short)0, (N - n0) * K * 2, 0x00020000);
-  int voffA[Cfg::A_INS], voffB[Cfg::B_INS];
+  int voffA[Cfg::A_INS], voffB[Cfg::B_INS], voffY[FUSED ? Cfg::A_INS : 1];
   auto qA = [&](int j) { return (wave * Cfg::A_INS + j) % Cfg::A_Q; };   // instruction of the stage
   auto qB = [&](int j) { return (wave * Cfg::B_INS + j) % Cfg::B_Q; };
 #pragma unroll
   for (int j = 0; j < Cfg::A_INS; ++j) {   // LDS unit u holds chunk of swz(row, kc) == u
     const int u = qA(j) * 64 + lane;
     const int row = u / Cfg::KCH, kc = Cfg::swz(row, u % Cfg::KCH) - row * Cfg::KCH;
-    voffA[j] = (row * K + kc * 8) * 2;
+    voffA[j] = (row * lda + kc * 8) * 2;
+    if constexpr (FUSED) voffY[j] = (row * ns.D + kc * 8) * 2;
   }
 #pragma unroll
   for (int j = 0; j < Cfg::B_INS; ++j) {
@@ -128,10 +141,17 @@ gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int
   auto issue = [&](int kt, int st) {
     const int soff = kt * Cfg::BK * 2;
     uint4 *base = smem + st * Cfg::STAGE;
+    if (FUSED && kt * Cfg::BK >= ns.Wa) {   // a k-tile of the y part
 #pragma unroll
-    for (int j = 0; j < Cfg::A_INS; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsA, (lds_void *)(base + qA(j) * 64), 16, voffA[j], soff, 0, 0);
+      for (int j = 0; j < Cfg::A_INS; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsY, (lds_void *)(base + qA(j) * 64), 16, voffY[FUSED ? j : 0], soff - ns.Wa * 2, 0, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < Cfg::A_INS; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsA, (lds_void *)(base + qA(j) * 64), 16, voffA[j], soff, 0, 0);
+    }
 #pragma unroll
     for (int j = 0; j < Cfg::B_INS; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -171,7 +191,56 @@ gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int
   const int kps = (ktiles_all + gridDim.y - 1) / gridDim.y;
   const int kt0 = blockIdx.y * kps;
   const int ktiles = max(0, min(ktiles_all - kt0, kps));
-  auto ktile = [&](int i) { return kt0 + min(i, ktiles - 1); };   // steps past the end repeat the last
+  // steps past the end repeat the last; FUSED starts at the y part's first k-tile
+  const int n_y = FUSED ? ns.D / Cfg::BK : 0, n_o = FUSED ? ns.Wa / Cfg::BK : 0;
+  auto ktile = [&](int i) {
+    const int t = min(i, ktiles - 1);
+    return FUSED ? (t < n_y ? n_o + t : t - n_y) : kt0 + t;
+  };
+  // FUSED: each lane's row scales s_o, s_y (A layout), from the partial sums
+  // of squares: lane half lh = 0 adds the o partials and the first half of
+  // the y partials, lh = 1 the rest
+  float rso[Cfg::TM], rsy[Cfg::TM];
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int i = 0; i < Cfg::TM; ++i) {
+      const int row = m0 + wm * Cfg::WM + i * 32 + lr;
+      float po = 0.0f, py = 0.0f;
+      // PCH loads in flight at a time, then their sum
+      constexpr int PCH = 16;
+      auto add_run = [&](const float *p, int cnt, float &acc) {
+        for (int g0 = 0; g0 < cnt; g0 += PCH) {
+          float v[PCH];
+#pragma unroll
+          for (int j = 0; j < PCH; ++j) v[j] = g0 + j < cnt ? p[g0 + j] : 0.0f;
+#pragma unroll
+          for (int j = 0; j < PCH; ++j) acc += v[j];
+        }
+      };
+      if (row < M) {
+        if (lh == 0) add_run(ns.ssq_o + (size_t)row * ns.go, ns.go, po);
+        const int half = ns.gy / 2;
+        const int y0 = lh == 0 ? 0 : half, y1 = lh == 0 ? half : ns.gy;
+        add_run(ns.ssq_y + (size_t)row * ns.gy + y0, y1 - y0, py);
+      }
+      const float qo = __shfl_xor(po, 32), qy = __shfl_xor(py, 32);
+      po = lh == 0 ? po + qo : qo + po;   // the same order in both halves
+      py = lh == 0 ? py + qy : qy + py;
+      rso[i] = 0.5f / sqrtf(po / (float)ns.Wa + ns.eps);
+      rsy[i] = 0.5f / sqrtf(py / (float)ns.D + ns.eps);
+    }
+  }
+  // multiply accumulator rows by v (given in the A layout)
+  auto scale_rows = [&](const float (&v)[Cfg::TM]) {
+#pragma unroll
+    for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float f = __shfl(v[i], 8 * (r >> 2) + 4 * lh + (r & 3));
+#pragma unroll
+        for (int j = 0; j < Cfg::TN; ++j) acc[i][j][r] *= f;
+      }
+  };
   auto stage = [&](int kt) { return smem + (kt % Cfg::STAGES) * Cfg::STAGE; };
   constexpr int PER_TILE = Cfg::A_INS + Cfg::B_INS;
   // Software pipeline per k-tile kt (its stage holds tile kt): each k-step's
@@ -188,6 +257,14 @@ gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int
   fload(stage(0), 0);
   for (int kt = 0; kt < ktiles; ++kt) {
     const uint4 *sA = stage(kt);
+    if constexpr (FUSED) {
+      if (kt == n_y) {   // the y part is done: acc = s_y/s_o * (beta_y Y) W_y^T
+        float ratio[Cfg::TM];
+#pragma unroll
+        for (int i = 0; i < Cfg::TM; ++i) ratio[i] = rsy[i] / rso[i];
+        scale_rows(ratio);
+      }
+    }
 #pragma unroll
     for (int ks = 0; ks < Cfg::KS; ++ks) {
       if (ks + 1 < Cfg::KS) fload(sA, ks + 1);
@@ -205,6 +282,7 @@ gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int
   }
   wait_vmcnt<0>();
   __syncthreads();
+  if constexpr (FUSED) scale_rows(rso);
 
   // the wave's WN columns are staged CW at a time (all of them when WN <= 64)
   constexpr int CW = Cfg::WN % 64 == 0 ? 64 : 32;
@@ -436,7 +514,7 @@ static hipError_t run_lds(const bf16 *A, int M, int K, const bf16 *B, int N, con
   const int tiles = ((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
   const int grid = (tiles + 7) / 8 * 8;
   hipLaunchKernelGGL((gemm_bf16_lds<Cfg, Epi>), dim3(grid), dim3(Cfg::NT), 0, s, A, B, M, N, K,
-                     epi);
+                     epi, NormScale{});
   return hipGetLastError();
 }
 
@@ -476,12 +554,12 @@ static hipError_t run_skinny_cfg(const bf16 *A, int M, int K, const bf16 *B, int
   const int grid = (tiles + 7) / 8 * 8;
   if (splits == 1) {
     hipLaunchKernelGGL((gemm_bf16_lds<Cfg, Epi>), dim3(grid), dim3(Cfg::NT), 0, s, A, B, M, N, K,
-                       epi);
+                       epi, NormScale{});
     return hipGetLastError();
   }
   PartialEpi pe{part, M, N};
   hipLaunchKernelGGL((gemm_bf16_lds<Cfg, PartialEpi>), dim3(grid, splits), dim3(Cfg::NT), 0, s, A,
-                     B, M, N, K, pe);
+                     B, M, N, K, pe, NormScale{});
   const long groups = (long)M * (N / 4);
   hipLaunchKernelGGL((reduce_splits<Epi>), dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s,
                      part, splits, M, N, epi);
@@ -502,17 +580,55 @@ static long tile_cost(int M, int N, int cus) {
   return (tiles + cus - 1) / cus * (long)Cfg::BM * Cfg::BN;
 }
 
+// the wide tile reads more LDS per flop: only where it saves a tenth
+static bool use_wide(int M, int N) {
+  const int cus = device_cus();
+  return 10 * tile_cost<CfgWide>(M, N, cus) < 9 * tile_cost<CfgLds>(M, N, cus);
+}
+
 template <class Epi>
 static hipError_t run_bf16_auto(const bf16 *A, int M, int K, const bf16 *B, int N, const Epi &epi,
                                 float *part, hipStream_t s) {
   if (M >= 1024) {
-    const int cus = device_cus();
-    // the wide tile reads more LDS per flop: only where it saves a tenth
-    if (10 * tile_cost<CfgWide>(M, N, cus) < 9 * tile_cost<CfgLds>(M, N, cus))
-      return run_lds<CfgWide>(A, M, K, B, N, epi, s);
+    if (use_wide(M, N)) return run_lds<CfgWide>(A, M, K, B, N, epi, s);
     return run_lds<CfgLds>(A, M, K, B, N, epi, s);
   }
   return run_skinny(A, M, K, B, N, epi, part, s);
+}
+
+template <class Cfg, class Epi>
+static hipError_t run_fused(const bf16 *o, const NormScale &ns, int M, const bf16 *w, int N,
+                            const Epi &epi, hipStream_t s) {
+  const int tiles = ((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
+  const int grid = (tiles + 7) / 8 * 8;
+  hipLaunchKernelGGL((gemm_bf16_lds<Cfg, Epi, true>), dim3(grid), dim3(Cfg::NT), 0, s, o, w, M, N,
+                     ns.Wa + ns.D, epi, ns);
+  return hipGetLastError();
+}
+
+template <class Epi>
+static hipError_t run_fused_auto(const bf16 *o, const NormScale &ns, int M, const bf16 *w, int N,
+                                 const Epi &epi, hipStream_t s) {
+  if (use_wide(M, N)) return run_fused<CfgWide>(o, ns, M, w, N, epi, s);
+  return run_fused<CfgLds>(o, ns, M, w, N, epi, s);
+}
+
+bool outproj_fused_ok(int M, int Wa, int D) {
+  static_assert(CfgWide::BK == CfgLds::BK, "one k-tile depth");
+  return M >= 1024 && Wa > 0 && D > 0 && Wa % CfgLds::BK == 0 && D % CfgLds::BK == 0;
+}
+
+template <>
+hipError_t launch_outproj_fused<bf16>(const bf16 *o, const NormScale &ns, int M, const bf16 *w, int Ncols,
+                                      bf16 *out, const bf16 *resid, hipStream_t s) {
+  if (!outproj_fused_ok(M, ns.Wa, ns.D)) return hipErrorInvalidValue;
+  if (resid) return run_fused_auto(o, ns, M, w, Ncols, ResidEpi<bf16>{out, resid, Ncols}, s);
+  return run_fused_auto(o, ns, M, w, Ncols, StoreEpi<bf16>{out, Ncols}, s);
+}
+template <>
+hipError_t launch_outproj_fused<float>(const float *, const NormScale &, int, const float *, int, float *,
+                                       const float *, hipStream_t) {
+  return hipErrorInvalidValue;   // the fp32 path keeps the separate norm kernel
 }
 
 size_t skinny_part_bytes(int M, int K, int N) {

@@ -209,6 +209,7 @@ PrefillLayout prefill_layout(const Shape &s, int B, int n) {
   take(HH_WS_Y, T * s.D * s.es);
   take(HH_WS_F, T * (s.Wa + s.D) * s.es);
   take(HH_WS_SCAN, hh::scan_carry_bytes(B, n, s.D, s.N, &L.chunk));
+  take(HH_WS_SSQ, T * (s.G + (s.D + 63) / 64) * 4);
   const size_t gp = s.dtype == HH_BF16
                         ? std::max(hh::skinny_part_bytes((int)T, s.d, s.n_in),
                                    hh::skinny_part_bytes((int)T, s.Wa + s.D, s.d))
@@ -315,6 +316,17 @@ bool concurrent_branches(const Shape &, long) {
   return v && v[0] == '1';
 }
 
+// The fusion of Eq. (3) inside the output projection (bf16, many rows): the
+// branches store beta-scaled outputs and per-row sums of squares, and the
+// GEMM applies the row scales to its accumulators, so no normalised copy of
+// the features is written or read.  HH_FUSED_NORM=0 selects the separate
+// norm kernel instead (same result up to where the bf16 roundings fall).
+bool fused_norm(const Shape &s, int rows) {
+  const char *v = std::getenv("HH_FUSED_NORM");
+  if (v && v[0] == '0') return false;
+  return s.dtype == HH_BF16 && hh::outproj_fused_ok(rows, s.Wa, s.D);
+}
+
 // Prefill.  With the branches side by side (concurrent_branches), the input
 // projection runs in two row ranges on the caller's stream; the SSM branch's
 // chunk summaries (scan pass 1) of the first range start on the side stream as
@@ -357,6 +369,10 @@ hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, i
   sa.tail_out = state ? state->conv : nullptr;
   sa.carry = reinterpret_cast<float *>(at(ws, L.off[HH_WS_SCAN]));
   sa.B = B; sa.n = n; sa.D = s.D; sa.N = s.N; sa.k = s.k; sa.S = s.S; sa.chunk = L.chunk;
+  const bool fused = fused_norm(s, rows);
+  float *ssq_o = reinterpret_cast<float *>(at(ws, L.off[HH_WS_SSQ]));
+  float *ssq_y = ssq_o + (size_t)rows * s.G;
+  if (fused) { sa.beta = w->beta_ssm; sa.ssq = ssq_y; }
 
   // the first row range: whole sequences when there are several, else the
   // rows of the first half of the chunks that have summaries
@@ -419,6 +435,11 @@ hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, i
   aa.o = at(ws, L.off[HH_WS_O]);
   aa.B = B; aa.n = n; aa.m = s.m; aa.H = s.H; aa.G = s.G; aa.hd = s.hd;
   aa.window = window; aa.is_global = is_global;
+  const bool set_len = prod && kv && kv->len;   // the cache now holds the prompt's n positions
+  if (fused) {
+    aa.beta = w->beta_attn; aa.ssq = ssq_o;
+    if (set_len) { aa.set_len = kv->len; aa.set_len_n = B; aa.set_len_value = n; }
+  }
   {
     Stage sg(st, "attention");
     err = sg.run([&] { return hh::launch_attention<T>(aa, st); });
@@ -435,13 +456,23 @@ hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, i
     return hip_fail(err, "joining the SSM branch");
   }
 
+  if (fused) {
+    const hh::NormScale ns{sa.y, ssq_o, ssq_y, s.Wa, s.D, s.G, (s.D + 63) / 64, s.eps};
+    Stage sg(st, "outproj");
+    err = sg.run([&] {
+      return hh::launch_outproj_fused<T>(static_cast<const T *>(aa.o), ns, rows,
+                                         static_cast<const T *>(w->w_out), s.d, static_cast<T *>(out),
+                                         static_cast<const T *>(resid), st);
+    });
+    if (err != hipSuccess) return hip_fail(err, "output projection");
+    return HH_OK;
+  }
+
   hh::NormArgs na{};
   na.o = aa.o; na.y = sa.y; na.beta_attn = w->beta_attn; na.beta_ssm = w->beta_ssm;
   na.f = at(ws, L.off[HH_WS_F]);
   na.rows = rows; na.Wa = s.Wa; na.D = s.D; na.eps = s.eps;
-  if (prod && kv && kv->len) {   // the cache now holds the prompt's n positions
-    na.set_len = kv->len; na.set_len_n = B; na.set_len_value = n;
-  }
+  if (set_len) { na.set_len = kv->len; na.set_len_n = B; na.set_len_value = n; }
   {
     Stage sg(st, "norm");
     err = sg.run([&] { return hh::launch_norm_fuse<T>(na, st); });

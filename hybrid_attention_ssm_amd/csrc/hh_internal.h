@@ -417,6 +417,29 @@ hipError_t launch_outproj(const T *f, int M, int K, const T *w, int Ncols, T *ou
 template <class T>
 hipError_t launch_mlp_gate_up(const T *x, int M, int K, const T *w, int Ncols, T *h,
                               float *part, hipStream_t s);
+// The fusion of Eq. (3) folded into the output projection (bf16, many rows):
+// the attention and SSM branches store beta-scaled outputs and per-row sums of
+// squares of the unscaled ones (ssq_o: G partials per row, one per KV group;
+// ssq_y: one per 64-channel block), and
+//   out[r] = s_o(r) (beta_a O)[r] W_a^T + s_y(r) (beta_y Y)[r] W_y^T,
+//   s(r) = 1 / (2 sqrt(mean of squares + eps)),
+// W = [W_a | W_y] the output-projection rows split at column Wa.  The GEMM
+// walks the Y columns first, rescales its accumulators by s_y / s_o, walks
+// the O columns and multiplies by s_o before the epilogue.
+struct NormScale {
+  const void *y;           // [M, D] beta_y Y (the A operand's columns Wa..Wa+D)
+  const float *ssq_o;      // [M, go]
+  const float *ssq_y;      // [M, gy]
+  int Wa, D, go, gy;
+  float eps;
+};
+// out = [o | y] w^T with the row scales of ns (+ resid); o is [M, Wa]
+template <class T>
+hipError_t launch_outproj_fused(const T *o, const NormScale &ns, int M, const T *w, int Ncols, T *out,
+                                const T *resid, hipStream_t s);
+// whether launch_outproj_fused takes this shape (bf16, many rows, Wa and D
+// whole k-tiles)
+bool outproj_fused_ok(int M, int Wa, int D);
 size_t skinny_part_bytes(int M, int K, int N);
 // compute units of the current device (256 if the query fails)
 int device_cus();
@@ -427,6 +450,14 @@ struct AttnArgs {
   const void *mk, *mv;     // meta keys [G, m, hd]
   void *o;                 // [B*n, H*hd]
   int B, n, m, H, G, hd, window, is_global;
+  // fused norm (bf16): o holds beta * O and ssq[row * G + g] the sum of the
+  // group's unscaled O^2 over its heads' columns; null: plain O
+  const float *beta;       // [H*hd]
+  float *ssq;              // [B*n, G]
+  // the producer's cache now holds the prompt: set_len[0..set_len_n) =
+  // set_len_value (written by the first workgroup); null: nothing
+  int32_t *set_len;
+  int set_len_n, set_len_value;
 };
 template <class T> hipError_t launch_attention(const AttnArgs &a, hipStream_t s);
 
@@ -449,6 +480,10 @@ struct ScanArgs {
   int chunk;               // time steps per chunk
   int S;                   // Mamba2 heads (per-head Delta, scalar A); 0: Mamba
   int ck0, b0;             // pass 1: chunk and sequence of the grid's first workgroup
+  // fused norm: y holds beta * Y and ssq[row * ceil(D/64) + c/64] the sum of
+  // unscaled Y^2 over the 64-channel block; null: plain Y
+  const float *beta;       // [D]
+  float *ssq;              // [B*n, ceil(D/64)]
 };
 template <class T> hipError_t launch_scan(const ScanArgs &a, hipStream_t s);
 // The scan in two parts, for a caller that overlaps the first with other

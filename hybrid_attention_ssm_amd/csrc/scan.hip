@@ -40,6 +40,7 @@ struct ChanParams {
   float A2[NS];             // A * log2(e) (Mamba2: A2[0] is the head's)
   float w[KC];              // conv taps, w[KC-1] multiplies the current row
   float bias;
+  float beta;               // fused norm: the channel's beta (else 1)
   int dcol;                 // Delta of this channel: its column
 };
 
@@ -60,6 +61,7 @@ __device__ __forceinline__ void load_params(const ScanArgs &a, int c, ChanParams
     p.w[j] = src >= 0 ? a.conv_w[(size_t)c * a.k + src] : 0.0f;
   }
   p.bias = a.conv_b[c];
+  p.beta = a.beta ? a.beta[c] : 1.0f;
 }
 
 // history: hist[0] = xs_{t0-1}, hist[1] = xs_{t0-2}, hist[2] = xs_{t0-3}
@@ -108,10 +110,19 @@ __device__ __forceinline__ float scan_step(const ChanParams &p, float h[NS], flo
 // TB steps at a time.
 constexpr int SUB = 64;
 
+// Fused norm (sq not null): each output step's unscaled Y^2 goes to row
+// (step % TB) of sq (TB x 65 floats, one column per lane).  After each batch
+// of TB steps (and after the block's last steps) lane l adds the 8 columns
+// 8(l%8).. of row l/8 and three DPP steps combine the 8 lanes of a row,
+// giving the row's sum over the wave's 64 channels.
+constexpr int SQ_LD = 65;
+static_assert(TB == 8, "one sq row per lane group of 8");
+
 template <class T, int MODE, bool SC>
 __device__ __forceinline__ void scan_range(const ScanArgs &a, int b, int c, bool active, int t0,
                                            int t1, const ChanParams &p, float h[NS],
-                                           float hist[KC - 1], float &dsum, float *sbc) {
+                                           float hist[KC - 1], float &dsum, float *sbc,
+                                           float *sq = nullptr) {
   const T *z = reinterpret_cast<const T *>(a.z);
   T *y = reinterpret_cast<T *>(a.y);
   const size_t D = a.D;
@@ -127,6 +138,26 @@ __device__ __forceinline__ void scan_range(const ScanArgs &a, int b, int c, bool
   const int lane = threadIdx.x;
   for (int s0 = t0; s0 < t1; s0 += SUB) {
     const int len = min(SUB, t1 - s0);
+    // Y of block step tt (the output: beta * Y; its square to sq row tt % TB)
+    auto emit = [&](int tt, float yv) {
+      if (active) y[(row0 + s0 + tt) * D + c] = from_f32<T>(p.beta * yv);
+      if (sq) sq[(tt % TB) * SQ_LD + lane] = active ? yv * yv : 0.0f;
+    };
+    // the row sums of block steps base .. base + rows - 1
+    auto flush = [&](int base, int rows) {
+      __builtin_amdgcn_wave_barrier();
+      const int r = lane >> 3, q = lane & 7;
+      float acc2 = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc2 += sq[r * SQ_LD + q * 8 + j];
+      // xor 1 and xor 2 inside each quad (quad_perm), then the mirrored lane
+      // of the same 8 (row_half_mirror: l <-> 7 - l, the other quad)
+      acc2 += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc2), 0xB1, 0xF, 0xF, false));
+      acc2 += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc2), 0x4E, 0xF, 0xF, false));
+      acc2 += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc2), 0x141, 0xF, 0xF, false));
+      if (q == 0 && r < rows) a.ssq[(row0 + s0 + base + r) * gridDim.y + blockIdx.y] = acc2;
+      __builtin_amdgcn_wave_barrier();
+    };
     __syncthreads();   // previous block's reads are done
     // all loads first, then the LDS writes (indices past the block repeat
     // its last vector, so every load is unconditional)
@@ -173,12 +204,13 @@ __device__ __forceinline__ void scan_range(const ScanArgs &a, int b, int c, bool
           }
         }
         const float acc = scan_step<MODE, SC>(p, h, hist, xv[i], dv[i], bv, cv, dsum);
-        if (MODE == 1 && y && active)
-          y[(row0 + s0 + t + i) * D + c] = from_f32<T>(acc * silu_f(to_f32(zv[i])));
+        if (MODE == 1 && y) emit(t + i, acc * silu_f(to_f32(zv[i])));
       }
+      if (MODE == 1 && y && sq) flush(t, TB);
 #pragma unroll
       for (int i = 0; i < TB; ++i) { xv[i] = xn[i]; dv[i] = dn[i]; zv[i] = zn[i]; }
     }
+    const int t_rest = t;
     for (; t < len; ++t) {
       const size_t idx = (size_t)(s0 + t) * 64;
       const float4 *bc4 = reinterpret_cast<const float4 *>(sbc + t * 2 * NS);
@@ -193,8 +225,9 @@ __device__ __forceinline__ void scan_range(const ScanArgs &a, int b, int c, bool
         }
       }
       const float acc = scan_step<MODE, SC>(p, h, hist, xs[idx], dtp[idx], bv, cv, dsum);
-      if (MODE == 1 && y && active) y[(row0 + s0 + t) * D + c] = from_f32<T>(acc * silu_f(to_f32(zp[idx])));
+      if (MODE == 1 && y) emit(t, acc * silu_f(to_f32(zp[idx])));
     }
+    if (MODE == 1 && y && sq && t_rest < len) flush(t_rest, len - t_rest);
   }
 }
 
@@ -320,7 +353,9 @@ __global__ void __launch_bounds__(64) scan_pass3(ScanArgs a) {
   }
   float dsum = 0.0f;
   __shared__ float4 sbc[SUB * 2 * NS / 4];
-  scan_range<T, 1, SC>(a, b, c, active, t0, t1, p, h, hist, dsum, reinterpret_cast<float *>(sbc));
+  __shared__ float sq[TB * SQ_LD];
+  scan_range<T, 1, SC>(a, b, c, active, t0, t1, p, h, hist, dsum, reinterpret_cast<float *>(sbc),
+                       a.ssq && a.y ? sq : nullptr);
   if (ck == nc - 1 && active) {
     if (a.h_out) {
       float *ho = a.h_out + ((size_t)b * a.D + c) * NS;

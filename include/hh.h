@@ -318,6 +318,10 @@ enum {
   HH_WS_F,       /* [B*n, H*hd + D] dtype fused features */
   HH_WS_SCAN,    /* scan chunk carries */
   HH_WS_GEMM,    /* split-K partial sums of the projections (few-row calls) */
+  HH_WS_SSQ,     /* [B*n, G + ceil(D/64)] fp32 row sums of squares of the
+                    branch outputs (bf16 prefill of 1024+ rows: the fusion
+                    runs inside the output projection, O and Y then hold
+                    beta-scaled values and F is not written) */
   HH_WS_COUNT
 };
 size_t hh_prefill_workspace_layout(const hh_dims *dims, int32_t batch,
