@@ -121,6 +121,13 @@ def lib() -> ctypes.CDLL:
         L.hh_block_decode_step.argtypes = [P(HHDims), P(HHBlockWeights), _vp, _i32, P(HHMeta),
                                            _i32, _i32, P(HHKV), P(HHSsmState), _vp, _vp,
                                            ctypes.c_size_t, _vp]
+        L.hh_stage_attn.restype = ctypes.c_int
+        L.hh_stage_attn.argtypes = [P(HHDims), _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]
+        L.hh_stage_ssm_workspace_size.restype = ctypes.c_size_t
+        L.hh_stage_ssm_workspace_size.argtypes = [P(HHDims), _i32, _i32]
+        L.hh_stage_ssm.restype = ctypes.c_int
+        L.hh_stage_ssm.argtypes = [P(HHDims), P(HHWeights), _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                   _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.hh_timing_enable.restype = ctypes.c_int
         L.hh_timing_enable.argtypes = [_i32]
         L.hh_timing_read.restype = _i32
@@ -323,6 +330,38 @@ def hh_prefill(layer: DeviceLayer, x: torch.Tensor, meta: HHMeta, window: int, i
         ctypes.byref(d), ctypes.byref(layer.struct), _ptr(x), B, n, ctypes.byref(meta),
         int(window), int(bool(is_global)), _ptr(out), ctypes.byref(kv) if kv is not None else None,
         ctypes.byref(st), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def hh_stage_attn(dims: LayerDims, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  meta_k: Optional[torch.Tensor], meta_v: Optional[torch.Tensor], window: int,
+                  is_global: bool, o: torch.Tensor, stream=None) -> None:
+    """hh_stage_attn: q [B, n, H*hd], k/v [B, G, n, hd], meta k/v [G, m, hd] -> o [B, n, H*hd]."""
+    B, n = q.shape[0], q.shape[1]
+    d = hh_dims(dims)
+    _check("hh_stage_attn", lib().hh_stage_attn(
+        ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(meta_k), _ptr(meta_v), B, n, int(window),
+        int(bool(is_global)), _ptr(o), _stream(stream)))
+
+
+def hh_stage_ssm_workspace_size(dims: LayerDims, batch: int, seqlen: int) -> int:
+    d = hh_dims(dims)
+    return lib().hh_stage_ssm_workspace_size(ctypes.byref(d), batch, seqlen)
+
+
+def hh_stage_ssm(layer: DeviceLayer, xs: torch.Tensor, z: torch.Tensor, delta: torch.Tensor,
+                 bc: torch.Tensor, h0: Optional[torch.Tensor], conv_tail: Optional[torch.Tensor],
+                 batch: int, seqlen: int, y: Optional[torch.Tensor], h_out: Optional[torch.Tensor],
+                 tail_out: Optional[torch.Tensor], ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    """hh_stage_ssm: xs/z/delta in the channel-block-major layout, bc [B*n, 2N] ->
+    y [B*n, D], h_out [B, D, N], tail_out [B, k-1, D]."""
+    need = hh_stage_ssm_workspace_size(layer.dims, batch, seqlen)
+    if ws is None:
+        ws = _default_ws.get(need, xs.device)
+    d = hh_dims(layer.dims)
+    _check("hh_stage_ssm", lib().hh_stage_ssm(
+        ctypes.byref(d), ctypes.byref(layer.struct), _ptr(xs), _ptr(z), _ptr(delta), _ptr(bc), _ptr(h0),
+        _ptr(conv_tail), batch, seqlen, _ptr(y), _ptr(h_out), _ptr(tail_out), _ptr(ws), ws.numel(),
+        _stream(stream)))
 
 
 def hh_decode_step(layer: DeviceLayer, x_t: torch.Tensor, meta: HHMeta, window: int,

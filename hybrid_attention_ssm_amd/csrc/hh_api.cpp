@@ -905,6 +905,67 @@ hh_status hh_prefill(const hh_dims *dims, const hh_weights *w, const void *x, in
              : prefill_t<float>(s, w, x, batch, seqlen, meta, window, is_global, out, kv, state, ws, L, st);
 }
 
+size_t hh_stage_ssm_workspace_size(const hh_dims *dims, int32_t batch, int32_t seqlen) {
+  Shape s;
+  if (check_dims(dims, 1, s) != HH_OK || batch <= 0 || seqlen <= 0) return 0;
+  return hh::scan_carry_bytes(batch, seqlen, s.D, s.N, nullptr);
+}
+
+hh_status hh_stage_attn(const hh_dims *dims, const void *q, const void *k, const void *v,
+                        const void *meta_k, const void *meta_v, int32_t batch, int32_t seqlen,
+                        int32_t window, int32_t is_global, void *o, void *stream) {
+  Shape s;
+  hh_status r = check_dims(dims, 1, s);
+  if (r != HH_OK) return r;
+  if (batch <= 0 || seqlen <= 0) return fail(HH_ERR_INVALID_ARG, "batch and seqlen must be positive");
+  if ((long long)batch * seqlen > (1LL << 30)) return fail(HH_ERR_UNSUPPORTED, "batch*seqlen above 2^30 tokens");
+  if (!is_global && window < 1) return fail(HH_ERR_INVALID_ARG, "window must be >= 1");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(HH_ERR_INVALID_ARG, "q/k/v/o NULL or not 16-byte aligned");
+  if (s.m > 0 && (!aligned16(meta_k) || !aligned16(meta_v)))
+    return fail(HH_ERR_INVALID_ARG, "meta k/v NULL or not 16-byte aligned");
+  hh::AttnArgs aa{};
+  aa.q = q; aa.k = k; aa.v = v; aa.mk = meta_k; aa.mv = meta_v; aa.o = o;
+  aa.B = batch; aa.n = seqlen; aa.m = s.m; aa.H = s.H; aa.G = s.G; aa.hd = s.hd;
+  aa.window = window; aa.is_global = is_global;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Stage sg(st, "stage_attn");
+  const hipError_t err = sg.run([&] {
+    return s.dtype == HH_BF16 ? hh::launch_attention<hh::bf16>(aa, st) : hh::launch_attention<float>(aa, st);
+  });
+  return err == hipSuccess ? HH_OK : hip_fail(err, "attention");
+}
+
+hh_status hh_stage_ssm(const hh_dims *dims, const hh_weights *w, const float *xs, const void *z,
+                       const float *delta, const float *bc, const float *h0, const float *conv_tail,
+                       int32_t batch, int32_t seqlen, void *y, float *h_out, float *tail_out, void *ws,
+                       size_t ws_bytes, void *stream) {
+  Shape s;
+  hh_status r = check_dims(dims, 1, s);
+  if (r != HH_OK) return r;
+  if (!w || !w->A || !w->conv_w || !w->conv_b) return fail(HH_ERR_INVALID_ARG, "A/conv_w/conv_b NULL");
+  if (batch <= 0 || seqlen <= 0) return fail(HH_ERR_INVALID_ARG, "batch and seqlen must be positive");
+  if ((long long)batch * seqlen > (1LL << 30)) return fail(HH_ERR_UNSUPPORTED, "batch*seqlen above 2^30 tokens");
+  if (!xs || !delta || !bc) return fail(HH_ERR_INVALID_ARG, "xs/delta/bc NULL");
+  if (y && !z) return fail(HH_ERR_INVALID_ARG, "y needs the gate z");
+  int chunk = 0;
+  const size_t need = hh::scan_carry_bytes(batch, seqlen, s.D, s.N, &chunk);
+  if (!ws || ws_bytes < need) return fail(HH_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  hh::ScanArgs sa{};
+  sa.xs = xs; sa.z = y ? z : nullptr; sa.dt = delta; sa.bc = bc;
+  sa.A = w->A; sa.conv_w = w->conv_w; sa.conv_b = w->conv_b;
+  sa.h0 = h0; sa.tail0 = conv_tail;
+  sa.y = y; sa.h_out = h_out; sa.tail_out = tail_out;
+  sa.carry = static_cast<float *>(ws);
+  sa.B = batch; sa.n = seqlen; sa.D = s.D; sa.N = s.N; sa.k = s.k; sa.S = s.S; sa.chunk = chunk;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Stage sg(st, "stage_ssm");
+  const hipError_t err = sg.run([&] {
+    return s.dtype == HH_BF16 ? hh::launch_scan<hh::bf16>(sa, st) : hh::launch_scan<float>(sa, st);
+  });
+  return err == hipSuccess ? HH_OK : hip_fail(err, "selective scan");
+}
+
 hh_status hh_decode_step(const hh_dims *dims, const hh_weights *w, const void *x_t, int32_t batch,
                          const hh_meta *meta, int32_t window, int32_t is_global, hh_kv *kv,
                          hh_ssm_state *state, void *out, void *ws, size_t ws_bytes, void *stream) {

@@ -29,6 +29,16 @@ For bf16 workloads x, R, W_in, conv_w and W_out are rounded to bf16 once
 (round to nearest even); every consumer sees the rounded values, and so are
 W_gu and W_down.  A, b_dt, the betas and the norm gains stay fp32.  A consumer layer (no K/V projection) drops the K and V
 rows of the same draw, so it shares every other weight with its producer.
+
+The stage hooks take their inputs from recipes of their own (one generator,
+seeded, draws in this order):
+  attention: q [B, n, H*hd], k, v [B, G, n, hd], meta_k, meta_v [G, m, hd],
+             all ~ N(0, 1), rounded to the storage type;
+  SSM:       A and conv_w as in steps 5-6, conv_b ~ 0.1 N(0, 1), then
+             xs [B*n, D] ~ N(0, 1) (fp32), z [B*n, D] ~ N(0, 1) (storage type),
+             delta [B*n, D or S] ~ exp(U[ln 1e-3, ln 1e-1]) (fp32),
+             B|C [B*n, 2N] ~ N(0, 1), h0 [D, N] ~ N(0, 1),
+             conv_tail [k-1, D] ~ N(0, 1) (fp32).
 """
 from __future__ import annotations
 
@@ -180,3 +190,34 @@ def stack_inputs(w: StackWorkload, steps: int, varied: bool = False, seed=None) 
         blk["conv"] = _store(dims, _normal(rng, (B, k - 1, D)))
     x = _store(dims, _normal(rng, (steps, B, dims.d_model)))
     return dict(blocks=blocks, caches=caches, x=x)
+
+
+def attn_stage_inputs(dims: LayerDims, batch: int, seqlen: int, seed: int) -> dict:
+    """Inputs of the attention stage hook (the recipe in the module header)."""
+    rng = np.random.default_rng(seed)
+    H, G, hd, m = dims.n_heads, dims.n_kv_heads, dims.head_dim, dims.n_meta
+    q = _store(dims, _normal(rng, (batch, seqlen, H * hd)))
+    k = _store(dims, _normal(rng, (batch, G, seqlen, hd)))
+    v = _store(dims, _normal(rng, (batch, G, seqlen, hd)))
+    mk = _store(dims, _normal(rng, (G, m, hd)))
+    mv = _store(dims, _normal(rng, (G, m, hd)))
+    return dict(q=q, k=k, v=v, meta_k=mk, meta_v=mv)
+
+
+def ssm_stage_inputs(dims: LayerDims, batch: int, seqlen: int, seed: int) -> dict:
+    """Inputs of the SSM stage hook (the recipe in the module header); row-major
+    [B*n, ...] arrays."""
+    rng = np.random.default_rng(seed)
+    D, N, k, R = dims.d_inner, dims.d_state, dims.d_conv, batch * seqlen
+    a_shape = (dims.ssm_heads,) if dims.ssm_heads else (D, N)
+    A = (-np.exp(rng.uniform(np.log(1.0), np.log(16.0), size=a_shape))).astype(np.float32)
+    conv_w = _store(dims, _normal(rng, (D, k), (1.0 / k) ** 0.5))
+    conv_b = _normal(rng, (D,), 0.1)
+    xs = _normal(rng, (R, D))
+    z = _store(dims, _normal(rng, (R, D)))
+    delta = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), size=(R, dims.dt_width))).astype(np.float32)
+    bc = _normal(rng, (R, 2 * N))
+    h0 = _normal(rng, (D, N))
+    conv_tail = _normal(rng, (k - 1, D))
+    return dict(A=A, conv_w=conv_w, conv_b=conv_b, xs=xs, z=z, delta=delta, bc=bc, h0=h0,
+                conv_tail=conv_tail)

@@ -318,15 +318,52 @@ enum {
   HH_WS_F,       /* [B*n, H*hd + D] dtype fused features */
   HH_WS_SCAN,    /* scan chunk carries */
   HH_WS_GEMM,    /* split-K partial sums of the projections (few-row calls) */
-  HH_WS_SSQ,     /* [B*n, G + ceil(D/64)] fp32 row sums of squares of the
-                    branch outputs (bf16 prefill of 1024+ rows: the fusion
-                    runs inside the output projection, O and Y then hold
-                    beta-scaled values and F is not written) */
+  HH_WS_SSQ,     /* fp32 partial row sums of squares of the branch
+                    outputs: [B*n, G] (O^2 per row and KV group), then
+                    [B*n, ceil(D/64)] (Y^2 per row and 64-channel block).
+                    Written by bf16 prefills of 1024+ rows, where the
+                    fusion runs inside the output projection: O and Y then
+                    hold beta-scaled values and F is not written */
   HH_WS_COUNT
 };
 size_t hh_prefill_workspace_layout(const hh_dims *dims, int32_t batch,
                                    int32_t seqlen, int32_t kv_producer,
                                    size_t *offs);
+
+/* ---- stage hooks (test aids) -------------------------------------------
+ * The prefill's own kernels on caller-given inputs, so each branch can be
+ * compared with a plain implementation on its own; hh_prefill runs the same
+ * kernels.  Validation and errors as for hh_prefill (nothing is enqueued on
+ * an error); all work goes to `stream`.
+ *
+ * hh_stage_attn: the attention heads of Hymba paper §2.1 Eq. (1) with the
+ * meta tokens of §2.3 and the window of §2.2 (real query i sees every meta
+ * key and the real keys j with i - window < j <= i, or j <= i when
+ * is_global).  q [B*n, H*hd], k and v [B, G, n, hd], meta_k and meta_v
+ * [G, n_meta, hd] (NULL when n_meta is 0), o [B*n, H*hd]: dtype, 16-byte
+ * aligned, caller-owned.  The rotary embedding, if any, is not applied here
+ * (q and k are taken as given). */
+hh_status hh_stage_attn(const hh_dims *dims, const void *q, const void *k, const void *v,
+                        const void *meta_k, const void *meta_v, int32_t batch,
+                        int32_t seqlen, int32_t window, int32_t is_global, void *o,
+                        void *stream);
+
+/* hh_stage_ssm: the SSM heads of Eq. (2) from their input features: the
+ * causal conv + SiLU on xs, the selective scan from h0 and the gate SiLU(z).
+ * Uses w->A, w->conv_w, w->conv_b only.  xs (fp32), z (dtype) and delta (fp32,
+ * softplus already applied; D columns, or ssm_heads for Mamba2 heads) are in
+ * the channel-block-major layout of the prefill workspace over R = B*n rows:
+ * element (r, c) at ((c/64)*R + r)*64 + c%64, whole 64-column blocks.
+ * bc [B*n, 2*d_state] fp32 (B_t then C_t).  h0 [D, N] and conv_tail
+ * [d_conv-1, D] fp32 start every sequence (NULL: zero).  Outputs: y [B*n, D]
+ * dtype, h_out [B, D, N] fp32 and tail_out [B, d_conv-1, D] fp32 (each may be
+ * NULL).  ws: at least hh_stage_ssm_workspace_size bytes (chunk carries). */
+size_t hh_stage_ssm_workspace_size(const hh_dims *dims, int32_t batch, int32_t seqlen);
+hh_status hh_stage_ssm(const hh_dims *dims, const hh_weights *w, const float *xs,
+                       const void *z, const float *delta, const float *bc,
+                       const float *h0, const float *conv_tail, int32_t batch,
+                       int32_t seqlen, void *y, float *h_out, float *tail_out, void *ws,
+                       size_t ws_bytes, void *stream);
 
 /* Per-stage GPU timing (measurement aid, off by default).  While enabled on
  * the calling thread, each kernel stage an entry point enqueues (in-proj GEMM,

@@ -29,6 +29,20 @@ def rel_err(got, want) -> float:
     return float(np.abs(got - want).max()) / max(rms, 1e-30)
 
 
+UNIT_ROUNDOFF = {"f32": 2.0 ** -24, "bf16": 2.0 ** -8}
+
+
+def rel_err_stored(got, want, dtype) -> float:
+    """rel_err of a result stored in `dtype` ("f32" or "bf16"), allowing each
+    element its own rounding to that type (the unit roundoff times |want|)
+    before the comparison with the RMS-relative bar."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    excess = np.maximum(np.abs(got - want) - UNIT_ROUNDOFF[dtype] * np.abs(want), 0.0)
+    rms = float(np.sqrt(np.mean(want * want)))
+    return float(excess.max() / rms) if rms > 0 else float(excess.max())
+
+
 def np_of(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 

@@ -25,7 +25,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["hh_prefill", "hh_decode_step", "hh_meta_prefix", "hh_prefill_workspace_size",
               "hh_decode_workspace_size", "hh_meta_prefix_workspace_size", "hh_last_error",
-              "hh_version", "hh_prefill_workspace_layout"]:
+              "hh_version", "hh_prefill_workspace_layout", "hh_stage_attn", "hh_stage_ssm",
+              "hh_stage_ssm_workspace_size"]:
         assert n in names
 
 
@@ -222,3 +223,29 @@ def test_injected_launch_failure_surfaces_as_hip_error(entry, stage, monkeypatch
     assert "injected" in msg and stage in msg, msg
     # validation still comes first: a bad argument is reported as such
     assert _call_prefill(TINY, n=0) == 1
+
+
+def test_stage_hooks_validate_before_launch():
+    """The stage hooks reject bad arguments on the host (fake device pointers
+    are never dereferenced)."""
+    L = hb.lib()
+    d = hb.hh_dims(TINY)
+    ok = dict(q=FAKE, k=FAKE, v=FAKE, mk=FAKE, mv=FAKE, B=1, n=64, W=16, g=0, o=FAKE)
+
+    def attn(**kw):
+        a = dict(ok, **kw)
+        return L.hh_stage_attn(ctypes.byref(d), a["q"], a["k"], a["v"], a["mk"], a["mv"], a["B"], a["n"],
+                               a["W"], a["g"], a["o"], None)
+    assert attn(q=None) == 1 and attn(o=FAKE + 4) == 1 and attn(mk=None) == 1
+    assert attn(W=0) == 1 and attn(B=0) == 1 and attn(n=-1) == 1
+    assert attn(W=0, g=1, mk=None, mv=None) == 1   # meta needed while n_meta > 0
+    w = _weights()
+    need = hb.hh_stage_ssm_workspace_size(TINY, 1, 64)
+    assert need > 0
+
+    def ssm(ws_bytes=need, xs=FAKE, z=FAKE, y=FAKE, wts=w):
+        return L.hh_stage_ssm(ctypes.byref(d), ctypes.byref(wts), xs, z, FAKE, FAKE, None, None, 1, 64,
+                              y, None, None, FAKE, ws_bytes, None)
+    assert ssm(ws_bytes=need - 1) == 3
+    assert ssm(xs=None) == 1 and ssm(z=None) == 1
+    assert ssm(wts=hb.HHWeights(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1)) == 1   # no A
