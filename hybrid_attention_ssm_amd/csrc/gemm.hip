@@ -242,13 +242,28 @@ gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int
       }
   };
   auto stage = [&](int kt) { return smem + (kt % Cfg::STAGES) * Cfg::STAGE; };
+  // in a scheduling region holding one k-step's MFMAs and the next k-step's
+  // fragment reads, alternate the two (an MFMA first: it needs no new read)
+  // so the reads are in flight under the MFMAs instead of queued behind all
+  // of them
+  auto interleave = [&]() {
+    constexpr int NR = Cfg::TM + Cfg::TN, NM = Cfg::TM * Cfg::TN;
+    constexpr int P = NR < NM ? NR : NM;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+    }
+    if constexpr (NM > P) __builtin_amdgcn_sched_group_barrier(0x008, NM - P, 0);
+    if constexpr (NR > P) __builtin_amdgcn_sched_group_barrier(0x100, NR - P, 0);
+  };
   constexpr int PER_TILE = Cfg::A_INS + Cfg::B_INS;
   // Software pipeline per k-tile kt (its stage holds tile kt): each k-step's
   // fragments are read while the previous k-step's MFMAs run; after the
   // first k-step the stage of tile kt-1 is refilled with tile kt+STAGES-1
-  // (every wave passed the barrier after its last read of it); after the
-  // last k-step wait for tile kt+1, barrier, and read its first fragments
-  // while the MFMAs drain.
+  // (every wave passed the barrier after its last read of it); before the
+  // last k-step's MFMAs (their fragments are already in registers) wait for
+  // tile kt+1, barrier, and read its first fragments under those MFMAs.
 #pragma unroll
   for (int st = 0; st < Cfg::STAGES - 1; ++st) issue(ktile(st), st);
   wait_vmcnt<(Cfg::STAGES - 2) * PER_TILE>();
@@ -266,19 +281,26 @@ gemm_bf16_lds(const bf16 *__restrict__ A, const bf16 *__restrict__ B, int M, int
       }
     }
 #pragma unroll
-    for (int ks = 0; ks < Cfg::KS; ++ks) {
-      if (ks + 1 < Cfg::KS) fload(sA, ks + 1);
+    for (int ks = 0; ks + 1 < Cfg::KS; ++ks) {
+      fload(sA, ks + 1);
       mfmas(ks);
+      interleave();
       __builtin_amdgcn_sched_barrier(0);
       if (ks == 0) {
         const int nt = kt + Cfg::STAGES - 1;
         issue(ktile(nt), nt % Cfg::STAGES);
       }
     }
+    // the last k-step's fragments are in registers: sync first, then read the
+    // next tile's first fragments under its MFMAs
     wait_vmcnt<(Cfg::STAGES - 2) * PER_TILE>();   // this wave's loads of tile kt+1 have landed
+    wait_lgkmcnt0();                             // its reads of tile kt are done
     __builtin_amdgcn_s_barrier();               // ... and every other wave's
     __builtin_amdgcn_sched_barrier(0);
     fload(stage(kt + 1), 0);                     // (past the last tile: a harmless re-read)
+    mfmas(Cfg::KS - 1);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
   }
   wait_vmcnt<0>();
   __syncthreads();

@@ -39,6 +39,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// Wait until this wave's LDS (and scalar-memory) operations have completed.
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+}
 __device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
 // x * sigmoid(x) with sigmoid = 1 / (1 + 2^(-x log2 e)); saturates cleanly:
 // x -> -inf gives 2^(+inf) = inf, rcp(inf) = 0.
