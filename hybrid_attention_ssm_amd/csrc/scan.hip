@@ -97,14 +97,15 @@ __device__ __forceinline__ float scan_step(const ChanParams &p, float h[NS], flo
   for (int s = 0; s < NS; ++s) {
     const float decay = SC ? decay1 : exp2_fast(dt * p.A2[s]);
     h[s] = fmaf(decay, h[s], du * bv[s]);
-    if (MODE == 1) acc = fmaf(cv[s], h[s], acc);
+    if (MODE == 1 || MODE == 2) acc = fmaf(cv[s], h[s], acc);
   }
   if (MODE == 0) dsum += dt;
   return acc;
 }
 
 // The scan over [t0, t1) of sequence b for channel c.  MODE 0: summary
-// (end state and sum of Delta); MODE 1: output (Y, and final state/history).
+// (end state and sum of Delta); MODE 1: Y; MODE 2: Y and its row sums of
+// squares (fused norm); MODE 3: no Y (only the final state and history).
 // B_t/C_t are the same for every channel: SUB steps of them are staged in LDS
 // (sbc, SUB*2N floats) and read back as broadcasts; per-lane inputs are read
 // TB steps at a time.
@@ -123,8 +124,8 @@ __device__ __forceinline__ void scan_range(const ScanArgs &a, int b, int c, bool
                                            int t1, const ChanParams &p, float h[NS],
                                            float hist[KC - 1], float &dsum, float *sbc,
                                            float *sq = nullptr) {
+  constexpr bool HAS_Y = MODE == 1 || MODE == 2;
   const T *z = reinterpret_cast<const T *>(a.z);
-  T *y = reinterpret_cast<T *>(a.y);
   const size_t D = a.D;
   const size_t row0 = (size_t)b * a.n;
   const size_t R = (size_t)a.B * a.n;
@@ -132,16 +133,28 @@ __device__ __forceinline__ void scan_range(const ScanArgs &a, int b, int c, bool
   // step t is element t * 64 (channel-block-major layout)
   const float *xs = a.xs + ssm_index(row0, c, R);
   const float *dtp = a.dt + ssm_index(row0, p.dcol, R);
-  // without Y the gate is not needed: read (and ignore) xs instead, so the
-  // loads stay unconditional
-  const T *zp = y ? z + ssm_index(row0, c, R) : reinterpret_cast<const T *>(xs);
+  const T *zp = HAS_Y ? z + ssm_index(row0, c, R) : nullptr;
   const int lane = threadIdx.x;
+  // Y is stored through a buffer resource based at the block's first row, so
+  // a step's address is a scalar offset; lanes past the last channel get an
+  // offset past the buffer's end, which the hardware drops
+  const unsigned yoff = active ? (unsigned)c * sizeof(T) : 0x80000000u;
   for (int s0 = t0; s0 < t1; s0 += SUB) {
     const int len = min(SUB, t1 - s0);
+    // (MODE 0 / 3: a.y may be null; the resource is then never used)
+    const __amdgpu_buffer_rsrc_t rsY = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<T *>(a.y) + (HAS_Y ? (row0 + s0) * D : 0), (short)0,
+        HAS_Y ? (int)(len * D * sizeof(T)) : 0, 0x00020000);
     // Y of block step tt (the output: beta * Y; its square to sq row tt % TB)
     auto emit = [&](int tt, float yv) {
-      if (active) y[(row0 + s0 + tt) * D + c] = from_f32<T>(p.beta * yv);
-      if (sq) sq[(tt % TB) * SQ_LD + lane] = active ? yv * yv : 0.0f;
+      const int so = tt * (int)(D * sizeof(T));
+      if constexpr (sizeof(T) == 2)
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, from_f32<T>(p.beta * yv)),
+                                              rsY, yoff, so, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, from_f32<T>(p.beta * yv)),
+                                              rsY, yoff, so, 0);
+      if constexpr (MODE == 2) sq[(tt % TB) * SQ_LD + lane] = active ? yv * yv : 0.0f;
     };
     // the row sums of block steps base .. base + rows - 1
     auto flush = [&](int base, int rows) {
@@ -176,13 +189,19 @@ __device__ __forceinline__ void scan_range(const ScanArgs &a, int b, int c, bool
     // the last full batch re-reads that batch (a cache hit)
     float xv[TB], dv[TB];
     T zv[TB];
+    // (one base address per batch; the steps' offsets are immediates)
     auto load_batch = [&](int tb, float (&xo)[TB], float (&dvo)[TB], T (&zo)[TB]) {
+      const size_t base = (size_t)(s0 + tb) * 64;
+      const float *xb = xs + base, *db = dtp + base;
 #pragma unroll
       for (int i = 0; i < TB; ++i) {
-        const size_t idx = (size_t)(s0 + tb + i) * 64;
-        xo[i] = xs[idx];
-        dvo[i] = dtp[idx];
-        if (MODE == 1) zo[i] = zp[idx];
+        xo[i] = xb[i * 64];
+        dvo[i] = db[i * 64];
+      }
+      if constexpr (HAS_Y) {
+        const T *zb = zp + base;
+#pragma unroll
+        for (int i = 0; i < TB; ++i) zo[i] = zb[i * 64];
       }
     };
     if (TB <= len) load_batch(0, xv, dv, zv);
@@ -198,15 +217,15 @@ __device__ __forceinline__ void scan_range(const ScanArgs &a, int b, int c, bool
         for (int q = 0; q < NS / 4; ++q) {
           const float4 v = bc4[q];
           bv[4 * q] = v.x; bv[4 * q + 1] = v.y; bv[4 * q + 2] = v.z; bv[4 * q + 3] = v.w;
-          if (MODE == 1) {
+          if (HAS_Y) {
             const float4 u = bc4[NS / 4 + q];
             cv[4 * q] = u.x; cv[4 * q + 1] = u.y; cv[4 * q + 2] = u.z; cv[4 * q + 3] = u.w;
           }
         }
         const float acc = scan_step<MODE, SC>(p, h, hist, xv[i], dv[i], bv, cv, dsum);
-        if (MODE == 1 && y) emit(t + i, acc * silu_f(to_f32(zv[i])));
+        if constexpr (HAS_Y) emit(t + i, acc * silu_f(to_f32(zv[i])));
       }
-      if (MODE == 1 && y && sq) flush(t, TB);
+      if constexpr (MODE == 2) flush(t, TB);
 #pragma unroll
       for (int i = 0; i < TB; ++i) { xv[i] = xn[i]; dv[i] = dn[i]; zv[i] = zn[i]; }
     }
@@ -219,15 +238,15 @@ __device__ __forceinline__ void scan_range(const ScanArgs &a, int b, int c, bool
       for (int q = 0; q < NS / 4; ++q) {
         const float4 v = bc4[q];
         bv[4 * q] = v.x; bv[4 * q + 1] = v.y; bv[4 * q + 2] = v.z; bv[4 * q + 3] = v.w;
-        if (MODE == 1) {
+        if (HAS_Y) {
           const float4 u = bc4[NS / 4 + q];
           cv[4 * q] = u.x; cv[4 * q + 1] = u.y; cv[4 * q + 2] = u.z; cv[4 * q + 3] = u.w;
         }
       }
       const float acc = scan_step<MODE, SC>(p, h, hist, xs[idx], dtp[idx], bv, cv, dsum);
-      if (MODE == 1 && y) emit(t, acc * silu_f(to_f32(zp[idx])));
+      if constexpr (HAS_Y) emit(t, acc * silu_f(to_f32(zp[idx])));
     }
-    if (MODE == 1 && y && sq && t_rest < len) flush(t_rest, len - t_rest);
+    if constexpr (MODE == 2) if (t_rest < len) flush(t_rest, len - t_rest);
   }
 }
 
@@ -328,8 +347,9 @@ __global__ void __launch_bounds__(256) scan_pass2(ScanArgs a) {
   }
 }
 
-// pass 3: outputs of every chunk.  grid (C, ceil(D/64), B)
-template <class T, bool SC>
+// pass 3: outputs of every chunk.  grid (C, ceil(D/64), B).  OUT: the
+// scan_range mode (1: Y, 2: Y and row sums of squares, 3: no Y)
+template <class T, bool SC, int OUT>
 __global__ void __launch_bounds__(64) scan_pass3(ScanArgs a) {
   const int ck = blockIdx.x, b = blockIdx.z;
   // lanes past the last channel compute a copy of it (every lane takes part
@@ -353,9 +373,8 @@ __global__ void __launch_bounds__(64) scan_pass3(ScanArgs a) {
   }
   float dsum = 0.0f;
   __shared__ float4 sbc[SUB * 2 * NS / 4];
-  __shared__ float sq[TB * SQ_LD];
-  scan_range<T, 1, SC>(a, b, c, active, t0, t1, p, h, hist, dsum, reinterpret_cast<float *>(sbc),
-                       a.ssq && a.y ? sq : nullptr);
+  __shared__ float sq[OUT == 2 ? TB * SQ_LD : 1];
+  scan_range<T, OUT, SC>(a, b, c, active, t0, t1, p, h, hist, dsum, reinterpret_cast<float *>(sbc), sq);
   if (ck == nc - 1 && active) {
     if (a.h_out) {
       float *ho = a.h_out + ((size_t)b * a.D + c) * NS;
@@ -414,7 +433,10 @@ static hipError_t launch_finish_t(const ScanArgs &a, hipStream_t s) {
     else if (g2 == 16) hipLaunchKernelGGL(scan_pass2<16>, grid2, dim3(256), 0, s, a);
     else hipLaunchKernelGGL(scan_pass2<64>, grid2, dim3(256), 0, s, a);
   }
-  hipLaunchKernelGGL((scan_pass3<T, SC>), dim3(nc, cw, a.B), dim3(64), 0, s, a);
+  const dim3 grid3(nc, cw, a.B);
+  if (!a.y) hipLaunchKernelGGL((scan_pass3<T, SC, 3>), grid3, dim3(64), 0, s, a);
+  else if (a.ssq) hipLaunchKernelGGL((scan_pass3<T, SC, 2>), grid3, dim3(64), 0, s, a);
+  else hipLaunchKernelGGL((scan_pass3<T, SC, 1>), grid3, dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
