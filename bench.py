@@ -10,7 +10,10 @@ cache + a global layer over 8192 cached positions).
 
 Prints ONE JSON line.  Per-kernel durations come from HIP events recorded
 by the library on the stream it launches on (hh_timing_*); the headline time
-is a separate event-bracketed loop without those per-stage events.
+is a separate event-bracketed loop without those per-stage events.  After
+both loops, --settle-steps more prefill steps run back to back and the second
+half of them is timed: the rate once the GPU's clocks have settled under
+continuous load, reported as "settled" beside (never as) the value.
 
   python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--only prefill|decode]
 """
@@ -104,7 +107,7 @@ def decode_bytes(dims, B, layers, p, window, ring_cap, global_cap):
 
 
 # ---------------------------------------------------------------------------
-def bench_prefill(args, hb, torch, rope_base=0.0, ssm_heads=0, concurrent=False):
+def bench_prefill(args, hb, torch, rope_base=0.0, ssm_heads=0, concurrent=False, settle_steps=0):
     """The 8k SWA prefill; rope_base > 0 times the same layer with Q and K
     turned by the rotary embedding (same inputs), ssm_heads > 0 with Mamba2
     SSM heads (inputs drawn for that layout); concurrent runs the SSM branch
@@ -161,6 +164,20 @@ def bench_prefill(args, hb, torch, rope_base=0.0, ssm_heads=0, concurrent=False)
     torch.cuda.synchronize()
     stages = hb.hh_timing_read()
     hb.hh_timing_enable(False)
+    settled = None
+    if settle_steps > 0:
+        # the rate once the GPU's clocks have settled under continuous load
+        # (reported beside the timed steps, never as the value): settle_steps
+        # more steps back to back, the second half of them timed
+        for _ in range(settle_steps // 2):
+            step()
+        s2, s3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s2.record()
+        for _ in range(settle_steps - settle_steps // 2):
+            step()
+        s3.record()
+        torch.cuda.synchronize()
+        settled = s2.elapsed_time(s3) / (settle_steps - settle_steps // 2)
     if prev_env is None:
         os.environ.pop("HH_CONCURRENT_BRANCHES", None)
     else:
@@ -169,7 +186,8 @@ def bench_prefill(args, hb, torch, rope_base=0.0, ssm_heads=0, concurrent=False)
     st_ms = {name: tot / cnt for name, (cnt, tot) in stages.items()}
     log(f"[bench] prefill{tag} {ms_step:.3f} ms/step; stages " +
         ", ".join(f"{k}={v * 1e3:.1f}us" for k, v in st_ms.items()))
-    return dict(workload=w.name, dims=dims, B=B, n=n, W=W, ms_step=ms_step, stages=st_ms,
+    return dict(workload=w.name, dims=dims, B=B, n=n, W=W, ms_step=ms_step, settled_ms=settled,
+                settle_steps=settle_steps, stages=st_ms,
                 flops=fl, inp=inp)
 
 
@@ -400,6 +418,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-steps", type=int, default=160,
+                    help="extra 8k prefill steps after the timed ones, the second half timed "
+                         "(the settled rate, reported beside the value; 0 = skip)")
     ap.add_argument("--only", choices=["prefill", "decode", "both"], default="both")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stack", action="store_true",
@@ -441,7 +462,8 @@ def main():
         log(f"[bench] copied {n} bytes x5 (each launch reads {n} and writes {n} bytes)")
         return
 
-    pre = bench_prefill(args, hb, torch) if args.only in ("prefill", "both") else None
+    pre = (bench_prefill(args, hb, torch, settle_steps=args.settle_steps)
+           if args.only in ("prefill", "both") else None)
     pre_rope = pre_m2 = None
     if pre is not None and not args.no_rope:
         pre_rope = bench_prefill(args, hb, torch, rope_base=ROPE_BASE)
@@ -473,6 +495,16 @@ def main():
                                      f"d_inner 3200, N 16, conv 4)",
                          "global_batch": pre["B"], "seq_len": pre["n"], "parallelism": "none"}
         rec["mfma_frac_layer"] = fl["total"] / (pre["ms_step"] * 1e-3) / MFMA_BF16_PEAK
+        if pre["settled_ms"]:
+            # the GPU's clocks ramp over the first ~30 ms of continuous load: the
+            # timed steps above run partly inside that ramp
+            rec["settled"] = {"ms_per_step": pre["settled_ms"],
+                              "tok_per_s": pre["B"] * pre["n"] / (pre["settled_ms"] * 1e-3),
+                              "mfma_frac_layer": fl["total"] / (pre["settled_ms"] * 1e-3) / MFMA_BF16_PEAK,
+                              "steps": pre["settle_steps"] - pre["settle_steps"] // 2,
+                              "after_steps": pre["settle_steps"] // 2,
+                              "note": "continuous prefill steps after the timed and stage-timed ones; "
+                                      "not the value"}
         rec["algorithmic_gflop_per_step"] = fl["total"] / 1e9
         rec["stage_us"] = {k: v * 1e3 for k, v in pre["stages"].items()}
         t_scan = pre["stages"].get("scan")
