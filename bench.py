@@ -107,11 +107,13 @@ def decode_bytes(dims, B, layers, p, window, ring_cap, global_cap):
 
 
 # ---------------------------------------------------------------------------
-def bench_prefill(args, hb, torch, rope_base=0.0, ssm_heads=0, concurrent=False, settle_steps=0):
+def bench_prefill(args, hb, torch, rope_base=0.0, ssm_heads=0, concurrent=False, settle_steps=0,
+                  one_launch=False):
     """The 8k SWA prefill; rope_base > 0 times the same layer with Q and K
     turned by the rotary embedding (same inputs), ssm_heads > 0 with Mamba2
     SSM heads (inputs drawn for that layout); concurrent runs the SSM branch
-    on the library's side stream (HH_CONCURRENT_BRANCHES=1)."""
+    on the library's side stream (HH_CONCURRENT_BRANCHES=1); one_launch runs
+    the attention and scan pass 3 in one grid (HH_ONE_LAUNCH_BRANCHES=1)."""
     from dataclasses import replace
     from hybrid_attention_ssm_amd.configs import CFG1_SWA_8K
     from hybrid_attention_ssm_amd.synth import prefill_inputs
@@ -121,9 +123,11 @@ def bench_prefill(args, hb, torch, rope_base=0.0, ssm_heads=0, concurrent=False,
     B, n, W = w.batch, w.seqlen, w.window
     tag = ((f" (RoPE base {rope_base:g})" if rope_base else "") +
            (f" (Mamba2 heads: {ssm_heads})" if ssm_heads else "") +
-           (" (branches on two streams)" if concurrent else ""))
-    prev_env = os.environ.get("HH_CONCURRENT_BRANCHES")
+           (" (branches on two streams)" if concurrent else "") +
+           (" (attention and scan pass 3 in one launch)" if one_launch else ""))
+    prev_env = {k: os.environ.get(k) for k in ("HH_CONCURRENT_BRANCHES", "HH_ONE_LAUNCH_BRANCHES")}
     os.environ["HH_CONCURRENT_BRANCHES"] = "1" if concurrent else "0"
+    os.environ["HH_ONE_LAUNCH_BRANCHES"] = "1" if one_launch else "0"
     log(f"[bench] prefill setup {w.name}{tag}")
     inp = prefill_inputs(w)
     sd = hb.storage_dtype(dims)
@@ -178,10 +182,11 @@ def bench_prefill(args, hb, torch, rope_base=0.0, ssm_heads=0, concurrent=False,
         s3.record()
         torch.cuda.synchronize()
         settled = s2.elapsed_time(s3) / (settle_steps - settle_steps // 2)
-    if prev_env is None:
-        os.environ.pop("HH_CONCURRENT_BRANCHES", None)
-    else:
-        os.environ["HH_CONCURRENT_BRANCHES"] = prev_env
+    for k, v in prev_env.items():
+        if v is None:
+            os.environ.pop(k, None)
+        else:
+            os.environ[k] = v
     fl = prefill_flops(dims, B, n, W, False)
     st_ms = {name: tot / cnt for name, (cnt, tot) in stages.items()}
     log(f"[bench] prefill{tag} {ms_step:.3f} ms/step; stages " +
@@ -430,7 +435,8 @@ def main():
     ap.add_argument("--no-mamba2", action="store_true",
                     help="skip the prefill line with Mamba2 SSM heads")
     ap.add_argument("--no-branches", action="store_true",
-                    help="skip the prefill line with the SSM branch on a second stream")
+                    help="skip the prefill lines with the SSM branch on a second stream and with the "
+                         "attention and scan pass 3 in one launch")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192,
                     help="prefill tokens the CPU oracle runs (default: the whole 8k workload)")
     ap.add_argument("--cpu-sample-seqs", type=int, default=64,
@@ -469,9 +475,10 @@ def main():
         pre_rope = bench_prefill(args, hb, torch, rope_base=ROPE_BASE)
     if pre is not None and not args.no_mamba2:
         pre_m2 = bench_prefill(args, hb, torch, ssm_heads=MAMBA2_HEADS)
-    pre_br = None
+    pre_br = pre_ol = None
     if pre is not None and not args.no_branches:
         pre_br = bench_prefill(args, hb, torch, concurrent=True)
+        pre_ol = bench_prefill(args, hb, torch, one_launch=True)
     dec = bench_decode(args, hb, torch) if args.only in ("decode", "both") else None
     stack = None
     if args.only in ("decode", "both") and not args.no_stack:
@@ -548,6 +555,14 @@ def main():
                                "ms_per_step": pre_br["ms_step"],
                                "value": pre["B"] * pre["n"] / (pre_br["ms_step"] * 1e-3), "unit": "tok/s",
                                "vs_one_stream": pre["ms_step"] / pre_br["ms_step"]}
+        if pre_ol is not None:
+            # the attention and scan pass 3 in one grid (opt-in: measured slower than two launches)
+            rec["one_launch"] = {"mode": "HH_ONE_LAUNCH_BRANCHES=1 (scan passes 1 and 2, then one grid of "
+                                         "attention and scan pass-3 workgroups)",
+                                 "ms_per_step": pre_ol["ms_step"],
+                                 "value": pre["B"] * pre["n"] / (pre_ol["ms_step"] * 1e-3), "unit": "tok/s",
+                                 "vs_two_launches": pre["ms_step"] / pre_ol["ms_step"],
+                                 "stage_us": {k: v * 1e3 for k, v in pre_ol["stages"].items()}}
         if t_in:
             ach = fl["inproj"] / (t_in * 1e-3)
             tr = measured_traffic("gemm_bf16_lds", pre["workload"])

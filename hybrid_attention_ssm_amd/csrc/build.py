@@ -22,7 +22,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libhymba_hh.so")
-SOURCES = ["hh_api.cpp", "gemm.hip", "attention.hip", "scan.hip", "norm.hip", "decode.hip"]
+SOURCES = ["hh_api.cpp", "gemm.hip", "attention.hip", "scan.hip", "branches.hip", "norm.hip", "decode.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = [

@@ -316,6 +316,18 @@ bool concurrent_branches(const Shape &, long) {
   return v && v[0] == '1';
 }
 
+// The attention and scan pass 3 in one launch whose workgroups take either
+// role (bf16, HH_ONE_LAUNCH_BRANCHES=1): the same arithmetic as the two
+// kernels one after the other, so the same results bit for bit.  Off by
+// default: on the 8k prefill the shared grid takes 250 us against 117 + 125 us
+// for the two kernels.  Each kernel alone already fills a CU's registers and
+// LDS, both hide latency with their wave count, and the scan's VALU work plus
+// the softmax's exceed the VALU issue rate, so sharing CUs only splits them.
+bool one_launch_branches(const Shape &s) {
+  const char *v = std::getenv("HH_ONE_LAUNCH_BRANCHES");
+  return v && v[0] == '1' && s.dtype == HH_BF16;
+}
+
 // The fusion of Eq. (3) inside the output projection (bf16, many rows): the
 // branches store beta-scaled outputs and per-row sums of squares, and the
 // GEMM applies the row scales to its accumulators, so no normalised copy of
@@ -440,13 +452,32 @@ hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, i
     aa.beta = w->beta_attn; aa.ssq = ssq_o;
     if (set_len) { aa.set_len = kv->len; aa.set_len_n = B; aa.set_len_value = n; }
   }
-  {
-    Stage sg(st, "attention");
-    err = sg.run([&] { return hh::launch_attention<T>(aa, st); });
+  if (!side && one_launch_branches(s)) {
+    // scan passes 1 and 2, then the attention beside scan pass 3
+    {
+      Stage sg(st, "scan_carries");
+      err = sg.run([&] {
+        hipError_t q = hh::launch_scan_summaries<T>(sa, 0, nchunks, 0, B, st);
+        return q == hipSuccess ? hh::launch_scan_carries<T>(sa, st) : q;
+      });
+    }
+    if (err != hipSuccess) return hip_fail(err, "selective scan");
+    {
+      Stage sg(st, "attention_scan");
+      err = sg.run([&] { return hh::launch_attn_scan3<T>(aa, sa, st); });
+    }
+    if (err != hipSuccess) return hip_fail(err, "attention and selective scan");
+  } else {
+    {
+      Stage sg(st, "attention");
+      err = sg.run([&] { return hh::launch_attention<T>(aa, st); });
+    }
+    if (err != hipSuccess) return hip_fail(err, "attention");
   }
-  if (err != hipSuccess) return hip_fail(err, "attention");
 
-  if (!side) {
+  if (!side && one_launch_branches(s)) {
+    // done above
+  } else if (!side) {
     {
       Stage sg(st, "scan");
       err = sg.run([&] { return hh::launch_scan<T>(sa, st); });

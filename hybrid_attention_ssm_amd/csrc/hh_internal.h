@@ -497,6 +497,12 @@ template <class T> hipError_t launch_scan(const ScanArgs &a, hipStream_t s);
 template <class T>
 hipError_t launch_scan_summaries(const ScanArgs &a, int ck0, int ck1, int b0, int b1, hipStream_t s);
 template <class T> hipError_t launch_scan_finish(const ScanArgs &a, hipStream_t s);
+// pass 2 alone (the carries), for a caller that runs pass 3 in the launch
+// beside the attention (launch_attn_scan3)
+template <class T> hipError_t launch_scan_carries(const ScanArgs &a, hipStream_t s);
+// The attention (aa) and scan pass 3 (sa) in one grid whose workgroups take
+// either role (bf16 only; pass 1 and pass 2 of sa must have run)
+template <class T> hipError_t launch_attn_scan3(const AttnArgs &aa, const ScanArgs &sa, hipStream_t s);
 int scan_chunks(const ScanArgs &a);
 size_t scan_carry_bytes(int B, int n, int D, int N, int *chunk_out);
 
