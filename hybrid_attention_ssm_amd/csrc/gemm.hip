@@ -545,8 +545,11 @@ static hipError_t run_lds(const bf16 *A, int M, int K, const bf16 *B, int N, con
 using CfgLds = LdsCfg<256, 256, 128, 64, 3>;
 // 256x224 tile, 8 waves of 32x224: for outputs whose 256x256 tiles leave part
 // of the chip idle in their last round (8192 x 1600: 224 tiles on 256 CUs,
-// with 12% padding), 224-wide tiles give every CU one tile of 7/8 the area
-using CfgWide = LdsCfg<256, 224, 32, 224, 3>;
+// with 12% padding), 224-wide tiles give every CU one tile of 7/8 the area.
+// 64-deep k-tiles in 2 stages (120 KB): half the barriers of 32-deep ones,
+// whose per-k-tile sync costs this shape more (its waves read the whole
+// 224-row B tile); needs K (and, fused, both parts of K) a multiple of 64
+using CfgWide = LdsCfg<256, 224, 32, 224, 2, 64>;
 // Few rows (decode, meta prefix): the weights dominate the traffic and each
 // workgroup streams a slab of 64 weight rows.  When those slabs alone leave
 // the chip short of workgroups (the output projection: 25 slabs) the K range
@@ -602,17 +605,18 @@ static long tile_cost(int M, int N, int cus) {
   return (tiles + cus - 1) / cus * (long)Cfg::BM * Cfg::BN;
 }
 
-// the wide tile reads more LDS per flop: only where it saves a tenth
-static bool use_wide(int M, int N) {
+// the wide tile reads more LDS per flop: only where it saves a tenth (and
+// where its deeper k-tiles divide K)
+static bool use_wide(int M, int N, int K) {
   const int cus = device_cus();
-  return 10 * tile_cost<CfgWide>(M, N, cus) < 9 * tile_cost<CfgLds>(M, N, cus);
+  return K % CfgWide::BK == 0 && 10 * tile_cost<CfgWide>(M, N, cus) < 9 * tile_cost<CfgLds>(M, N, cus);
 }
 
 template <class Epi>
 static hipError_t run_bf16_auto(const bf16 *A, int M, int K, const bf16 *B, int N, const Epi &epi,
                                 float *part, hipStream_t s) {
   if (M >= 1024) {
-    if (use_wide(M, N)) return run_lds<CfgWide>(A, M, K, B, N, epi, s);
+    if (use_wide(M, N, K)) return run_lds<CfgWide>(A, M, K, B, N, epi, s);
     return run_lds<CfgLds>(A, M, K, B, N, epi, s);
   }
   return run_skinny(A, M, K, B, N, epi, part, s);
@@ -631,12 +635,14 @@ static hipError_t run_fused(const bf16 *o, const NormScale &ns, int M, const bf1
 template <class Epi>
 static hipError_t run_fused_auto(const bf16 *o, const NormScale &ns, int M, const bf16 *w, int N,
                                  const Epi &epi, hipStream_t s) {
-  if (use_wide(M, N)) return run_fused<CfgWide>(o, ns, M, w, N, epi, s);
+  if (ns.Wa % CfgWide::BK == 0 && ns.D % CfgWide::BK == 0 && use_wide(M, N, ns.Wa + ns.D))
+    return run_fused<CfgWide>(o, ns, M, w, N, epi, s);
   return run_fused<CfgLds>(o, ns, M, w, N, epi, s);
 }
 
+// (the y and o parts of K must each be whole k-tiles of the tile used)
 bool outproj_fused_ok(int M, int Wa, int D) {
-  static_assert(CfgWide::BK == CfgLds::BK, "one k-tile depth");
+  static_assert(CfgWide::BK % CfgLds::BK == 0, "the deeper k-tile is a multiple of the other");
   return M >= 1024 && Wa > 0 && D > 0 && Wa % CfgLds::BK == 0 && D % CfgLds::BK == 0;
 }
 
