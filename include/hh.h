@@ -15,6 +15,17 @@
  * to a stage name (e.g. "inproj", "scan", "decode_inproj", "decode_norm")
  * makes that stage report a failed launch on the host without launching.
  *
+ * Launch-plan switches read from the environment at each hh_prefill call
+ * (every plan computes the same values; the defaults are the fastest measured):
+ *   HH_FUSED_NORM=0           bf16 prefills of 1024+ rows run the fusion step
+ *                             as its own kernel instead of inside the output
+ *                             projection (same result up to bf16 rounding);
+ *   HH_CONCURRENT_BRANCHES=1  the SSM branch runs on a library side stream
+ *                             beside the input projection and the attention;
+ *   HH_ONE_LAUNCH_BRANCHES=1  (bf16) the attention and the scan's last pass
+ *                             run in one grid of role-split workgroups.
+ * The last two give results identical bit for bit to the default plan.
+ *
  * What the layer computes (the method of "Hymba: A Hybrid-head Architecture
  * for Small Language Models", arXiv 2411.13676, and the authors' OpenReview
  * replies on implementation details):
