@@ -79,11 +79,24 @@ __device__ __forceinline__ float scan_step(const ChanParams &p, float h[NS], flo
   const float du = dt * silu_f(conv);
   float acc = 0.0f;
   const float decay1 = SC ? exp2_fast(dt * p.A2[0]) : 0.0f;   // Mamba2: one per step
+  if constexpr (!SC) {
+    // all decays first: 16 independent exponentials for the scheduler to
+    // interleave, instead of 16 dependent mul -> exp -> FMA chains
+    float dec[NS];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const float decay = SC ? decay1 : exp2_fast(dt * p.A2[s]);
-    h[s] = fmaf(decay, h[s], du * bv[s]);
-    if (MODE == 1 || MODE == 2) acc = fmaf(cv[s], h[s], acc);
+    for (int s = 0; s < NS; ++s) dec[s] = exp2_fast(dt * p.A2[s]);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      h[s] = fmaf(dec[s], h[s], du * bv[s]);
+      if (MODE == 1 || MODE == 2) acc = fmaf(cv[s], h[s], acc);
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const float decay = SC ? decay1 : exp2_fast(dt * p.A2[s]);
+      h[s] = fmaf(decay, h[s], du * bv[s]);
+      if (MODE == 1 || MODE == 2) acc = fmaf(cv[s], h[s], acc);
+    }
   }
   if (MODE == 0) dsum += dt;
   return acc;
