@@ -120,17 +120,23 @@ def test_ragged_lengths_decode(dims):
     _ragged_decode(dims, lens, window=16, gcap=64, seed=61)
 
 
-@pytest.mark.parametrize("dims", [
+WIDE_BF16 = LayerDims(d_model=128, n_heads=2, n_kv_heads=1, head_dim=64, d_inner=4160, d_state=16, d_conv=4,
+                      n_meta=4, dtype="bf16")
+
+
+@pytest.mark.parametrize("dims,fused_norm", [
     # fp32 rows wider than 512 four-wide chunks and bf16 rows wider than 512
     # eight-wide chunks, with at least 2048 rows: the norm kernel that keeps
-    # no row in registers
-    LayerDims(d_model=64, n_heads=2, n_kv_heads=1, head_dim=32, d_inner=2560, d_state=16, d_conv=4,
-              n_meta=4, dtype="f32"),
-    LayerDims(d_model=128, n_heads=2, n_kv_heads=1, head_dim=64, d_inner=4160, d_state=16, d_conv=4,
-              n_meta=4, dtype="bf16")], ids=["f32-D2560", "bf16-D4160"])
-def test_wide_ssm_branch_many_rows(dims):
+    # no row in registers (bf16 with the fusion step as its own kernel,
+    # HH_FUSED_NORM=0; the default runs it inside the output projection)
+    (LayerDims(d_model=64, n_heads=2, n_kv_heads=1, head_dim=32, d_inner=2560, d_state=16, d_conv=4,
+               n_meta=4, dtype="f32"), "1"),
+    (WIDE_BF16, "0"),
+    (WIDE_BF16, "1")], ids=["f32-D2560", "bf16-D4160-norm-kernel", "bf16-D4160-fused"])
+def test_wide_ssm_branch_many_rows(dims, fused_norm, monkeypatch):
+    monkeypatch.setenv("HH_FUSED_NORM", fused_norm)
     n, W = 2048, 16
-    print(f"case wide SSM {dims.dtype} D={dims.d_inner} n={n}", flush=True)
+    print(f"case wide SSM {dims.dtype} D={dims.d_inner} n={n} HH_FUSED_NORM={fused_norm}", flush=True)
     inp = prefill_inputs(PrefillWorkload("wide", 52, dims, 1, n, W, False), varied=True)
     want = ref.prefill(dims.as_dict(), inp["weights"], inp["R"], inp["x"], W, False)
     got = run_prefill(dims, inp["weights"], inp["R"], inp["x"], W, False)
