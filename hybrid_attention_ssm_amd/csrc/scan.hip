@@ -140,16 +140,27 @@ __global__ void __launch_bounds__(64) scan_pass3(ScanArgs a) {
 }
 
 size_t scan_carry_bytes(int B, int n, int D, int N, int *chunk_out) {
-  // enough (channel-wave x chunk) work items to fill 256 CUs several times
-  const int cw = (D + 63) / 64;
-  const long waves = (long)B * cw;
-  int nc = (int)((4096 + waves - 1) / waves);
-  // at most 64 * P2_RUN + 1 chunks, so pass 2's lane groups hold every carry
-  nc = std::max(1, std::min({nc, (n + 63) / 64, 1024}));
-  int chunk = (n + nc - 1) / nc;
-  chunk = (chunk + 7) / 8 * 8;
-  if (chunk < 8) chunk = 8;
-  nc = (n + chunk - 1) / chunk;
+  // Passes 1 and 3 run one wave per (chunk, 64 channels, sequence).  At three
+  // waves per SIMD (their register budget) 256 CUs hold kScanSlots of them at
+  // once, and a wave that finds no slot waits for a whole wave's time.  The
+  // chunk is the shortest multiple of 8 steps (at least 64; at most 1024
+  // chunks, so pass 2's lane groups hold every carry) whose waves all fit in
+  // one round, or whose full chunks do while the last is at most a quarter
+  // as long: its waves finish early and hand their slots to the few that did
+  // not fit.  8k, one sequence: 62 chunks of 136 steps (the last 24),
+  // against 80 chunks of 104 steps (1.3 rounds): scan 192-195 against
+  // 199-201 us on one box.
+  constexpr long kScanSlots = 3 * 4 * 256;
+  const long wpc = (long)B * ((D + 63) / 64);   // waves per chunk index
+  int chunk = std::max(64, ((n + 1023) / 1024 + 7) / 8 * 8);
+  for (; chunk < n; chunk += 8) {
+    const long full = n / chunk, rem = n % chunk;
+    if ((full + (rem ? 1 : 0)) * wpc <= kScanSlots ||
+        (full * wpc <= kScanSlots && 4L * rem <= chunk))
+      break;
+  }
+  chunk = std::min(chunk, std::max(n, 1));
+  const int nc = (n + chunk - 1) / chunk;
   if (chunk_out) *chunk_out = chunk;
   return (size_t)B * nc * (N + 1) * D * sizeof(float);
 }
