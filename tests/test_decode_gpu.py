@@ -55,14 +55,15 @@ def _decode_steps(dims, got, x_new, window, is_global, cap, consumer=None):
     return outs
 
 
-@pytest.mark.parametrize("dims,n0,steps,window,is_global,cap", [
-    (TINY, 10, 12, 8, False, 8),          # ring of 8 wraps during decode
-    (TINY, 20, 5, 16, True, 32),          # linear cache
-    (SMALL_BF16, 60, 9, 64, False, 64),   # bf16 ring wrap
-    (SMALL_BF16, 130, 4, 64, True, 160),
+@pytest.mark.parametrize("dims,n0,steps,window,is_global,cap,B", [
+    (TINY, 10, 12, 8, False, 8, 2),          # ring of 8 wraps during decode
+    (TINY, 20, 5, 16, True, 32, 2),          # linear cache
+    (SMALL_BF16, 60, 9, 64, False, 64, 2),   # bf16 ring wrap
+    (SMALL_BF16, 130, 4, 64, True, 160, 2),
+    (SMALL_BF16, 40, 6, 32, False, 32, 1),   # one sequence
+    (SMALL_BF16, 50, 3, 64, True, 53, 5),    # five sequences, the linear cache filled to its last slot
 ])
-def test_prefill_then_decode_matches_longer_prefill(dims, n0, steps, window, is_global, cap):
-    B = 2
+def test_prefill_then_decode_matches_longer_prefill(dims, n0, steps, window, is_global, cap, B):
     inp = prefill_inputs(PrefillWorkload("pd", n0 + steps, dims, B, n0 + steps, window, is_global),
                          varied=True)
     x = inp["x"]

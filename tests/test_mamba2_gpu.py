@@ -32,8 +32,6 @@ SMALL_P32 = replace(SMALL_BF16, ssm_heads=16)          # 32 channels per head
     (2, 1100, 64, False)])    # with the 256x256-tile in-projection
 def test_prefill_mamba2_32_channel_heads(B, n, window, is_global):
     """bf16, 32 channels per head, sequences of one partial chunk to many."""
-    # a global cache of about the sequence length (the error metric is relative
-    # to the RMS over all slots, so unwritten ones would inflate it)
     _check_prefill(SMALL_P32, B, n, window, is_global, seed=400 + n, cache_cap=128 if not is_global else 256)
 
 
