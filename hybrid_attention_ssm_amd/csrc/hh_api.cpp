@@ -452,7 +452,8 @@ hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, i
     aa.beta = w->beta_attn; aa.ssq = ssq_o;
     if (set_len) { aa.set_len = kv->len; aa.set_len_n = B; aa.set_len_value = n; }
   }
-  if (!side && one_launch_branches(s)) {
+  const bool one_launch = !side && one_launch_branches(s);   // read once per call
+  if (one_launch) {
     // scan passes 1 and 2, then the attention beside scan pass 3
     {
       Stage sg(st, "scan_carries");
@@ -475,7 +476,7 @@ hh_status prefill_t(const Shape &s, const hh_weights *w, const void *x, int B, i
     if (err != hipSuccess) return hip_fail(err, "attention");
   }
 
-  if (!side && one_launch_branches(s)) {
+  if (one_launch) {
     // done above
   } else if (!side) {
     {
